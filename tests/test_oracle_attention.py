@@ -1,0 +1,143 @@
+"""Pins for the oracle's compressed-space decode attention.
+
+Pages: "RotaryQuant ..." (arXiv 2608.08081), Abstract -- attention runs
+directly on the packed 3-bit tensors without materialising full-precision
+KV.  Pinned by the orthogonality identity (compressed space equals dense
+attention on dequantized, unrotated K/V), by PyTorch's fp64 scaled-dot-
+product attention on tiny cases, and by closed-form special cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def _case(rng, B=2, Hq=4, Hkv=2, T=37, lens=None):
+    p = rng.standard_normal((B, Hkv, 32, 2, 4))
+    p /= np.linalg.norm(p, axis=-1, keepdims=True)
+    p = p.reshape(B, Hkv, 32, 8)
+    q = rng.standard_normal((B, Hq, 128))
+    k = rng.standard_normal((B, Hkv, T, 128)) * 2.0
+    v = rng.standard_normal((B, Hkv, T, 128))
+    kc = np.zeros((B, Hkv, T, 128), np.uint8)
+    vc = np.zeros_like(kc)
+    ks = np.zeros((B, Hkv, T), np.float32)
+    vs = np.zeros_like(ks)
+    for b in range(B):
+        for g in range(Hkv):
+            kc[b, g], ks[b, g], _, _ = oracle.quantize(k[b, g], p[b, g])
+            vc[b, g], vs[b, g], _, _ = oracle.quantize(v[b, g], p[b, g])
+    if lens is None:
+        lens = np.full(B, T)
+    return q, kc, ks, vc, vs, p, np.asarray(lens)
+
+
+def test_compressed_space_equals_dense_on_dequantized():
+    rng = np.random.default_rng(20)
+    args = _case(rng, lens=[37, 11])
+    a = oracle.decode_attention(*args)
+    b = oracle.dense_attention_on_dequantized(*args)
+    np.testing.assert_allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_matches_torch_sdpa_fp64():
+    rng = np.random.default_rng(21)
+    q, kc, ks, vc, vs, p, lens = _case(rng, B=1, Hq=6, Hkv=3, T=19)
+    out = oracle.decode_attention(q, kc, ks, vc, vs, p, lens)
+    G = 2
+    for g in range(3):
+        R = oracle.rotation_matrix(p[0, g])
+        khat = torch.tensor(oracle.dequantize_rotated(kc[0, g], ks[0, g]) @ R)
+        vhat = torch.tensor(oracle.dequantize_rotated(vc[0, g], vs[0, g]) @ R)
+        for h in range(g * G, (g + 1) * G):
+            qq = torch.tensor(q[0, h])[None, None, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, khat[None, None], vhat[None, None])[0, 0, 0].numpy()
+            np.testing.assert_allclose(out[0, h], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_gqa_mapping_uses_contiguous_groups():
+    # Query head h must read KV head h // G (contiguous groups).  KV head 0 gets every V code 7
+    # (rotated-space level +3.5 s) and KV head 1 every code 0 (-3.5 s): rotating an output back
+    # into its KV head's space gives a vector of one sign, telling which KV head it read.
+    rng = np.random.default_rng(22)
+    q, kc, ks, vc, vs, p, lens = _case(rng, B=1, Hq=4, Hkv=2, T=5)
+    vc[0, 0] = 7
+    vc[0, 1] = 0
+    out = oracle.decode_attention(q, kc, ks, vc, vs, p, lens)
+    for h in range(4):
+        g = h // 2
+        rot = oracle.rotation_matrix(p[0, g]) @ out[0, h]
+        expect = np.sum(vs[0, g]) / 5 * 3.5   # mean scale is an upper bound; check sign and constancy
+        assert np.all(rot > 0) if g == 0 else np.all(rot < 0)
+        assert np.ptp(rot) < 1e-12 * expect
+
+
+def test_single_token_returns_its_value():
+    rng = np.random.default_rng(23)
+    q, kc, ks, vc, vs, p, _ = _case(rng, B=1, Hq=2, Hkv=1, T=4)
+    out = oracle.decode_attention(q, kc, ks, vc, vs, p, np.array([1]))
+    R = oracle.rotation_matrix(p[0, 0])
+    ref = R.T @ oracle.dequantize_rotated(vc[0, 0, 0], vs[0, 0, 0])
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-13)
+    np.testing.assert_allclose(out[0, 1], ref, atol=1e-13)
+
+
+def test_zero_query_gives_mean_and_zero_length_gives_zero():
+    rng = np.random.default_rng(24)
+    q, kc, ks, vc, vs, p, _ = _case(rng, B=2, Hq=2, Hkv=1, T=9)
+    q[:] = 0
+    out = oracle.decode_attention(q, kc, ks, vc, vs, p, np.array([9, 0]))
+    R = oracle.rotation_matrix(p[0, 0])
+    ref = R.T @ oracle.dequantize_rotated(vc[0, 0], vs[0, 0]).mean(axis=0)
+    np.testing.assert_allclose(out[0, 0], ref, atol=1e-13)
+    assert np.all(out[1] == 0)
+
+
+def test_softmax_scale_default_and_override():
+    rng = np.random.default_rng(25)
+    args = list(_case(rng, B=1, Hq=1, Hkv=1, T=8))
+    a = oracle.decode_attention(*args, sm_scale=None)
+    b = oracle.decode_attention(*args, sm_scale=1 / np.sqrt(128))
+    c = oracle.decode_attention(*args, sm_scale=0.5)
+    np.testing.assert_array_equal(a, b)
+    assert np.max(np.abs(a - c)) > 1e-6
+
+
+def test_split_merge_equals_two_pass():
+    # Online split-K merge (max, rescale, sum) reproduces the two-pass softmax: this is the
+    # identity the combine step relies on.
+    rng = np.random.default_rng(26)
+    z = rng.standard_normal(100) * 5
+    v = rng.standard_normal((100, 128))
+    p = np.exp(z - z.max())
+    ref = (p @ v) / p.sum()
+    parts = []
+    for lo in range(0, 100, 17):
+        zz = z[lo:lo + 17]
+        m = zz.max()
+        w = np.exp(zz - m)
+        parts.append((m, w.sum(), w @ v[lo:lo + 17]))
+    M = max(m for m, _, _ in parts)
+    L = sum(np.exp(m - M) * l for m, l, _ in parts)
+    O = sum(np.exp(m - M) * o for m, _, o in parts)
+    np.testing.assert_allclose(O / L, ref, atol=1e-13)
+
+
+def test_retrieval_of_a_planted_key_survives_quantization_in_oracle():
+    # Small analogue of the long-context planted-key workload: the planted position wins
+    # the softmax after 3-bit quantization.
+    rng = np.random.default_rng(27)
+    T = 2048
+    p = rng.standard_normal((1, 1, 32, 2, 4))
+    p /= np.linalg.norm(p, axis=-1, keepdims=True)
+    p = p.reshape(1, 1, 32, 8)
+    q = rng.standard_normal((1, 1, 128))
+    k = rng.standard_normal((1, 1, T, 128))
+    pos = 777
+    k[0, 0, pos] = 4 * q[0, 0]
+    kc, ks, _, _ = oracle.quantize(k[0, 0], p[0, 0])
+    R = oracle.rotation_matrix(p[0, 0])
+    z = oracle.dequantize_rotated(kc, ks) @ (R @ q[0, 0])
+    assert int(np.argmax(z)) == pos
