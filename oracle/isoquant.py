@@ -146,30 +146,34 @@ def dequantize_rotated(codes, scales):
 # layout itself is a reading).
 #
 # The record is four 12-byte quarters; quarter q holds coordinates
-# 32q..32q+31.  A quarter is six little-endian 16-bit words u_0..u_5.
-#   * bits 3j..3j+2 of u_k hold the code of coordinate 32q + 5k + j (j < 5);
-#   * bit 15 of u_(2b+h) holds bit b of the code of coordinate 32q + 30 + h.
+# 32q..32q+31 as two halves of 16 (half h: coordinates 32q+16h..32q+16h+15).
+# A quarter is six little-endian 16-bit words u_0..u_5; word u_(2k+h)
+# (k = 0, 1, 2) belongs to half h:
+#   * its bits 3j..3j+2 hold the code of coordinate 32q + 16h + 5k + j (j < 5);
+#   * its bit 15 holds bit k of the code of coordinate 32q + 16h + 15.
 # --------------------------------------------------------------------------
+def _word_index(q, h, k):
+    return 12 * q + 2 * (2 * k + h)     # byte offset of word u_(2k+h) in quarter q
+
+
 def pack(codes):
     """uint8 codes [..., 128] (values 0..7) -> uint8 records [..., 48]."""
     c = np.asarray(codes)
     assert c.shape[-1] == D and np.all(c < LEVELS)
     c = c.astype(np.uint32)
     lead = c.shape[:-1]
-    words = np.zeros(lead + (4, 6), dtype=np.uint32)
-    for q in range(4):
-        for k in range(6):
-            w = np.zeros(lead, dtype=np.uint32)
-            for j in range(5):
-                w |= c[..., 32 * q + 5 * k + j] << np.uint32(3 * j)
-            b, h = k // 2, k % 2
-            w |= ((c[..., 32 * q + 30 + h] >> np.uint32(b)) & np.uint32(1)) << np.uint32(15)
-            words[..., q, k] = w
     out = np.zeros(lead + (RECORD_BYTES,), dtype=np.uint8)
     for q in range(4):
-        for k in range(6):
-            out[..., 12 * q + 2 * k] = words[..., q, k] & 0xFF
-            out[..., 12 * q + 2 * k + 1] = words[..., q, k] >> 8
+        for h in range(2):
+            base = 32 * q + 16 * h
+            for k in range(3):
+                w = np.zeros(lead, dtype=np.uint32)
+                for j in range(5):
+                    w |= c[..., base + 5 * k + j] << np.uint32(3 * j)
+                w |= ((c[..., base + 15] >> np.uint32(k)) & np.uint32(1)) << np.uint32(15)
+                off = _word_index(q, h, k)
+                out[..., off] = w & 0xFF
+                out[..., off + 1] = w >> 8
     return out
 
 
@@ -181,12 +185,14 @@ def unpack(records):
     lead = r.shape[:-1]
     codes = np.zeros(lead + (D,), dtype=np.uint32)
     for q in range(4):
-        for k in range(6):
-            w = r[..., 12 * q + 2 * k] | (r[..., 12 * q + 2 * k + 1] << np.uint32(8))
-            for j in range(5):
-                codes[..., 32 * q + 5 * k + j] = (w >> np.uint32(3 * j)) & np.uint32(7)
-            b, h = k // 2, k % 2
-            codes[..., 32 * q + 30 + h] |= ((w >> np.uint32(15)) & np.uint32(1)) << np.uint32(b)
+        for h in range(2):
+            base = 32 * q + 16 * h
+            for k in range(3):
+                off = _word_index(q, h, k)
+                w = r[..., off] | (r[..., off + 1] << np.uint32(8))
+                for j in range(5):
+                    codes[..., base + 5 * k + j] = (w >> np.uint32(3 * j)) & np.uint32(7)
+                codes[..., base + 15] |= ((w >> np.uint32(15)) & np.uint32(1)) << np.uint32(k)
     return codes.astype(np.uint8)
 
 
