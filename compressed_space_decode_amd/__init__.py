@@ -1,0 +1,11 @@
+"""IsoQuant 3-bit KV compression and compressed-space decode attention for
+AMD MI355X (gfx950): HIP kernels behind a C ABI (include/iq.h), with a thin
+ctypes binding.
+
+Method: "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
+Compressed-Space Attention" (arXiv 2608.08081), Abstract.
+"""
+from .iq import (  # noqa: F401
+    IQError, make_rotation, quantize_kv, decode_workspace_bytes, decode_attention,
+    lib, LIB_PATH, HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS,
+)

@@ -1,0 +1,199 @@
+// C-ABI entry points of libiq: argument validation, then kernel launches on
+// the caller's stream.  Declarations and documentation: include/iq.h.
+#include <cstdarg>
+#include <cstdio>
+
+#include "iq.h"
+#include "iq_internal.h"
+
+namespace iq {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+}  // namespace iq
+
+namespace {
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int check_dims(const char* fn, int32_t head_dim, int32_t bits) {
+  if (head_dim != IQ_HEAD_DIM) {
+    iq::set_error("%s: head_dim must be 128 (got %d)", fn, head_dim);
+    return IQ_EUNSUPPORTED;
+  }
+  if (bits != IQ_BITS) {
+    iq::set_error("%s: bits must be 3 (got %d)", fn, bits);
+    return IQ_EUNSUPPORTED;
+  }
+  return IQ_OK;
+}
+
+}  // namespace
+
+extern "C" const char* iq_last_error(void) { return iq::g_err; }
+
+extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64_t n_seq, int32_t n_heads,
+                              int64_t n_tokens, int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
+                              const float* rot, int64_t rot_stride_seq, uint8_t* k_codes, float* k_scales,
+                              uint8_t* v_codes, float* v_scales, int64_t cache_cap, int64_t tok_offset,
+                              int32_t head_dim, int32_t bits, void* stream) {
+  static const char* fn = "iq_quantize_kv";
+  iq::clear_error();
+  int rc = check_dims(fn, head_dim, bits);
+  if (rc) return rc;
+  if (dtype != IQ_F32 && dtype != IQ_BF16) {
+    iq::set_error("%s: unknown dtype %d", fn, dtype);
+    return IQ_EUNSUPPORTED;
+  }
+  if (n_seq < 1 || n_seq > 65535 || n_heads < 1 || n_heads > 65535 || n_tokens < 0) {
+    iq::set_error("%s: need 1 <= n_seq <= 65535, 1 <= n_heads <= 65535, n_tokens >= 0", fn);
+    return IQ_EINVAL;
+  }
+  if (n_tokens == 0) return IQ_OK;   // nothing to do (empty inputs may have NULL data pointers)
+  if (k == nullptr && v == nullptr) {
+    iq::set_error("%s: k and v are both NULL", fn);
+    return IQ_EINVAL;
+  }
+  if ((k && (!k_codes || !k_scales)) || (v && (!v_codes || !v_scales))) {
+    iq::set_error("%s: codes/scales output missing for a side that has input", fn);
+    return IQ_EINVAL;
+  }
+  if (rot == nullptr || rot_stride_seq < 0 || stride_seq < 0 || stride_head < 0 || stride_tok < 0) {
+    iq::set_error("%s: rot is NULL or a stride is negative", fn);
+    return IQ_EINVAL;
+  }
+  if (cache_cap < 1 || tok_offset < 0 || tok_offset + n_tokens > cache_cap) {
+    iq::set_error("%s: need cache_cap >= 1, tok_offset >= 0, tok_offset + n_tokens <= cache_cap", fn);
+    return IQ_EINVAL;
+  }
+  const int64_t vec_align = dtype == IQ_BF16 ? 8 : 4;   // 16 bytes
+  if ((stride_seq % vec_align) || (stride_head % vec_align) || (stride_tok % vec_align) ||
+      (k && !aligned(k, 16)) || (v && !aligned(v, 16))) {
+    iq::set_error("%s: inputs must be 16-byte aligned with strides a multiple of 16 bytes", fn);
+    return IQ_EINVAL;
+  }
+  if ((k && (!aligned(k_codes, 4) || !aligned(k_scales, 4))) || (v && (!aligned(v_codes, 4) || !aligned(v_scales, 4))) ||
+      !aligned(rot, 4)) {
+    iq::set_error("%s: codes, scales and rot must be 4-byte aligned", fn);
+    return IQ_EINVAL;
+  }
+  iq::QuantizeLaunch a{};
+  a.side[0] = {k, k ? k_codes : nullptr, k ? k_scales : nullptr};
+  a.side[1] = {v, v ? v_codes : nullptr, v ? v_scales : nullptr};
+  a.bf16 = dtype == IQ_BF16;
+  a.n_seq = n_seq;
+  a.n_heads = n_heads;
+  a.n_tokens = n_tokens;
+  a.stride_seq = stride_seq;
+  a.stride_head = stride_head;
+  a.stride_tok = stride_tok;
+  a.rot = rot;
+  a.rot_stride_seq = rot_stride_seq;
+  a.cache_cap = cache_cap;
+  a.tok_offset = tok_offset;
+  const hipError_t err = iq::launch_quantize(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
+    return IQ_EHIP;
+  }
+  return IQ_OK;
+}
+
+namespace {
+
+int check_decode_sizes(const char* fn, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap) {
+  if (batch < 1 || batch > 65535 || n_q_heads < 1 || n_kv_heads < 1 || cache_cap < 1) {
+    iq::set_error("%s: need 1 <= batch <= 65535, n_q_heads >= 1, n_kv_heads >= 1, cache_cap >= 1", fn);
+    return IQ_EINVAL;
+  }
+  if (n_q_heads % n_kv_heads != 0) {
+    iq::set_error("%s: n_q_heads (%d) must be a multiple of n_kv_heads (%d)", fn, n_q_heads, n_kv_heads);
+    return IQ_EINVAL;
+  }
+  const int64_t gy = (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 7) / 8);
+  if (gy > 65535 || (int64_t)batch * n_q_heads > 0x7FFFFFFF || cache_cap > ((int64_t)1 << 40)) {
+    iq::set_error("%s: sizes exceed the launch limits", fn);
+    return IQ_EINVAL;
+  }
+  return IQ_OK;
+}
+
+}  // namespace
+
+extern "C" int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                             int64_t cache_cap) {
+  iq::clear_error();
+  const int rc = check_decode_sizes("iq_decode_workspace_bytes", batch, n_q_heads, n_kv_heads, cache_cap);
+  if (rc) return rc;
+  return iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap).workspace_bytes;
+}
+
+extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t* k_codes, const float* k_scales,
+                                   const uint8_t* v_codes, const float* v_scales, const float* rot,
+                                   int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap, float sm_scale,
+                                   float* out, void* workspace, int64_t workspace_bytes, int32_t head_dim,
+                                   int32_t bits, void* stream) {
+  static const char* fn = "iq_decode_attention";
+  iq::clear_error();
+  int rc = check_dims(fn, head_dim, bits);
+  if (rc) return rc;
+  if (q_dtype != IQ_F32 && q_dtype != IQ_BF16) {
+    iq::set_error("%s: unknown q_dtype %d", fn, q_dtype);
+    return IQ_EUNSUPPORTED;
+  }
+  rc = check_decode_sizes(fn, batch, n_q_heads, n_kv_heads, cache_cap);
+  if (rc) return rc;
+  if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !rot || !out) {
+    iq::set_error("%s: a required pointer is NULL", fn);
+    return IQ_EINVAL;
+  }
+  if (rot_stride_batch < 0) {
+    iq::set_error("%s: rot_stride_batch must be >= 0", fn);
+    return IQ_EINVAL;
+  }
+  if (!aligned(k_codes, 4) || !aligned(v_codes, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
+      !aligned(rot, 4) || !aligned(out, 4) || !aligned(q, q_dtype == IQ_BF16 ? 2 : 4) ||
+      (seq_lens && !aligned(seq_lens, 4))) {
+    iq::set_error("%s: misaligned pointer", fn);
+    return IQ_EINVAL;
+  }
+  const iq::DecodeGeometry geo = iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap);
+  if (!workspace || workspace_bytes < geo.workspace_bytes || !aligned(workspace, 256)) {
+    iq::set_error("%s: workspace must be 256-byte aligned and hold %lld bytes (got %lld)", fn,
+                  (long long)geo.workspace_bytes, (long long)workspace_bytes);
+    return IQ_EWORKSPACE;
+  }
+  iq::DecodeLaunch a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == IQ_BF16;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.v_codes = v_codes;
+  a.v_scales = v_scales;
+  a.rot = rot;
+  a.rot_stride_batch = rot_stride_batch;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.cache_cap = cache_cap;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.workspace = workspace;
+  const hipError_t err = iq::launch_decode(a, geo, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
+    return IQ_EHIP;
+  }
+  return IQ_OK;
+}

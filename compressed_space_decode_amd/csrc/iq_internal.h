@@ -1,0 +1,62 @@
+// Internal interface between the C-ABI entry points and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace iq {
+
+void set_error(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+void clear_error();
+
+// One side (K or V) of a quantize call.
+struct QuantSide {
+  const void* src;      // input vectors (bf16 bits or f32)
+  uint8_t* codes;       // [n_seq][n_heads][cap][48]
+  float* scales;        // [n_seq][n_heads][cap]
+};
+
+struct QuantizeLaunch {
+  QuantSide side[2];    // K, V (src == nullptr: side skipped)
+  int bf16;
+  int64_t n_seq;
+  int n_heads;
+  int64_t n_tokens;
+  int64_t stride_seq, stride_head, stride_tok;   // elements
+  const float* rot;
+  int64_t rot_stride_seq;                        // floats
+  int64_t cache_cap, tok_offset;
+};
+
+hipError_t launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
+
+struct DecodeLaunch {
+  const void* q;
+  int q_bf16;
+  const uint8_t* k_codes;
+  const float* k_scales;
+  const uint8_t* v_codes;
+  const float* v_scales;
+  const float* rot;
+  int64_t rot_stride_batch;
+  const int32_t* seq_lens;
+  int batch, n_q_heads, n_kv_heads;
+  int64_t cache_cap;
+  float sm_scale;
+  float* out;
+  void* workspace;
+};
+
+// Split-K geometry shared by the workspace query and the launch.
+struct DecodeGeometry {
+  int chunk;          // tokens per work-group (multiple of 128)
+  int n_chunks;       // ceil(cache_cap / chunk)
+  int head_groups;    // ceil(G / 8): query heads are processed 8 at a time
+  int64_t workspace_bytes;
+};
+
+DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t cache_cap);
+
+hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipStream_t stream);
+
+}  // namespace iq

@@ -1,0 +1,170 @@
+"""Thin Python binding of libiq (ctypes).  Argument marshalling only: every
+step of the method runs in the HIP kernels behind the C ABI (include/iq.h).
+
+PyTorch is used for device memory and the current HIP stream.  There is no
+fallback: if libiq.so is missing or fails to load, importing the functions
+raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libiq.so")
+
+IQ_OK, IQ_EINVAL, IQ_EUNSUPPORTED, IQ_EWORKSPACE, IQ_EHIP = 0, -1, -2, -3, -4
+IQ_F32, IQ_BF16 = 0, 1
+HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS = 128, 3, 48, 256
+
+# (name, restype, argtypes) of every entry point declared in include/iq.h
+_P = ctypes.c_void_p
+_I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+SIGNATURES = {
+    "iq_last_error": (ctypes.c_char_p, []),
+    "iq_make_rotation": (ctypes.c_int, [_U64, _I32, _P]),
+    "iq_quantize_kv": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64,
+                                      _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
+    "iq_decode_workspace_bytes": (_I64, [_I32, _I32, _I32, _I64]),
+    "iq_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                           _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
+}
+
+
+class IQError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("libiq error %d: %s" % (code, msg))
+        self.code = code
+
+
+_lib = None
+
+
+def lib():
+    """Load libiq.so once (raises ImportError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libiq.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(rc):
+    if rc != IQ_OK:
+        raise IQError(rc, lib().iq_last_error().decode())
+
+
+def last_error():
+    return lib().iq_last_error().decode()
+
+
+# ----------------------------------------------------------------------------
+def make_rotation(seed, n_heads):
+    """float32 numpy [n_heads][32][8] rotation parameters (host, seeded)."""
+    out = np.zeros((int(n_heads), 32, 8), dtype=np.float32)
+    _check(lib().iq_make_rotation(int(seed) & ((1 << 64) - 1), int(n_heads), out.ctypes.data))
+    return out
+
+
+def _stream(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return IQ_F32
+    if t.dtype == torch.bfloat16:
+        return IQ_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
+
+
+def quantize_kv(k, v, rot, k_codes, k_scales, v_codes, v_scales, tok_offset=0, shared_rot=False):
+    """Quantize K and/or V [n_seq][n_heads][n_tokens][128] (cuda, f32/bf16, last dim
+    contiguous) into the cache (codes uint8 [n_seq][n_heads][cap][48], scales float32
+    [n_seq][n_heads][cap]).  ``rot`` is float32 [n_seq][n_heads][32][8] on the device
+    (or [n_heads][32][8] with shared_rot=True).  Either k or v may be None."""
+    ref = k if k is not None else v
+    n_seq, n_heads, n_tokens, d = ref.shape
+    if d != HEAD_DIM:
+        raise ValueError("head dim must be 128")
+    for t in (k, v):
+        if t is not None and (t.shape != ref.shape or t.stride() != ref.stride() or t.dtype != ref.dtype):
+            raise ValueError("k and v must share shape, strides and dtype")
+        if t is not None and t.stride(3) != 1:
+            raise ValueError("coordinates must be contiguous")
+    cache = k_codes if k is not None else v_codes
+    cap = cache.shape[2]
+    for c, sc, t in ((k_codes, k_scales, k), (v_codes, v_scales, v)):
+        if t is None:
+            continue
+        if (tuple(c.shape) != (n_seq, n_heads, cap, RECORD_BYTES) or tuple(sc.shape) != (n_seq, n_heads, cap)
+                or not c.is_contiguous() or not sc.is_contiguous()):
+            raise ValueError("cache must be contiguous codes [n_seq][n_heads][cap][48] and scales [n_seq][n_heads][cap]")
+    want_rot = (n_heads if shared_rot else n_seq * n_heads) * ROT_PARAMS
+    if rot.numel() != want_rot or not rot.is_contiguous():
+        raise ValueError("rot must be a contiguous float32 tensor of %d values" % want_rot)
+    rot_stride = 0 if shared_rot else n_heads * ROT_PARAMS
+    rc = lib().iq_quantize_kv(
+        k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+        _dtype_code(ref), n_seq, n_heads, n_tokens,
+        ref.stride(0), ref.stride(1), ref.stride(2),
+        rot.data_ptr(), rot_stride,
+        k_codes.data_ptr() if k is not None else None, k_scales.data_ptr() if k is not None else None,
+        v_codes.data_ptr() if v is not None else None, v_scales.data_ptr() if v is not None else None,
+        cap, int(tok_offset), HEAD_DIM, BITS, _stream(ref))
+    _check(rc)
+
+
+def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, cache_cap):
+    n = lib().iq_decode_workspace_bytes(int(batch), int(n_q_heads), int(n_kv_heads), int(cache_cap))
+    if n < 0:
+        raise IQError(int(n), last_error())
+    return int(n)
+
+
+def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None, sm_scale=0.0,
+                     out=None, workspace=None, shared_rot=False):
+    """One decode step on the packed cache.  q [B][Hq][128] (cuda f32/bf16, contiguous);
+    caches [B][Hkv][cap][48] / [B][Hkv][cap]; rot float32 [B][Hkv][32][8] (or [Hkv][32][8]
+    with shared_rot=True); seq_lens int32 [B] on the device or None.  Returns out
+    float32 [B][Hq][128]."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    if d != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B][Hq][128]")
+    for t in (k_codes, k_scales, v_codes, v_scales, rot):
+        if not t.is_contiguous():
+            raise ValueError("cache and rotation tensors must be contiguous")
+    for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
+        if tuple(c.shape) != (B, Hkv, cap, RECORD_BYTES) or tuple(sc.shape) != (B, Hkv, cap):
+            raise ValueError("caches must be [B][Hkv][cap][48] codes and [B][Hkv][cap] scales")
+    if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
+        raise ValueError("rot has the wrong number of values")
+    if seq_lens is not None and seq_lens.numel() != B:
+        raise ValueError("seq_lens must hold one length per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, cap)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be a contiguous int32 tensor")
+    rc = lib().iq_decode_attention(
+        q.data_ptr(), _dtype_code(q), k_codes.data_ptr(), k_scales.data_ptr(),
+        v_codes.data_ptr(), v_scales.data_ptr(), rot.data_ptr(),
+        0 if shared_rot else Hkv * ROT_PARAMS,
+        seq_lens.data_ptr() if seq_lens is not None else None,
+        B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        HEAD_DIM, BITS, _stream(q))
+    _check(rc)
+    return out

@@ -1,0 +1,170 @@
+/*
+ * iq.h -- C ABI of libiq: IsoQuant 3-bit KV compression and decode attention
+ * computed directly on the packed codes, for AMD MI355X (gfx950).
+ *
+ * Method: "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via
+ * Fused Compressed-Space Attention" (arXiv 2608.08081), Abstract.  Each
+ * key/value head vector (d = 128) goes through a Walsh-Hadamard transform,
+ * then a block-diagonal SO(4) rotation (256 stored parameters per head),
+ * then 3-bit scalar quantization; attention then runs on the packed 3-bit
+ * tensors without materialising full-precision KV.
+ *
+ * Conventions (all entry points):
+ *   - Return IQ_OK (0) or a negative IQ_E* code; iq_last_error() then holds
+ *     a message (thread-local, valid until the next call on that thread).
+ *   - Pointers are DEVICE pointers unless the argument is marked "host".
+ *     All device buffers are owned by the caller; the library never
+ *     allocates, frees or synchronises inside these calls.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
+ *     the default stream) and is complete when the stream reaches it.
+ *   - Every argument is validated before anything is launched, so an error
+ *     return means nothing was enqueued.
+ *   - head_dim must be 128 and bits must be 3 (IQ_EUNSUPPORTED otherwise).
+ *
+ * Data layouts (the pages only say "packed 3-bit tensors"; these are this
+ * library's readings):
+ *   rotation params  float[.][32][8] per head: block b acts on coordinates
+ *                    4b..4b+3 as v -> qL * v * conj(qR) (Hamilton product,
+ *                    components (w,x,y,z)), params[b][0:4] = qL,
+ *                    params[b][4:8] = qR.  Quaternions are normalised before
+ *                    use.  The rotation is R = blockdiag(M_b) * H with H the
+ *                    normalised Sylvester Walsh-Hadamard matrix.
+ *   quantizer        x' = R x; s = max|x'| / 3.5 (fp32, one per vector);
+ *                    code = clamp(floor(x'/s + 4), 0, 7); level s*(c-3.5);
+ *                    a zero vector gives s = 0 and all codes 4.
+ *   code record      48 bytes per vector: four 12-byte quarters, quarter q
+ *                    holds coordinates 32q..32q+31 in two halves of 16
+ *                    (half h = 32q+16h .. 32q+16h+15) as six little-endian
+ *                    16-bit words u_0..u_5; word u_(2k+h), k = 0..2, belongs
+ *                    to half h: its bits 3j..3j+2 hold coordinate
+ *                    32q+16h+5k+j (j<5) and its bit 15 holds bit k of
+ *                    coordinate 32q+16h+15.
+ *   KV cache         codes uint8[n_seq][n_heads][cache_cap][48] and scales
+ *                    float[n_seq][n_heads][cache_cap], contiguous.
+ */
+#ifndef IQ_H
+#define IQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  IQ_OK = 0,
+  IQ_EINVAL = -1,        /* null pointer, bad count, stride or shape */
+  IQ_EUNSUPPORTED = -2,  /* head_dim != 128, bits != 3, unknown dtype */
+  IQ_EWORKSPACE = -3,    /* workspace missing or smaller than required */
+  IQ_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+};
+
+enum { IQ_F32 = 0, IQ_BF16 = 1 };
+
+#define IQ_HEAD_DIM 128
+#define IQ_BITS 3
+#define IQ_RECORD_BYTES 48
+#define IQ_ROT_PARAMS 256
+
+/* Message describing the last error on the calling thread ("" if none). */
+const char* iq_last_error(void);
+
+/*
+ * iq_make_rotation -- draw rotation parameters (host only, no GPU work).
+ * Source: Abstract ("256 stored parameters per head").  How the parameters
+ * are drawn is not stated; this draws each block's left and right
+ * quaternions uniformly on the 3-sphere: SplitMix64 (Steele, Lea, Flood
+ * 2014) outputs z_i = mix(seed + (i+1)*0x9E3779B97F4A7C15) give uniforms
+ * v = (z >> 11) * 2^-52 - 1 on [-1, 1); Marsaglia's 1972 method turns them
+ * into a point on S^3 (x1,x2 with s1 = x1^2+x2^2 < 1; x3,x4 with
+ * 0 < s2 = x3^2+x4^2 < 1; then (x1, x2, x3 f, x4 f), f = sqrt((1-s1)/s2)),
+ * in the order head, block, qL then qR; components rounded to fp32.
+ *   seed         any 64-bit value; the output is a pure function of it.
+ *   n_heads      >= 1.
+ *   params_host  host buffer of n_heads*256 floats, [n_heads][32][8].
+ * Errors: IQ_EINVAL for n_heads < 1 or a NULL buffer.
+ */
+int iq_make_rotation(uint64_t seed, int32_t n_heads, float* params_host);
+
+/*
+ * iq_quantize_kv -- rotate, 3-bit quantize and pack K and/or V vectors into
+ * the KV cache.  Source: Abstract (WHT, then block-diagonal SO(4), then
+ * 3-bit scalar quantization; packed 3-bit tensors).
+ *   k, v         input vectors, dtype IQ_F32 or IQ_BF16, element (s,h,t,i)
+ *                at k[s*stride_seq + h*stride_head + t*stride_tok + i]
+ *                (strides in elements, coordinates i contiguous).  Either k
+ *                or v may be NULL, and that side is skipped (its code and
+ *                scale pointers may then be NULL too).
+ *   n_seq        sequences (or layers) >= 1; n_heads >= 1; n_tokens >= 0
+ *                (0 is a no-op).
+ *   rot          params of (s,h) at rot + s*rot_stride_seq + h*256 (floats);
+ *                rot_stride_seq = 0 shares one set of heads across s.
+ *                K and V of a head share its rotation.
+ *   k_codes ...  cache arrays [n_seq][n_heads][cache_cap][48] / [...][cache_cap];
+ *                token t is written at cache position tok_offset + t.
+ *   cache_cap    >= tok_offset + n_tokens.
+ * Errors: IQ_EINVAL (NULL where required, non-positive sizes, negative
+ * strides or offset, tok_offset + n_tokens > cache_cap, misaligned input
+ * pointers or strides that are not multiples of 8 elements for bf16 / 4
+ * for f32), IQ_EUNSUPPORTED, IQ_EHIP.
+ */
+int iq_quantize_kv(const void* k, const void* v, int32_t dtype,
+                   int64_t n_seq, int32_t n_heads, int64_t n_tokens,
+                   int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
+                   const float* rot, int64_t rot_stride_seq,
+                   uint8_t* k_codes, float* k_scales,
+                   uint8_t* v_codes, float* v_scales,
+                   int64_t cache_cap, int64_t tok_offset,
+                   int32_t head_dim, int32_t bits, void* stream);
+
+/*
+ * iq_decode_workspace_bytes -- device workspace that iq_decode_attention
+ * needs for its split-K partial results with these sizes (the split size
+ * is chosen by the library from the same arguments).  Negative IQ_E* code
+ * on invalid sizes.
+ */
+int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
+                                  int32_t n_kv_heads, int64_t cache_cap);
+
+/*
+ * iq_decode_attention -- one decode step of attention computed on the
+ * packed cache.  Source: Abstract ("performs attention directly on packed
+ * 3-bit tensors without materializing full-precision KV state").  The
+ * query is rotated into the compressed space, codes are turned into
+ * numbers only in registers, softmax is online and split over the
+ * sequence, V is accumulated in rotated space and rotated back once per
+ * output row.
+ *   q            [batch][n_q_heads][128], q_dtype IQ_F32 or IQ_BF16.
+ *   k_*, v_*     the cache written by iq_quantize_kv, [batch][n_kv_heads]
+ *                [cache_cap][48] codes and [batch][n_kv_heads][cache_cap]
+ *                scales.
+ *   rot          params of (b,g) at rot + b*rot_stride_batch + g*256;
+ *                rot_stride_batch = 0 shares them across the batch (a
+ *                layer-stacked call passes n_kv_heads*256).
+ *   seq_lens     device int32[batch], 0 <= len <= cache_cap; NULL means
+ *                every sequence has cache_cap tokens.  Positions >= len are
+ *                never read into the result.
+ *   query head h attends with KV head h / (n_q_heads / n_kv_heads).
+ *   sm_scale     softmax scale; <= 0 selects 1/sqrt(128).
+ *   out          float [batch][n_q_heads][128]; a sequence with len 0 gets
+ *                zeros.
+ *   workspace    device buffer of at least iq_decode_workspace_bytes(...)
+ *                bytes, 256-byte aligned, used only during the call.
+ * Errors: IQ_EINVAL (NULL pointers, sizes < 1, n_q_heads % n_kv_heads != 0,
+ * negative stride), IQ_EWORKSPACE, IQ_EUNSUPPORTED, IQ_EHIP.
+ */
+int iq_decode_attention(const void* q, int32_t q_dtype,
+                        const uint8_t* k_codes, const float* k_scales,
+                        const uint8_t* v_codes, const float* v_scales,
+                        const float* rot, int64_t rot_stride_batch,
+                        const int32_t* seq_lens,
+                        int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                        int64_t cache_cap, float sm_scale, float* out,
+                        void* workspace, int64_t workspace_bytes,
+                        int32_t head_dim, int32_t bits, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IQ_H */

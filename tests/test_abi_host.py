@@ -1,0 +1,124 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads and exports
+every entry point include/iq.h declares, argument validation returns the
+documented error codes before anything is launched, and iq_make_rotation
+reproduces the oracle's generator bit for bit."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import compressed_space_decode_amd as iq
+import oracle
+from compressed_space_decode_amd import iq as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
+                                  "iq_decode_workspace_bytes", "iq_decode_attention"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(iq.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert set(binding.SIGNATURES) == set(_declared())
+
+
+def test_make_rotation_matches_oracle_bit_for_bit():
+    for seed, n in [(0, 1), (1234567, 4), (2 ** 64 - 1, 3), (42, 192)]:
+        got = iq.make_rotation(seed, n)
+        want = oracle.make_rotation(seed, n)
+        assert got.shape == (n, 32, 8)
+        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_make_rotation_errors():
+    lib = iq.lib()
+    assert lib.iq_make_rotation(1, 0, ctypes.c_void_p(16)) == binding.IQ_EINVAL
+    assert "n_heads" in binding.last_error()
+    assert lib.iq_make_rotation(1, 2, None) == binding.IQ_EINVAL
+
+
+FAKE = 1 << 20   # an aligned non-null address; validation fails before any use
+
+
+def _quant(**kw):
+    args = dict(k=FAKE, v=FAKE, dtype=1, n_seq=1, n_heads=1, n_tokens=4, ss=512, sh=512, st=128,
+                rot=FAKE, rs=256, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, cap=4, off=0, hd=128, bits=3)
+    args.update(kw)
+    return iq.lib().iq_quantize_kv(args["k"], args["v"], args["dtype"], args["n_seq"], args["n_heads"],
+                                   args["n_tokens"], args["ss"], args["sh"], args["st"], args["rot"], args["rs"],
+                                   args["kc"], args["ks"], args["vc"], args["vs"], args["cap"], args["off"],
+                                   args["hd"], args["bits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hd=64), binding.IQ_EUNSUPPORTED),
+    (dict(bits=4), binding.IQ_EUNSUPPORTED),
+    (dict(dtype=7), binding.IQ_EUNSUPPORTED),
+    (dict(k=None, v=None), binding.IQ_EINVAL),
+    (dict(kc=None), binding.IQ_EINVAL),
+    (dict(rot=None), binding.IQ_EINVAL),
+    (dict(n_seq=0), binding.IQ_EINVAL),
+    (dict(n_heads=70000), binding.IQ_EINVAL),
+    (dict(n_tokens=-1), binding.IQ_EINVAL),
+    (dict(off=1), binding.IQ_EINVAL),            # 1 + 4 > cap
+    (dict(st=-128), binding.IQ_EINVAL),
+    (dict(st=100), binding.IQ_EINVAL),           # not a multiple of 16 bytes
+    (dict(k=FAKE + 2), binding.IQ_EINVAL),       # misaligned input
+    (dict(n_tokens=0), binding.IQ_OK),           # no-op, nothing launched
+])
+def test_quantize_validation(kw, code):
+    assert _quant(**kw) == code
+    if code != binding.IQ_OK:
+        assert binding.last_error().startswith("iq_quantize_kv")
+
+
+def _dec(**kw):
+    args = dict(q=FAKE, qd=1, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, rot=FAKE, rs=0, lens=None, B=1, Hq=8, Hkv=2,
+                cap=1000, sm=0.0, out=FAKE, ws=FAKE, wsb=1 << 30, hd=128, bits=3)
+    args.update(kw)
+    return iq.lib().iq_decode_attention(args["q"], args["qd"], args["kc"], args["ks"], args["vc"], args["vs"],
+                                        args["rot"], args["rs"], args["lens"], args["B"], args["Hq"], args["Hkv"],
+                                        args["cap"], args["sm"], args["out"], args["ws"], args["wsb"],
+                                        args["hd"], args["bits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hd=96), binding.IQ_EUNSUPPORTED),
+    (dict(bits=2), binding.IQ_EUNSUPPORTED),
+    (dict(qd=3), binding.IQ_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), binding.IQ_EINVAL),
+    (dict(B=0), binding.IQ_EINVAL),
+    (dict(cap=0), binding.IQ_EINVAL),
+    (dict(q=None), binding.IQ_EINVAL),
+    (dict(vs=None), binding.IQ_EINVAL),
+    (dict(rs=-1), binding.IQ_EINVAL),
+    (dict(kc=FAKE + 1), binding.IQ_EINVAL),
+    (dict(ws=None), binding.IQ_EWORKSPACE),
+    (dict(wsb=16), binding.IQ_EWORKSPACE),
+    (dict(ws=FAKE + 64), binding.IQ_EWORKSPACE),  # not 256-byte aligned
+])
+def test_decode_validation(kw, code):
+    assert _dec(**kw) == code
+    assert binding.last_error().startswith("iq_decode_attention")
+
+
+def test_workspace_bytes():
+    n = iq.decode_workspace_bytes(1, 32, 4, 32768)
+    assert n > 0
+    # partials: (o' [128] + max + sum) floats per (sequence, query head, chunk)
+    assert (n - 256) % (130 * 4) == 0
+    assert iq.lib().iq_decode_workspace_bytes(1, 6, 4, 100) == binding.IQ_EINVAL
+    assert iq.decode_workspace_bytes(16, 32, 8, 32768) >= iq.decode_workspace_bytes(1, 32, 8, 32768)
