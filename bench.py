@@ -1,0 +1,258 @@
+"""Benchmark: 3-bit compressed-space decode attention at 32K context on one MI355X.
+
+One step is one decode step of a 48-layer model whose every layer has the
+long-context shape (batch 1, 32 query heads, 4 KV heads, head_dim 128, 32768
+cached tokens, bf16 K/V/Q drawn as in the long32k workload): the new token's
+K and V of all layers are rotated, quantized and packed into the caches
+(iq_quantize_kv, one call), then attention of all layers runs on the packed
+caches (iq_decode_attention, one layer-stacked call: layers are passed as
+batch entries, each with its own rotation).  Inputs are resident in HBM
+before the timed region.
+
+Prints one JSON line.  `value` is KV tokens/s: cached token positions
+attended per second, summed over layers, each position covering all 4 KV
+heads.  The roofline object is for the decode call (split-K kernel plus its
+small combine kernel), timed with HIP events on the stream it runs on; its
+algorithmic bytes are the packed K/V codes and scales read, 104 bytes per
+(token, KV head).  Extra fields report a single-layer decode call and the
+bulk prefill quantization (48 layers x 4 KV heads x 32768 tokens, K and V
+Student-t(3), bf16) against the same roofline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+LAYERS, HQ, HKV, T, D = 48, 32, 4, 32768, 128
+BYTES_PER_TOKEN_HEAD = 2 * (48 + 4)          # K and V: 48-byte record + fp32 scale
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layers", type=int, default=LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
+                         "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the timed decode steps (for counter runs); prints the JSON line")
+    return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20)
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n, "copies": 5}), flush=True)
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def time_calls(fn, iters, stream):
+    """Average duration (s) of fn() over iters calls, HIP events on `stream`."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(iters):
+        fn()
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / iters
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+    import torch
+
+    import compressed_space_decode_amd as iq
+    from compressed_space_decode_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    L = args.layers
+
+    # ---------------- inputs (seeded, synthetic) ----------------
+    t0 = time.time()
+    w = W.decode_workload("long32k", batch=L)
+    log("generated %d layers of long32k inputs in %.1fs" % (L, time.time() - t0))
+
+    def bf16(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    k_all = bf16(w["k"])                      # [L][Hkv][T][128]
+    v_all = bf16(w["v"])
+    q = bf16(w["q"])                          # [L][Hq][128]
+    rot = torch.from_numpy(w["params"]).to(dev)   # [L][Hkv][32][8]
+    del w
+    kc = torch.empty((L, HKV, T, 48), dtype=torch.uint8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((L, HKV, T), dtype=torch.float32, device=dev)
+    vs = torch.empty_like(ks)
+    iq.quantize_kv(k_all, v_all, rot, kc, ks, vc, vs)          # prefill the caches
+    lens = torch.full((L,), T, dtype=torch.int32, device=dev)
+    out = torch.empty((L, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(iq.decode_workspace_bytes(L, HQ, HKV, T), dtype=torch.uint8, device=dev)
+    k_new = k_all[:, :, T - 1:T]              # the step's new token: position T-1 of every layer
+    v_new = v_all[:, :, T - 1:T]
+    torch.cuda.synchronize()
+
+    def append():
+        iq.quantize_kv(k_new, v_new, rot, kc, ks, vc, vs, tok_offset=T - 1)
+
+    def decode():
+        iq.decode_attention(q, kc, ks, vc, vs, rot, seq_lens=lens, out=out, workspace=ws)
+
+    def step():
+        append()
+        decode()
+
+    # ---------------- timed steps ----------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_step = time_calls(step, args.steps, stream)
+    t_decode = time_calls(decode, args.steps, stream)
+    t_append = time_calls(append, args.steps, stream)
+    log("step %.1f us (decode %.1f us, append %.1f us)" % (t_step * 1e6, t_decode * 1e6, t_append * 1e6))
+
+    decode_bytes = L * T * HKV * BYTES_PER_TOKEN_HEAD
+    decode_gbs = decode_bytes / t_decode / 1e9
+    tokens_per_step = L * T
+
+    if args.decode_only:
+        print(json.dumps({"decode_us": t_decode * 1e6, "step_us": t_step * 1e6,
+                          "decode_GBs": decode_bytes / t_decode / 1e9}), flush=True)
+        return
+
+    # single-layer decode call (the one-layer shape, unadjusted)
+    ws1 = torch.empty(iq.decode_workspace_bytes(1, HQ, HKV, T), dtype=torch.uint8, device=dev)
+    out1 = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
+
+    def decode1():
+        iq.decode_attention(q[:1], kc[:1], ks[:1], vc[:1], vs[:1], rot[:1], seq_lens=lens[:1], out=out1,
+                            workspace=ws1)
+
+    for _ in range(args.warmup):
+        decode1()
+    t_decode1 = time_calls(decode1, args.steps, stream)
+    single = {"ms": t_decode1 * 1e3, "GBs": T * HKV * BYTES_PER_TOKEN_HEAD / t_decode1 / 1e9,
+              "kv_tokens_per_s": T / t_decode1}
+
+    # ---------------- bulk prefill quantization ----------------
+    prefill = None
+    if not args.no_prefill:
+        del k_all, v_all
+        torch.cuda.empty_cache()
+        t0 = time.time()
+        data = W.prefill_layers(range(LAYERS))
+        pk = torch.empty((LAYERS, HKV, T, D), dtype=torch.bfloat16, device=dev)
+        pv = torch.empty_like(pk)
+        prot = torch.from_numpy(np.stack([d[2] for d in data])).to(dev)
+        for l, (kk, vv, _) in enumerate(data):
+            pk[l] = bf16(kk)
+            pv[l] = bf16(vv)
+        del data
+        log("generated prefill inputs in %.1fs" % (time.time() - t0))
+        pkc = torch.empty((LAYERS, HKV, T, 48), dtype=torch.uint8, device=dev)
+        pvc = torch.empty_like(pkc)
+        pks = torch.empty((LAYERS, HKV, T), dtype=torch.float32, device=dev)
+        pvs = torch.empty_like(pks)
+
+        def quant():
+            iq.quantize_kv(pk, pv, prot, pkc, pks, pvc, pvs)
+
+        quant()
+        torch.cuda.synchronize()
+        t_q = time_calls(quant, max(3, args.steps // 4), stream)
+        qbytes = LAYERS * HKV * T * 2 * (D * 2 + 48 + 4)
+        prefill = {"workload": "prefill 48x4x32768 K+V bf16 Student-t(3)", "ms": t_q * 1e3,
+                   "GBs": qbytes / t_q / 1e9, "frac_of_hbm_peak": qbytes / t_q / 1e9 / HBM_PEAK_GBS,
+                   "vectors_per_s": LAYERS * HKV * T * 2 / t_q}
+        log("prefill quantize %.2f ms, %.0f GB/s" % (t_q * 1e3, prefill["GBs"]))
+
+    # ---------------- CPU oracle baseline ----------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            blas_threads = 1
+        kcn, ksn, vcn, vsn = kc.cpu().numpy(), ks.cpu().numpy(), vc.cpu().numpy(), vs.cpu().numpy()
+        qn = q.float().cpu().numpy().astype(np.float64)
+        rotn = rot.cpu().numpy()
+        done, t0 = 0, time.time()
+        while done < L and (done == 0 or time.time() - t0 < args.cpu_seconds):
+            l = done
+            oracle.decode_attention(qn[l:l + 1], oracle.unpack(kcn[l:l + 1]), ksn[l:l + 1],
+                                    oracle.unpack(vcn[l:l + 1]), vsn[l:l + 1], rotn[l:l + 1], np.array([T]))
+            done += 1
+        el = time.time() - t0
+        cpu = {"value": done * T / el, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
+               "sample": "%d of %d layers (4 KV heads, 32 query heads, 32768 tokens each): oracle unpack of the "
+                         "packed caches + fp64 decode attention, %.1f s; numpy single-threaded except BLAS" %
+                         (done, L, el)}
+        log("cpu oracle: %d layers in %.1fs" % (done, el))
+
+    res = {
+        "metric": "3-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% peak) at 32K",
+        "value": tokens_per_step / t_step,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": t_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "long32k decode step x%d layers (per layer: batch 1, 32 query / 4 KV heads, "
+                               "head_dim 128, 32768 cached tokens, bf16 inputs, 3-bit packed KV; append the new "
+                               "token's K/V, then layer-stacked decode attention)" % L,
+                   "layers": L, "batch": 1, "n_q_heads": HQ, "n_kv_heads": HKV, "context": T,
+                   "head_dim": D, "kv_bits": 3},
+        "roofline": {"bound": "hbm", "achieved": decode_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": decode_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "iq_decode_attention (decode_split_kernel + combine_kernel)",
+                     "algorithmic_bytes_per_launch": decode_bytes, "avg_launch_us": t_decode * 1e6},
+        "decode_ms": t_decode * 1e3,
+        "append_ms": t_append * 1e3,
+        "single_layer_decode": single,
+        "prefill_quantize": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -162,7 +162,7 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
     return IQ_EINVAL;
   }
   if (!aligned(k_codes, 4) || !aligned(v_codes, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
-      !aligned(rot, 4) || !aligned(out, 4) || !aligned(q, q_dtype == IQ_BF16 ? 2 : 4) ||
+      !aligned(rot, 4) || !aligned(out, 4) || !aligned(q, 16) ||
       (seq_lens && !aligned(seq_lens, 4))) {
     iq::set_error("%s: misaligned pointer", fn);
     return IQ_EINVAL;

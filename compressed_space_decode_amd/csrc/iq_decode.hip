@@ -7,24 +7,30 @@
 // once, V levels are summed in rotated space, and R^T is applied once per
 // output row.
 //
-// Kernel 1 (decode_split_kernel), one work-group of 4 waves per (sequence,
-// KV head, group of up to 8 query heads, chunk of tokens):
-//   * set-up: rotate the group's queries (WHT in LDS, then SO(4) blocks) and
-//     lay them out as the fp16 B operand of the QK product, hi and lo parts
-//     (q = hi + lo) in separate columns so the product carries ~22 bits;
-//   * each wave walks 32-token blocks.  A lane loads 12 bytes (one quarter of
-//     a record) of one token; one AND per pair of codes turns them into fp16
-//     numbers c * 2^(p-24) (subnormals, handled exactly by the matrix cores),
-//     the power 2^-p being folded into the query operand;
-//   * S^T[token][head,part] = codes x q' via v_mfma_f32_16x16x32_f16, online
-//     softmax in base 2, P'' = p s_V (scaled) split hi/lo in fp16;
+// Kernel 1 (decode_split_kernel): one work-group of 4 waves per (sequence,
+// KV head, group of up to 8 query heads, chunk of tokens).  Each wave works
+// on its own, with no work-group barrier until the final merge:
+//   * set-up: the wave rotates the group's queries in registers (8 lanes per
+//     head, 16 coordinates per lane: cross-lane Hadamard stages through DPP /
+//     swizzle, in-lane stages, then the 4x4 SO(4) blocks) and lays them out as
+//     the fp16 B operand of the QK product, hi and lo parts (q = hi + lo) in
+//     columns n and n+8 so the product carries ~22 bits;
+//   * loop over 32-token blocks, loads of block i+1 issued before block i is
+//     processed.  A lane loads 12 bytes (one quarter of a record) of one
+//     token; one AND per pair of codes turns them into fp16 subnormals
+//     c * 2^(p-24) that the matrix cores multiply exactly, the 2^-p being
+//     folded into the query operand;
+//   * S^T[token][head,part] = codes x q' on v_mfma_f32_16x16x32_f16; the hi and
+//     lo columns are summed with one DPP add; online softmax in base 2;
+//   * P'' = p * s_V * 4096 / vlim (vlim a running power of two above every V
+//     scale seen), split hi/lo in fp16, is the A operand of the PV product;
 //   * V codes of the block are unpacked the same way into LDS ([token][slot]
-//     rows) and read back transposed with ds_read_b64_tr_b16 as the B
-//     operand of O[head,part][slot] += P'' x V;
+//     rows) and read back transposed with ds_read_b64_tr_b16 as the B operand
+//     of O[head,part][slot] += P'' x V;
 //   * the 4 waves merge in LDS and write one (max, sum, o') partial.
-// Kernel 2 (combine_kernel), one work-group per (sequence, query head):
-//   log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
-//   blocks followed by the WHT).
+// Kernel 2 (combine_kernel): one work-group per (sequence, query head):
+// log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
+// blocks followed by the Hadamard transform).
 #include "iq_internal.h"
 
 namespace iq {
@@ -33,18 +39,20 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef unsigned uint4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 32;          // tokens per wave step
-constexpr int kRowHalves = 136;     // fp16 elements per LDS V row (128 + 8 padding)
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kPScale = 4096.f;   // P'' = p * (s_V / sigma) * 4096 keeps fp16 lo parts normal
+constexpr float kPScale = 4096.f;   // P'' <= 4096: the fp16 lo part stays in the normal range
+constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 
 // Coordinate (within a quarter) held by extraction slot s: the 16 words that
 // one quarter unpacks into carry coordinate (s >> 1) of half (s & 1).
 __device__ __forceinline__ int slot_coord(int s) { return 16 * (s & 1) + (s >> 1); }
-// Power of two carried by the fp16 value of slot s (field position p: value = c * 2^(p-24)).
+// Power of two carried by slot s: field position p gives the value c * 2^(p-24).
 __device__ __forceinline__ int slot_pow(int s) {
   const int d = s >> 1;
   if (d == 15) return 0;
@@ -69,11 +77,19 @@ __device__ __forceinline__ void unpack_quarter(unsigned w0, unsigned w1, unsigne
 }
 
 __device__ __forceinline__ half8 as_half8(unsigned a, unsigned b, unsigned c, unsigned d) {
-  typedef unsigned u4 __attribute__((ext_vector_type(4)));
-  u4 v = {a, b, c, d};
+  uint4v v = {a, b, c, d};
   return __builtin_bit_cast(half8, v);
 }
 
+__device__ __forceinline__ float dpp_xor1(float x) {   // quad_perm [1,0,3,2]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {   // quad_perm [2,3,0,1]
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor4(float x) {   // bitmask swizzle, xor 4
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (4 << 10) | 0x1F));
+}
 __device__ __forceinline__ float wave_xor(float x, int m) { return __shfl_xor(x, m, 64); }
 
 struct DecodeKArgs {
@@ -94,24 +110,22 @@ struct DecodeKArgs {
   float* part_ml;         // [B][Hq][n_chunks][2]  (max in log2 units, sum)
 };
 
-struct SetupSmem {
-  float qr[8][128];       // query rows, rotated in place
-  float mats[32][16];     // SO(4) blocks M_b
-  float red[kThreads];
-};
 struct MergeSmem {
   float o[kWaves][8][128];
   float m[kWaves][8];
   float l[kWaves][8];
 };
-struct LoopSmem {
-  _Float16 v[kWaves][kBlock][kRowHalves];
-  float sc[kWaves][64];
+// Per-wave loop staging: unpacked V block [32 tokens][128 slots] fp16 in rows of 288 bytes,
+// P'' block [32 tokens][16 (head, part)] fp16, and the block's K/V scales.
+constexpr int kVRow = 288;
+struct WaveLoopSmem {
+  char v[kBlock * kVRow];
+  char p[kBlock * 32];
+  float sc[64];
 };
 union DecodeSmem {
-  SetupSmem setup;
   MergeSmem merge;
-  LoopSmem loop;
+  WaveLoopSmem loop[kWaves];
 };
 
 __device__ void build_block(const float* p, float* out16) {
@@ -134,7 +148,194 @@ __device__ void build_block(const float* p, float* out16) {
     }
 }
 
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeKArgs a) {
+// V staging rows are 288 bytes apart (72 words: consecutive rows start 8 banks apart) and the
+// two 16-byte halves of each 32-byte sector are swapped in rows where bit 2 xor bit 3 of the row
+// is set.  With the token order of the PV product (rows 4*g4 + i/4 and 16 + 4*g4 + i/4), the
+// 16-byte row writes and the transposed 8-byte reads then hit distinct banks, and every read
+// address is a per-lane base plus an immediate.
+__device__ __forceinline__ int vhalf_flip(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+
+struct BlockData {
+  unsigned kw[2][3];
+  unsigned vw[2][3];
+  float sc;               // row group 0/1: K scale of token n / 16+n; 2/3: V scale of token n / 16+n
+};
+
+// Per-lane constant offsets of a 32-token block; the block base is uniform.
+struct LaneOffsets {
+  unsigned code[2];       // byte offset of this lane's quarter in tile tt (token 16*tt + n)
+  unsigned scale;         // token of this lane's scale load
+};
+
+__device__ __forceinline__ void load_block(BlockData& d, const uint8_t* kbase, const uint8_t* vbase,
+                                           const float* ksb, const float* vsb, int64_t t0, int64_t cap,
+                                           const LaneOffsets& lo, bool vscale) {
+  const float* sb = vscale ? vsb : ksb;
+  if (t0 + kBlock <= cap) {                                  // uniform: whole block inside the cache
+    const uint8_t* kb = kbase + t0 * 48;
+    const uint8_t* vb = vbase + t0 * 48;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const uint3 kq = *reinterpret_cast<const uint3*>(kb + lo.code[tt]);
+      const uint3 vq = *reinterpret_cast<const uint3*>(vb + lo.code[tt]);
+      d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
+      d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
+    }
+    d.sc = sb[t0 + lo.scale];
+  } else {                                                   // block reaches past the cache end
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      int64_t t = t0 + lo.code[tt] / 48;
+      t = t < cap ? t : cap - 1;
+      const int64_t off = t * 48 + lo.code[tt] % 48;
+      const uint3 kq = *reinterpret_cast<const uint3*>(kbase + off);
+      const uint3 vq = *reinterpret_cast<const uint3*>(vbase + off);
+      d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
+      d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
+    }
+    int64_t t = t0 + lo.scale;
+    t = t < cap ? t : cap - 1;
+    d.sc = sb[t];
+  }
+}
+
+// Running state of one wave's online softmax.  Lane (n, g4) owns heads 2*g4 and 2*g4+1.
+struct WaveState {
+  floatx4 O[8];           // O[(head, part)][slot]: rows 4*g4 + r = (head 2*g4 + r/2, part r%2)
+  float m_run[2];         // running max (log2 units), uniform over the 16 lanes of a row group
+  float l_run[2];         // sum of p over this lane's tokens
+  float ls_run[2];        // sum of P'' over this lane's tokens
+  int vexp;               // vlim = 2^vexp is above every V scale seen; -200: none yet
+};
+
+__device__ __forceinline__ float row_max(float x) {   // max over the 16 lanes of a row (DPP row_ror)
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, true)));
+  return x;
+}
+__device__ __forceinline__ float row_sum(float x) {   // sum over the 16 lanes of a row
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, true));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, true));
+  return x;
+}
+
+typedef __attribute__((address_space(3))) short4v* lds_s4;
+
+__device__ __forceinline__ void process_block(const BlockData& cur, int rem, WaveState& st, const half8 (&qop)[4],
+                                              float c1, const float (&c2)[2], WaveLoopSmem& ws, int lane, int n,
+                                              int g4, unsigned vw0, unsigned vw1, unsigned vrd, unsigned prd) {
+  ws.sc[lane] = cur.sc;
+  // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
+  floatx4 S[2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    unsigned u[16];
+    unpack_quarter(cur.kw[tt][0], cur.kw[tt][1], cur.kw[tt][2], u);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[kb],
+                                                  as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
+                                                  acc, 0, 0, 0);
+    S[tt] = acc;
+  }
+  // ---- V: unpack into the staging rows (read back transposed below) ----
+  char* vbytes = ws.v;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    unsigned u[16];
+    unpack_quarter(cur.vw[tt][0], cur.vw[tt][1], cur.vw[tt][2], u);
+    char* r0 = vbytes + 16 * tt * kVRow;
+    *reinterpret_cast<uint4*>(r0 + vw0) = make_uint4(u[0], u[1], u[2], u[3]);
+    *reinterpret_cast<uint4*>(r0 + vw1) = make_uint4(u[4], u[5], u[6], u[7]);
+    *reinterpret_cast<uint4*>(r0 + vw0 + 32) = make_uint4(u[8], u[9], u[10], u[11]);
+    *reinterpret_cast<uint4*>(r0 + vw1 + 32) = make_uint4(u[12], u[13], u[14], u[15]);
+  }
+  // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
+  const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
+  float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
+  float z[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    z[j][0] = sk0 * fmaf(S[0][2 * j] + S[0][2 * j + 1], c1, -c2[j]);
+    z[j][1] = sk1 * fmaf(S[1][2 * j] + S[1][2 * j + 1], c1, -c2[j]);
+  }
+  if (rem < kBlock) {                                         // last, partial block only
+    if (n >= rem) { z[0][0] = z[1][0] = -INFINITY; sv0 = 0.f; }
+    if (16 + n >= rem) { z[0][1] = z[1][1] = -INFINITY; sv1 = 0.f; }
+  }
+  const float vmax = row_max(fmaxf(sv0, sv1));                // same in every row: wave-uniform
+  float m_new[2];
+  bool grow = false;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    m_new[j] = fmaxf(st.m_run[j], row_max(fmaxf(z[j][0], z[j][1])));
+    grow |= m_new[j] > st.m_run[j];
+  }
+  const bool vgrow = vmax >= ldexpf(1.f, st.vexp);
+  if (__any(grow) || vgrow) {
+    float ratio = 1.f;
+    if (vgrow) {
+      int ex;
+      frexpf(vmax, &ex);                                       // vmax < 2^ex
+      ex = ex < -60 ? -60 : ex;
+      ratio = st.vexp == -200 ? 0.f : ldexpf(1.f, st.vexp - ex);
+      st.vexp = ex;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[j] - m_new[j]);   // 0 when m_run = -inf
+      st.l_run[j] *= alpha;
+      st.ls_run[j] *= alpha * ratio;
+      st.m_run[j] = m_new[j];
+      const float f = alpha * ratio;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        st.O[nt][2 * j] *= f;
+        st.O[nt][2 * j + 1] *= f;
+      }
+    }
+  }
+  // ---- probabilities; P'' = p s_V 4096 / vlim split hi/lo into the P staging rows ----
+  const float pmul = ldexpf(kPScale, -st.vexp);
+  const float svm[2] = {sv0 * pmul, sv1 * pmul};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    _Float16 h4[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float p = __builtin_amdgcn_exp2f(z[j][tt] - st.m_run[j]);
+      st.l_run[j] += p;
+      const float pp = p * svm[tt];
+      st.ls_run[j] += pp;
+      const _Float16 hi = (_Float16)pp;
+      h4[2 * j] = hi;
+      h4[2 * j + 1] = (_Float16)(pp - (float)hi);
+    }
+    *reinterpret_cast<short4v*>(ws.p + (16 * tt + n) * 32 + 8 * g4) = __builtin_bit_cast(short4v, h4);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // ---- PV: A = P'' (rows (head, part)), B = V; K slot e of row group g4 is token 4*g4 + e
+  //      (e < 4) or 16 + 4*g4 + e - 4 (e >= 4), the same order for both operands ----
+  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd));
+  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd + 16 * 32));
+  const half8 pop = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + vrd + 32 * nt));
+    const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + vrd + 16 * kVRow + 32 * nt));
+    const short8v both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    st.O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(half8, both), st.O[nt], 0, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
   const int chunk_id = blockIdx.x;
   const int g = blockIdx.y / a.head_groups;
@@ -157,275 +358,190 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeKArgs a) {
   const int64_t kv = (int64_t)b * a.Hkv + g;
   const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
 
-  // ---------------- set-up: rotate queries, build operands ----------------
-  if (tid < 32) build_block(rot + tid * 8, sm.setup.mats[tid]);
-  {
-    const int i = tid >> 5;              // query row 0..7
-    const int d4 = (tid & 31) * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (i < nh) {
-      const int64_t off = ((int64_t)b * a.Hq + h0 + i) * 128 + d4;
-      if (a.q_bf16) {
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + off;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = __uint_as_float((unsigned)qp[u] << 16);
-      } else {
-        const float* qp = static_cast<const float*>(a.q) + off;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = qp[u];
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sm.setup.qr[i][d4 + u] = v[u];
-  }
-  __syncthreads();
-  // Unnormalised Sylvester WHT of each row: 7 butterfly stages, 512 pairs per stage.
-  for (int m = 1; m < 128; m <<= 1) {
-#pragma unroll
-    for (int rep = 0; rep < 2; ++rep) {
-      const int pidx = tid + rep * kThreads;    // pair index 0..511
-      const int row = pidx >> 6;
-      const int p = pidx & 63;
-      const int lo = ((p / m) * 2 * m) + (p % m);
-      const float u = sm.setup.qr[row][lo], w = sm.setup.qr[row][lo + m];
-      sm.setup.qr[row][lo] = u + w;
-      sm.setup.qr[row][lo + m] = u - w;
-    }
-    __syncthreads();
-  }
-  // SO(4) blocks and 1/sqrt(128): thread (row i, block bb).
-  float amax_local;
-  {
-    const int i = tid >> 5, bb = tid & 31;
-    const float* M = sm.setup.mats[bb];
-    const float y0 = sm.setup.qr[i][4 * bb], y1 = sm.setup.qr[i][4 * bb + 1];
-    const float y2 = sm.setup.qr[i][4 * bb + 2], y3 = sm.setup.qr[i][4 * bb + 3];
-    float r[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr)
-      r[rr] = (M[4 * rr] * y0 + M[4 * rr + 1] * y1 + M[4 * rr + 2] * y2 + M[4 * rr + 3] * y3) *
-              0.08838834764831845f;
-    __syncthreads();
-    amax_local = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      sm.setup.qr[i][4 * bb + rr] = r[rr];
-      amax_local = fmaxf(amax_local, fabsf(r[rr]));
-    }
-  }
-  // sigma = max V scale over the chunk (keeps P'' <= 4096 in fp16).
-  float vmax_local = 0.f;
-  for (int64_t t = tok0 + tid; t < tok_end; t += kThreads) vmax_local = fmaxf(vmax_local, a.vs[kv * a.cap + t]);
-  sm.setup.red[tid] = fmaxf(amax_local, 0.f);
-  __syncthreads();
-  for (int st = kThreads / 2; st > 0; st >>= 1) {
-    if (tid < st) sm.setup.red[tid] = fmaxf(sm.setup.red[tid], sm.setup.red[tid + st]);
-    __syncthreads();
-  }
-  const float qamax = sm.setup.red[0];
-  __syncthreads();
-  sm.setup.red[tid] = vmax_local;
-  __syncthreads();
-  for (int st = kThreads / 2; st > 0; st >>= 1) {
-    if (tid < st) sm.setup.red[tid] = fmaxf(sm.setup.red[tid], sm.setup.red[tid + st]);
-    __syncthreads();
-  }
-  const float sigma = sm.setup.red[0] > 0.f ? sm.setup.red[0] : 1.f;
-  // Query operand scaling 2^E keeps the largest |q'| * 2^E near 2^14 in fp16.
-  int E = 0;
-  if (qamax > 0.f) {
-    int ex;
-    frexpf(qamax, &ex);                // qamax in [2^(ex-1), 2^ex)
-    E = 14 - ex;
-  }
-  // B operand of the QK product: lane = (column n = head + 8*part, quarter g4).
-  const int n = lane & 15;
-  const int g4 = lane >> 4;
-  const int head = n & 7;
-  const int part = n >> 3;
-  half8 qop[4];
-  float qsum = 0.f;                    // sum over coordinates of q' for this lane's head
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    _Float16 hv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int s = 8 * kb + e;
-      const float qv = sm.setup.qr[head][32 * g4 + slot_coord(s)];
-      const float v = ldexpf(qv, E - slot_pow(s));
-      const _Float16 hi = (_Float16)v;
-      hv[e] = part ? (_Float16)(v - (float)hi) : hi;
-      qsum += qv;
-    }
-    qop[kb] = half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
-  }
-  // qsum so far covers this lane's quarter; add the other three quarters.
-  qsum += wave_xor(qsum, 16);
-  qsum += wave_xor(qsum, 32);
-  __syncthreads();                     // set-up smem is reused by the loop below
-
-  // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
-  const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
-  const float c2 = a.sm_log2 * 3.5f * qsum;
-  const float pmul = kPScale / sigma;
-
-  floatx4 O[8];
-#pragma unroll
-  for (int nt = 0; nt < 8; ++nt) O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;             // running max (log2 units) of this lane's head
-  float l_run = 0.f;                   // sum of p
-  float ls_run = 0.f;                  // sum of the P'' values fed to the PV product (own part)
-
   const uint8_t* kbase = a.kc + kv * a.cap * 48;
   const uint8_t* vbase = a.vc + kv * a.cap * 48;
   const float* ksb = a.ks + kv * a.cap;
   const float* vsb = a.vs + kv * a.cap;
-  _Float16(*vrow)[kRowHalves] = sm.loop.v[wave];
-  float* sc = sm.loop.sc[wave];
+  const int n = lane & 15;          // MFMA column: token within a 16-token tile / V slot
+  const int g4 = lane >> 4;         // row group: quarter of the record; heads 2*g4, 2*g4+1
+  LaneOffsets lo;
+  lo.code[0] = (unsigned)(n * 48 + 12 * g4);
+  lo.code[1] = (unsigned)((16 + n) * 48 + 12 * g4);
+  lo.scale = (unsigned)(n + 16 * (g4 & 1));
+  const bool vscale = g4 >= 2;
 
-  for (int64_t t0 = tok0 + (int64_t)wave * kBlock; t0 < tok_end; t0 += (int64_t)kWaves * kBlock) {
-    // ---- loads ----
-    unsigned kw[2][3], vw[2][3];
+  // Issue the first block's loads before the set-up so their latency overlaps it.
+  const int64_t step = (int64_t)kWaves * kBlock;
+  int64_t t0 = tok0 + (int64_t)wave * kBlock;
+  BlockData bufA, bufB;
+  if (t0 < tok_end) load_block(bufA, kbase, vbase, ksb, vsb, t0, a.cap, lo, vscale);
+
+  // ---------------- set-up (per wave): rotate the queries ----------------
+  WaveLoopSmem& ws = sm.loop[wave];
+  float* scratch = reinterpret_cast<float*>(ws.v);           // 9 KB per wave
+  float* qrot = scratch;                                     // [8][128]
+  float* blk = scratch + 1024;                               // [32][16] (overlaps ws.p, ws.sc: unused yet)
+  if (lane < 32) build_block(rot + lane * 8, blk + lane * 16);
+  const int qi = lane >> 3, qe = lane & 7;                   // head row, 16-coordinate slice
+  float x[16];
+  {
+    const bool have = qi < nh;
+    const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * qe;
+    if (a.q_bf16) {
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+      const uint4 u0 = qp[0], u1 = qp[1];
+      const unsigned w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      int64_t t = t0 + 16 * tt + n;
-      if (t >= a.cap) t = a.cap - 1;
-      const unsigned* kp = reinterpret_cast<const unsigned*>(kbase + t * 48 + 12 * g4);
-      const unsigned* vp = reinterpret_cast<const unsigned*>(vbase + t * 48 + 12 * g4);
-      kw[tt][0] = kp[0]; kw[tt][1] = kp[1]; kw[tt][2] = kp[2];
-      vw[tt][0] = vp[0]; vw[tt][1] = vp[1]; vw[tt][2] = vp[2];
-    }
-    {
-      int64_t t = t0 + (lane & 31);
-      if (t >= a.cap) t = a.cap - 1;
-      sc[lane] = (lane < 32) ? ksb[t] : vsb[t];
-    }
-    // ---- QK: S^T[token][head,part] ----
-    floatx4 S[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      unsigned u[16];
-      unpack_quarter(kw[tt][0], kw[tt][1], kw[tt][2], u);
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
-                                                    qop[kb], acc, 0, 0, 0);
-      S[tt] = acc;
-    }
-    // ---- scores (this lane: head, tokens 4*g4 + r of each 16-token tile) ----
-    float z[8], sv[8];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float raw = S[tt][r] + __shfl_xor(S[tt][r], 8, 64);   // hi + lo columns
-        const int tl = 16 * tt + 4 * g4 + r;                          // token within block
-        const float sk = sc[tl];
-        sv[4 * tt + r] = sc[32 + tl];
-        float zz = sk * fmaf(raw, c1, -c2);
-        if (t0 + tl >= tok_end) zz = -INFINITY;
-        z[4 * tt + r] = zz;
-        bmax = fmaxf(bmax, zz);
+      for (int i = 0; i < 8; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
       }
-    bmax = fmaxf(bmax, wave_xor(bmax, 16));
-    bmax = fmaxf(bmax, wave_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
-    if (__any(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 when m_run = -inf
-      l_run *= alpha;
-      ls_run *= alpha;
-      // O rows are (head, part) = 4*g4 + r; fetch alpha of head (4*g4 + r) & 7.
+    } else {
+      const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, ((4 * g4 + r) & 7), 64);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) O[nt][r] *= ar;
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = qp[i];
+        x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
       }
-      m_run = m_new;
     }
-    // ---- probabilities and the A operand of PV ----
-    _Float16 ph[8];
+    if (!have) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = __builtin_amdgcn_exp2f(z[j] - m_run);
-      l_run += p;
-      const float pp = p * sv[j] * pmul;
-      const _Float16 hi = (_Float16)pp;
-      const _Float16 val = part ? (_Float16)(pp - (float)hi) : hi;
-      ph[j] = val;
-      ls_run += (float)val;
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
     }
-    const half8 pop = half8{ph[0], ph[1], ph[2], ph[3], ph[4], ph[5], ph[6], ph[7]};
-    // ---- V: unpack to LDS rows [token][slot], read back transposed ----
+  }
+  {
+    // Sylvester Hadamard (unnormalised): strides 16, 32, 64 across lanes qe^1, ^2, ^4,
+    // strides 8, 4, 2, 1 inside the lane.  new = partner + sg * mine.
+    const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      unsigned u[16];
-      unpack_quarter(vw[tt][0], vw[tt][1], vw[tt][2], u);
-      uint4* dst = reinterpret_cast<uint4*>(&vrow[16 * tt + n][32 * g4]);
-      dst[0] = make_uint4(u[0], u[1], u[2], u[3]);
-      dst[1] = make_uint4(u[4], u[5], u[6], u[7]);
-      dst[2] = make_uint4(u[8], u[9], u[10], u[11]);
-      dst[3] = make_uint4(u[12], u[13], u[14], u[15]);
-    }
-    __builtin_amdgcn_wave_barrier();
-    // Transposed read: lane (g4, i) points at row 4*g4 + i/4 (+16), column 4*(i%4).
-    const int trow = 4 * g4 + (n >> 2);
-    const int tcol = 4 * (n & 3);
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      typedef __attribute__((address_space(3))) short4v* lds_s4;
-      const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&vrow[trow][16 * nt + tcol]));
-      const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(&vrow[16 + trow][16 * nt + tcol]));
-      typedef short short8v __attribute__((ext_vector_type(8)));
-      const short8v both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-      O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(half8, both), O[nt], 0, 0, 0);
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i & m) == 0) {
+          const float u = x[i], v = x[i + m];
+          x[i] = u + v;
+          x[i + m] = u - v;
+        }
+  }
+  __builtin_amdgcn_wave_barrier();
+  float qamax = 0.f, qs = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float* M = blk + (4 * qe + j) * 16;
+    float y[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      y[r] = (M[4 * r] * x[4 * j] + M[4 * r + 1] * x[4 * j + 1] + M[4 * r + 2] * x[4 * j + 2] +
+              M[4 * r + 3] * x[4 * j + 3]) * kInvSqrtD;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      qrot[qi * 128 + 16 * qe + 4 * j + r] = y[r];
+      qamax = fmaxf(qamax, fabsf(y[r]));
+      qs += y[r];
     }
-    __builtin_amdgcn_wave_barrier();
+  }
+  // Operand scaling 2^E keeps the largest |q'| * 2^E in [2^13, 2^14).
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) qamax = fmaxf(qamax, wave_xor(qamax, m));
+  qs += dpp_xor1(qs);
+  qs += dpp_xor2(qs);
+  qs += swz_xor4(qs);                 // sum of q' over head qi (all 8 lanes of the head)
+  int E = 0;
+  if (qamax > 0.f) {
+    int ex;
+    frexpf(qamax, &ex);
+    E = 14 - ex;
+  }
+  const float qsum0 = __shfl(qs, (2 * g4) * 8, 64);
+  const float qsum1 = __shfl(qs, (2 * g4 + 1) * 8, 64);
+  __builtin_amdgcn_wave_barrier();
+  // A operand of the QK product: lane row n = (head n/2, part n%2), K slots of quarter g4.
+  half8 qop[4];
+  {
+    const int head = n >> 1, part = n & 1;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      _Float16 hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int s = 8 * kb + e;
+        const float v = ldexpf(qrot[head * 128 + 32 * g4 + slot_coord(s)], E - slot_pow(s));
+        const _Float16 hi = (_Float16)v;
+        hv[e] = part ? (_Float16)(v - (float)hi) : hi;
+      }
+      qop[kb] = half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+    }
+  }
+  __builtin_amdgcn_wave_barrier();   // set-up scratch is the V staging area below
+
+  // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
+  const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
+  const float c2[2] = {a.sm_log2 * 3.5f * qsum0, a.sm_log2 * 3.5f * qsum1};
+  // LDS addresses: this lane's V staging writes (row n of each tile, sectors 2*g4 and 2*g4+1, the
+  // halves swapped in flipped rows), its transposed V reads (row 4*g4 + n/4, piece n%4) and its
+  // transposed P'' reads.  Tile 1 rows and the second read (+16 rows) keep the same flip.
+  const unsigned vw0 = (unsigned)(n * kVRow + 64 * g4 + 16 * vhalf_flip(n));
+  const unsigned vw1 = (unsigned)(n * kVRow + 64 * g4 + 16 * (1 - vhalf_flip(n)));
+  const int rrow = 4 * g4 + (n >> 2);
+  const unsigned vrd = (unsigned)(rrow * kVRow + 8 * ((n & 3) ^ (2 * vhalf_flip(rrow))));
+  const unsigned prd = (unsigned)(rrow * 32 + 8 * (n & 3));
+
+  WaveState st;
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) st.O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  st.m_run[0] = st.m_run[1] = -INFINITY;
+  st.l_run[0] = st.l_run[1] = 0.f;
+  st.ls_run[0] = st.ls_run[1] = 0.f;
+  st.vexp = -200;
+
+  // Two buffers in turn: the loads of the next block are in flight while a block is processed.
+  while (t0 < tok_end) {
+    int64_t tn = t0 + step;
+    if (tn < tok_end) load_block(bufB, kbase, vbase, ksb, vsb, tn, a.cap, lo, vscale);
+    process_block(bufA, (int)((tok_end - t0) < kBlock ? (tok_end - t0) : kBlock), st, qop, c1, c2, ws, lane, n, g4,
+                  vw0, vw1, vrd, prd);
+    t0 = tn;
+    if (t0 >= tok_end) break;
+    tn = t0 + step;
+    if (tn < tok_end) load_block(bufA, kbase, vbase, ksb, vsb, tn, a.cap, lo, vscale);
+    process_block(bufB, (int)((tok_end - t0) < kBlock ? (tok_end - t0) : kBlock), st, qop, c1, c2, ws, lane, n, g4,
+                  vw0, vw1, vrd, prd);
+    t0 = tn;
   }
 
   // ---------------- per-wave results ----------------
-  // l: the two part lanes hold identical p; count part 0 only, then sum quarters.
-  float l_tot = part ? 0.f : l_run;
-  l_tot += wave_xor(l_tot, 8);
-  l_tot += wave_xor(l_tot, 16);
-  l_tot += wave_xor(l_tot, 32);
-  float ls_tot = ls_run;               // hi (part 0) + lo (part 1) over all quarters
-  ls_tot += wave_xor(ls_tot, 8);
-  ls_tot += wave_xor(ls_tot, 16);
-  ls_tot += wave_xor(ls_tot, 32);
-  // O: rows 4*g4 + r, g4 < 2 hold the hi part, g4 >= 2 the lo part of head 4*(g4&1) + r.
-  floatx4 Of[8];
+  float l_tot[2], ls_tot[2];
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) Of[nt][r] = O[nt][r] + __shfl_xor(O[nt][r], 32, 64);
-  __syncthreads();                     // loop smem -> merge smem
-  if (lane < 8) {
-    sm.merge.m[wave][lane] = m_run;    // lane h holds head h (column n = h)
-    sm.merge.l[wave][lane] = l_tot;
+  for (int j = 0; j < 2; ++j) {
+    l_tot[j] = row_sum(st.l_run[j]);
+    ls_tot[j] = row_sum(st.ls_run[j]);
   }
-  // Each lane of g4 < 2 writes o' for heads 4*g4 + r and slot 16*nt + n.
-  // o'[coord] = sigma/4096 * (O * 2^(24 - p) - 3.5 * ls), ls taken from lane (head).
+  __syncthreads();                     // every wave is done with the loop smem
+  if (n == 0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      sm.merge.m[wave][2 * g4 + j] = st.m_run[j];
+      sm.merge.l[wave][2 * g4 + j] = l_tot[j];
+    }
+  }
+  // o'[coord] = vlim/4096 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row
   {
-    float lsr[4];
+    const float back = ldexpf(1.f / kPScale, st.vexp);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lsr[r] = __shfl(ls_tot, (4 * (g4 & 1) + r), 64);
-    if (g4 < 2) {
-      const float back = sigma / kPScale;
+    for (int nt = 0; nt < 8; ++nt) {
+      const int slot = 16 * nt + n;          // quarter slot/32, extraction slot slot%32
+      const int qd = slot >> 5, s = slot & 31;
+      const int coord = 32 * qd + slot_coord(s);
+      const float up = ldexpf(1.f, 24 - slot_pow(s));
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int slot = 16 * nt + n;          // dim-slot: quarter slot/32, extraction slot slot%32
-        const int qd = slot >> 5, s = slot & 31;
-        const int coord = 32 * qd + slot_coord(s);
-        const float up = ldexpf(1.f, 24 - slot_pow(s));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int hrow = 4 * g4 + r;
-          sm.merge.o[wave][hrow][coord] = back * fmaf(Of[nt][r], up, -3.5f * lsr[r]);
-        }
-      }
+      for (int j = 0; j < 2; ++j)
+        sm.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[nt][2 * j] + st.O[nt][2 * j + 1], up, -3.5f * ls_tot[j]);
     }
   }
   __syncthreads();
@@ -464,9 +580,13 @@ struct CombineArgs {
   float* out;
 };
 
+constexpr int kMaxChunks = 1024;
+
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   __shared__ float y[128];
   __shared__ float mats[32][16];
+  __shared__ float wgt[kMaxChunks];
+  __shared__ float red[128];
   const int bh = blockIdx.x;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int g = h / a.G;
@@ -484,17 +604,41 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   const int nvalid = (int)((len + a.chunk - 1) / a.chunk);
   const float* ml = a.part_ml + (int64_t)bh * a.n_chunks * 2;
   const float* po = a.part_o + (int64_t)bh * a.n_chunks * 128;
-  float M = -INFINITY;
-  for (int c = 0; c < nvalid; ++c) M = fmaxf(M, ml[2 * c]);
-  float L = 0.f, acc = 0.f;
-  for (int c = 0; c < nvalid; ++c) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-    L += f * ml[2 * c + 1];
-    acc += f * po[(int64_t)c * 128 + d];
-  }
   const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
   if (d < 32) build_block(rot + d * 8, mats[d]);
-  y[d] = acc / L;
+  float M = -INFINITY;
+  for (int c = d; c < nvalid; c += 128) M = fmaxf(M, ml[2 * c]);
+  red[d] = M;
+  __syncthreads();
+  for (int st = 64; st > 0; st >>= 1) {
+    if (d < st) red[d] = fmaxf(red[d], red[d + st]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  float Lp = 0.f;
+  for (int c = d; c < nvalid; c += 128) {
+    const float f = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+    wgt[c] = f;
+    Lp += f * ml[2 * c + 1];
+  }
+  red[d] = Lp;
+  __syncthreads();
+  for (int st = 64; st > 0; st >>= 1) {
+    if (d < st) red[d] += red[d + st];
+    __syncthreads();
+  }
+  const float L = red[0];
+  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+  int c = 0;
+  for (; c + 4 <= nvalid; c += 4) {
+    acc0 += wgt[c] * po[(int64_t)c * 128 + d];
+    acc1 += wgt[c + 1] * po[(int64_t)(c + 1) * 128 + d];
+    acc2 += wgt[c + 2] * po[(int64_t)(c + 2) * 128 + d];
+    acc3 += wgt[c + 3] * po[(int64_t)(c + 3) * 128 + d];
+  }
+  for (; c < nvalid; ++c) acc0 += wgt[c] * po[(int64_t)c * 128 + d];
+  y[d] = ((acc0 + acc1) + (acc2 + acc3)) / L;
   __syncthreads();
   // Transposed blocks: z[4bb + i] = sum_k M_bb[k][i] o'[4bb + k].
   const int bb = d >> 2, i = d & 3;
@@ -510,7 +654,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     y[d] = (d & m) ? (other - self) : (self + other);
     __syncthreads();
   }
-  outp[d] = y[d] * 0.08838834764831845f;
+  outp[d] = y[d] * kInvSqrtD;
 }
 
 }  // namespace
@@ -519,12 +663,14 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   DecodeGeometry geo{};
   const int G = n_q_heads / n_kv_heads;
   geo.head_groups = (G + 7) / 8;
-  // Aim for ~2048 work-groups; chunks are a power-of-two multiple of 128 tokens in [128, 2048].
+  // About 1024 work-groups; chunks are a power-of-two multiple of 128 tokens, at least 256,
+  // and large enough that no row has more than kMaxChunks partials.
   const int64_t units = (int64_t)batch * n_kv_heads * geo.head_groups;
-  const int64_t want = (units * cache_cap + 2047) / 2048;
-  int chunk = 128;
-  while (chunk < 2048 && chunk < want) chunk <<= 1;
-  geo.chunk = chunk;
+  const int64_t want = (units * cache_cap + 1023) / 1024;
+  int64_t chunk = 256;
+  while (chunk < 4096 && chunk < want) chunk <<= 1;
+  while ((cache_cap + chunk - 1) / chunk > kMaxChunks) chunk <<= 1;
+  geo.chunk = (int)chunk;
   geo.n_chunks = (int)((cache_cap + chunk - 1) / chunk);
   const int64_t parts = (int64_t)batch * n_q_heads * geo.n_chunks;
   geo.workspace_bytes = parts * 128 * 4 + parts * 2 * 4 + 256;
@@ -536,7 +682,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   const int64_t parts = (int64_t)a.batch * a.n_q_heads * geo.n_chunks;
   float* part_o = static_cast<float*>(a.workspace);
   float* part_ml = part_o + parts * 128;
-  const float sm = a.sm_scale > 0.f ? a.sm_scale : 0.08838834764831845f;
+  const float sm = a.sm_scale > 0.f ? a.sm_scale : kInvSqrtD;
 
   DecodeKArgs k{};
   k.q = a.q;

@@ -134,7 +134,8 @@ int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * numbers only in registers, softmax is online and split over the
  * sequence, V is accumulated in rotated space and rotated back once per
  * output row.
- *   q            [batch][n_q_heads][128], q_dtype IQ_F32 or IQ_BF16.
+ *   q            [batch][n_q_heads][128], q_dtype IQ_F32 or IQ_BF16,
+ *                16-byte aligned.
  *   k_*, v_*     the cache written by iq_quantize_kv, [batch][n_kv_heads]
  *                [cache_cap][48] codes and [batch][n_kv_heads][cache_cap]
  *                scales.
@@ -151,7 +152,8 @@ int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  *   workspace    device buffer of at least iq_decode_workspace_bytes(...)
  *                bytes, 256-byte aligned, used only during the call.
  * Errors: IQ_EINVAL (NULL pointers, sizes < 1, n_q_heads % n_kv_heads != 0,
- * negative stride), IQ_EWORKSPACE, IQ_EUNSUPPORTED, IQ_EHIP.
+ * negative stride, misaligned pointers: q 16 bytes, the rest 4), IQ_EWORKSPACE,
+ * IQ_EUNSUPPORTED, IQ_EHIP.
  */
 int iq_decode_attention(const void* q, int32_t q_dtype,
                         const uint8_t* k_codes, const float* k_scales,
