@@ -29,6 +29,8 @@ def flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
             # packed fp32 VALU ops are kept out of the generated code on purpose
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # no NaN semantics needed (infinities still are): lets min/max skip canonicalisation
+            "-fno-honor-nans",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

@@ -22,8 +22,10 @@
 //     folded into the query operand;
 //   * S^T[token][head,part] = codes x q' on v_mfma_f32_16x16x32_f16; the hi and
 //     lo columns are summed with one DPP add; online softmax in base 2;
-//   * P'' = p * s_V * 4096 / vlim (vlim a running power of two above every V
-//     scale seen), split hi/lo in fp16, is the A operand of the PV product;
+//   * lazy online softmax: the running max moves only when a score passes it
+//     by more than 8 (log2 units), so p <= 256; P'' = p * s_V * 16 / vlim
+//     (vlim a running power of two above every V scale seen) is split hi/lo
+//     in fp16 and staged through LDS as the A operand of the PV product;
 //   * V codes of the block are unpacked the same way into LDS ([token][slot]
 //     rows) and read back transposed with ds_read_b64_tr_b16 as the B operand
 //     of O[head,part][slot] += P'' x V;
@@ -46,7 +48,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 32;          // tokens per wave step
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kPScale = 4096.f;   // P'' <= 4096: the fp16 lo part stays in the normal range
+constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running max before a rescale
+constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 
 // Coordinate (within a quarter) held by extraction slot s: the 16 words that
@@ -126,6 +129,13 @@ struct WaveLoopSmem {
 union DecodeSmem {
   MergeSmem merge;
   WaveLoopSmem loop[kWaves];
+};
+// Computed once per work-group by wave 0: the QK A operand in lane order, sum of q' per head,
+// and the operand exponent E.
+struct SetupShared {
+  uint4v qop[64][4];
+  float qsum[8];
+  int E;
 };
 
 __device__ void build_block(const float* p, float* out16) {
@@ -268,18 +278,16 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
     if (n >= rem) { z[0][0] = z[1][0] = -INFINITY; sv0 = 0.f; }
     if (16 + n >= rem) { z[0][1] = z[1][1] = -INFINITY; sv1 = 0.f; }
   }
-  const float vmax = row_max(fmaxf(sv0, sv1));                // same in every row: wave-uniform
-  float m_new[2];
-  bool grow = false;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    m_new[j] = fmaxf(st.m_run[j], row_max(fmaxf(z[j][0], z[j][1])));
-    grow |= m_new[j] > st.m_run[j];
-  }
-  const bool vgrow = vmax >= ldexpf(1.f, st.vexp);
-  if (__any(grow) || vgrow) {
+  // Lazy rescaling: the running max only moves when a score exceeds it by more than kHeadroom
+  // (so p <= 2^kHeadroom), or when a V scale reaches the running power-of-two bound.
+  const float vlim = ldexpf(1.f, st.vexp);
+  const bool vgrow_l = (sv0 >= vlim) || (sv1 >= vlim);
+  const bool grow_l = (z[0][0] > st.m_run[0] + kHeadroom) || (z[0][1] > st.m_run[0] + kHeadroom) ||
+                      (z[1][0] > st.m_run[1] + kHeadroom) || (z[1][1] > st.m_run[1] + kHeadroom);
+  if (__any(grow_l || vgrow_l)) {
+    const float vmax = row_max(fmaxf(sv0, sv1));              // same in every row: wave-uniform
     float ratio = 1.f;
-    if (vgrow) {
+    if (vmax >= vlim) {
       int ex;
       frexpf(vmax, &ex);                                       // vmax < 2^ex
       ex = ex < -60 ? -60 : ex;
@@ -288,10 +296,11 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const float alpha = __builtin_amdgcn_exp2f(st.m_run[j] - m_new[j]);   // 0 when m_run = -inf
+      const float m_new = fmaxf(st.m_run[j], row_max(fmaxf(z[j][0], z[j][1])));
+      const float alpha = __builtin_amdgcn_exp2f(st.m_run[j] - m_new);   // 0 when m_run = -inf
       st.l_run[j] *= alpha;
       st.ls_run[j] *= alpha * ratio;
-      st.m_run[j] = m_new[j];
+      st.m_run[j] = m_new;
       const float f = alpha * ratio;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -300,7 +309,7 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
       }
     }
   }
-  // ---- probabilities; P'' = p s_V 4096 / vlim split hi/lo into the P staging rows ----
+  // ---- probabilities; P'' = p s_V 16 / vlim split hi/lo into the P staging rows ----
   const float pmul = ldexpf(kPScale, -st.vexp);
   const float svm[2] = {sv0 * pmul, sv1 * pmul};
 #pragma unroll
@@ -337,13 +346,14 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
+  __shared__ SetupShared ss;
   const int chunk_id = blockIdx.x;
   const int g = blockIdx.y / a.head_groups;
   const int hg = blockIdx.y % a.head_groups;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
 
   int64_t len = a.cap;
   if (a.seq_lens) {
@@ -376,94 +386,93 @@ void decode_split_kernel(DecodeKArgs a) {
   BlockData bufA, bufB;
   if (t0 < tok_end) load_block(bufA, kbase, vbase, ksb, vsb, t0, a.cap, lo, vscale);
 
-  // ---------------- set-up (per wave): rotate the queries ----------------
+  // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   WaveLoopSmem& ws = sm.loop[wave];
-  float* scratch = reinterpret_cast<float*>(ws.v);           // 9 KB per wave
-  float* qrot = scratch;                                     // [8][128]
-  float* blk = scratch + 1024;                               // [32][16] (overlaps ws.p, ws.sc: unused yet)
-  if (lane < 32) build_block(rot + lane * 8, blk + lane * 16);
-  const int qi = lane >> 3, qe = lane & 7;                   // head row, 16-coordinate slice
-  float x[16];
-  {
-    const bool have = qi < nh;
-    const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * qe;
-    if (a.q_bf16) {
-      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-      const uint4 u0 = qp[0], u1 = qp[1];
-      const unsigned w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+  if (wave == 0) {
+    float* scratch = reinterpret_cast<float*>(ws.v);         // 9 KB: wave 0's staging area, unused yet
+    float* qrot = scratch;                                   // [8][128]
+    float* blk = scratch + 1024;                             // [32][16]
+    if (lane < 32) build_block(rot + lane * 8, blk + lane * 16);
+    const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
+    float x[16];
+    {
+      const bool have = qi < nh;
+      const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * qe;
+      if (a.q_bf16) {
+        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+        const uint4 u0 = qp[0], u1 = qp[1];
+        const unsigned w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x[2 * i] = __uint_as_float(w[i] << 16);
-        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-      }
-    } else {
-      const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 v = qp[i];
-        x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-      }
-    }
-    if (!have) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.f;
-    }
-  }
-  {
-    // Sylvester Hadamard (unnormalised): strides 16, 32, 64 across lanes qe^1, ^2, ^4,
-    // strides 8, 4, 2, 1 inside the lane.  new = partner + sg * mine.
-    const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i & m) == 0) {
-          const float u = x[i], v = x[i + m];
-          x[i] = u + v;
-          x[i + m] = u - v;
+        for (int i = 0; i < 8; ++i) {
+          x[2 * i] = __uint_as_float(w[i] << 16);
+          x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
-  }
-  __builtin_amdgcn_wave_barrier();
-  float qamax = 0.f, qs = 0.f;
+      } else {
+        const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float* M = blk + (4 * qe + j) * 16;
-    float y[4];
+        for (int i = 0; i < 4; ++i) {
+          const float4 v = qp[i];
+          x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+        }
+      }
+      if (!have) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      y[r] = (M[4 * r] * x[4 * j] + M[4 * r + 1] * x[4 * j + 1] + M[4 * r + 2] * x[4 * j + 2] +
-              M[4 * r + 3] * x[4 * j + 3]) * kInvSqrtD;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      qrot[qi * 128 + 16 * qe + 4 * j + r] = y[r];
-      qamax = fmaxf(qamax, fabsf(y[r]));
-      qs += y[r];
+        for (int i = 0; i < 16; ++i) x[i] = 0.f;
+      }
     }
-  }
-  // Operand scaling 2^E keeps the largest |q'| * 2^E in [2^13, 2^14).
+    {
+      // Sylvester Hadamard (unnormalised): strides 16, 32, 64 across lanes qe^1, ^2, ^4,
+      // strides 8, 4, 2, 1 inside the lane.  new = partner + sg * mine.
+      const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) qamax = fmaxf(qamax, wave_xor(qamax, m));
-  qs += dpp_xor1(qs);
-  qs += dpp_xor2(qs);
-  qs += swz_xor4(qs);                 // sum of q' over head qi (all 8 lanes of the head)
-  int E = 0;
-  if (qamax > 0.f) {
-    int ex;
-    frexpf(qamax, &ex);
-    E = 14 - ex;
-  }
-  const float qsum0 = __shfl(qs, (2 * g4) * 8, 64);
-  const float qsum1 = __shfl(qs, (2 * g4 + 1) * 8, 64);
-  __builtin_amdgcn_wave_barrier();
-  // A operand of the QK product: lane row n = (head n/2, part n%2), K slots of quarter g4.
-  half8 qop[4];
-  {
+      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i & m) == 0) {
+            const float u = x[i], v = x[i + m];
+            x[i] = u + v;
+            x[i + m] = u - v;
+          }
+    }
+    __builtin_amdgcn_wave_barrier();
+    float qamax = 0.f, qs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* M = blk + (4 * qe + j) * 16;
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        y[r] = (M[4 * r] * x[4 * j] + M[4 * r + 1] * x[4 * j + 1] + M[4 * r + 2] * x[4 * j + 2] +
+                M[4 * r + 3] * x[4 * j + 3]) * kInvSqrtD;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        qrot[qi * 128 + 16 * qe + 4 * j + r] = y[r];
+        qamax = fmaxf(qamax, fabsf(y[r]));
+        qs += y[r];
+      }
+    }
+    // Operand scaling 2^E keeps the largest |q'| * 2^E in [2^13, 2^14).
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) qamax = fmaxf(qamax, wave_xor(qamax, m));
+    qs += dpp_xor1(qs);
+    qs += dpp_xor2(qs);
+    qs += swz_xor4(qs);               // sum of q' over head qi (all 8 lanes of the head)
+    int E = 0;
+    if (qamax > 0.f) {
+      int ex;
+      frexpf(qamax, &ex);
+      E = 14 - ex;
+    }
+    if (qe == 0) ss.qsum[qi] = qs;
+    if (lane == 0) ss.E = E;
+    __builtin_amdgcn_wave_barrier();
+    // A operand of the QK product: lane row n = (head n/2, part n%2), K slots of quarter g4.
     const int head = n >> 1, part = n & 1;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -475,10 +484,15 @@ void decode_split_kernel(DecodeKArgs a) {
         const _Float16 hi = (_Float16)v;
         hv[e] = part ? (_Float16)(v - (float)hi) : hi;
       }
-      qop[kb] = half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+      ss.qop[lane][kb] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
     }
   }
-  __builtin_amdgcn_wave_barrier();   // set-up scratch is the V staging area below
+  __syncthreads();
+  half8 qop[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) qop[kb] = __builtin_bit_cast(half8, ss.qop[lane][kb]);
+  const int E = ss.E;
+  const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
@@ -530,7 +544,7 @@ void decode_split_kernel(DecodeKArgs a) {
       sm.merge.l[wave][2 * g4 + j] = l_tot[j];
     }
   }
-  // o'[coord] = vlim/4096 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row
+  // o'[coord] = vlim/16 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row
   {
     const float back = ldexpf(1.f / kPScale, st.vexp);
 #pragma unroll
@@ -663,12 +677,13 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   DecodeGeometry geo{};
   const int G = n_q_heads / n_kv_heads;
   geo.head_groups = (G + 7) / 8;
-  // About 1024 work-groups; chunks are a power-of-two multiple of 128 tokens, at least 256,
-  // and large enough that no row has more than kMaxChunks partials.
+  // About 768 work-groups (3 resident per compute unit on 256 CUs: one round); chunks are a
+  // power-of-two multiple of 128 tokens in [256, 8192], and large enough that no row has more
+  // than kMaxChunks partials.
   const int64_t units = (int64_t)batch * n_kv_heads * geo.head_groups;
-  const int64_t want = (units * cache_cap + 1023) / 1024;
+  const int64_t want = (units * cache_cap + 767) / 768;
   int64_t chunk = 256;
-  while (chunk < 4096 && chunk < want) chunk <<= 1;
+  while (chunk < 8192 && chunk < want) chunk <<= 1;
   while ((cache_cap + chunk - 1) / chunk > kMaxChunks) chunk <<= 1;
   geo.chunk = (int)chunk;
   geo.n_chunks = (int)((cache_cap + chunk - 1) / chunk);
