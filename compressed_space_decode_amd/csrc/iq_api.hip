@@ -110,6 +110,10 @@ extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64
 
 namespace {
 
+// The decode kernels address one (sequence, KV head)'s codes through a buffer resource with a
+// 32-bit byte range, and token indices are 32-bit.
+constexpr int64_t kMaxCacheCap = 0xFFFFFFFFll / 48;
+
 int check_decode_sizes(const char* fn, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap) {
   if (batch < 1 || batch > 65535 || n_q_heads < 1 || n_kv_heads < 1 || cache_cap < 1) {
     iq::set_error("%s: need 1 <= batch <= 65535, n_q_heads >= 1, n_kv_heads >= 1, cache_cap >= 1", fn);
@@ -120,7 +124,7 @@ int check_decode_sizes(const char* fn, int32_t batch, int32_t n_q_heads, int32_t
     return IQ_EINVAL;
   }
   const int64_t gy = (int64_t)n_kv_heads * ((n_q_heads / n_kv_heads + 7) / 8);
-  if (gy > 65535 || (int64_t)batch * n_q_heads > 0x7FFFFFFF || cache_cap > ((int64_t)1 << 40)) {
+  if (gy > 65535 || (int64_t)batch * n_q_heads > 0x7FFFFFFF || cache_cap > kMaxCacheCap) {
     iq::set_error("%s: sizes exceed the launch limits", fn);
     return IQ_EINVAL;
   }

@@ -171,42 +171,36 @@ struct BlockData {
   float sc;               // row group 0/1: K scale of token n / 16+n; 2/3: V scale of token n / 16+n
 };
 
-// Per-lane constant offsets of a 32-token block; the block base is uniform.
+// Per-lane constant offsets of a 32-token block; the block base is a scalar buffer offset.
 struct LaneOffsets {
   unsigned code[2];       // byte offset of this lane's quarter in tile tt (token 16*tt + n)
-  unsigned scale;         // token of this lane's scale load
+  unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
 };
 
-__device__ __forceinline__ void load_block(BlockData& d, const uint8_t* kbase, const uint8_t* vbase,
-                                           const float* ksb, const float* vsb, int64_t t0, int64_t cap,
-                                           const LaneOffsets& lo, bool vscale) {
-  const float* sb = vscale ? vsb : ksb;
-  if (t0 + kBlock <= cap) {                                  // uniform: whole block inside the cache
-    const uint8_t* kb = kbase + t0 * 48;
-    const uint8_t* vb = vbase + t0 * 48;
+// Raw buffer resources over one (sequence, KV head)'s codes and scales.  Loads past the
+// end of a buffer return zeros, so a block that reaches past the cache needs no clamping
+// (those tokens are masked out of the softmax anyway).
+struct CacheBuffers {
+  __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
+};
+
+constexpr int kBufferConfig = 0x00020000;   // raw (untyped) buffer, 32-bit data format
+
+__device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb, int t0, const LaneOffsets& lo,
+                                           bool vscale) {
+  typedef unsigned u3v __attribute__((ext_vector_type(3)));
+  const int so = t0 * 48;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const uint3 kq = *reinterpret_cast<const uint3*>(kb + lo.code[tt]);
-      const uint3 vq = *reinterpret_cast<const uint3*>(vb + lo.code[tt]);
-      d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
-      d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
-    }
-    d.sc = sb[t0 + lo.scale];
-  } else {                                                   // block reaches past the cache end
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      int64_t t = t0 + lo.code[tt] / 48;
-      t = t < cap ? t : cap - 1;
-      const int64_t off = t * 48 + lo.code[tt] % 48;
-      const uint3 kq = *reinterpret_cast<const uint3*>(kbase + off);
-      const uint3 vq = *reinterpret_cast<const uint3*>(vbase + off);
-      d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
-      d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
-    }
-    int64_t t = t0 + lo.scale;
-    t = t < cap ? t : cap - 1;
-    d.sc = sb[t];
+  for (int tt = 0; tt < 2; ++tt) {
+    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, lo.code[tt], so, 0);
+    const u3v vq = __builtin_amdgcn_raw_buffer_load_b96(cb.vc, lo.code[tt], so, 0);
+    d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
+    d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
   }
+  // Both scale loads run in every lane (one 4-byte load each); a select keeps the resources uniform.
+  const unsigned kscale = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, lo.scale, t0 * 4, 0);
+  const unsigned vscale_v = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, lo.scale, t0 * 4, 0);
+  d.sc = __uint_as_float(vscale ? vscale_v : kscale);
 }
 
 // Running state of one wave's online softmax.  Lane (n, g4) owns heads 2*g4 and 2*g4+1.
@@ -355,36 +349,40 @@ void decode_split_kernel(DecodeKArgs a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
 
-  int64_t len = a.cap;
+  // Token indices are 32-bit and a sequence's codes fit one buffer resource (the capacity is
+  // validated: cap * 48 < 2^32): uniform token arithmetic stays on the scalar unit.
+  const int cap = (int)a.cap;
+  int len = cap;
   if (a.seq_lens) {
-    const int64_t l = a.seq_lens[b];
-    len = l < 0 ? 0 : (l > a.cap ? a.cap : l);
+    const int l = a.seq_lens[b];
+    len = l < 0 ? 0 : (l > cap ? cap : l);
   }
-  const int64_t tok0 = (int64_t)chunk_id * a.chunk;
+  const int tok0 = chunk_id * a.chunk;
   if (tok0 >= len) return;                                   // uniform
-  const int64_t tok_end = (tok0 + a.chunk < len) ? tok0 + a.chunk : len;
+  const int tok_end = (tok0 + a.chunk < len) ? tok0 + a.chunk : len;
   const int h0 = g * a.G + hg * 8;
   const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
   const int64_t kv = (int64_t)b * a.Hkv + g;
   const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
 
-  const uint8_t* kbase = a.kc + kv * a.cap * 48;
-  const uint8_t* vbase = a.vc + kv * a.cap * 48;
-  const float* ksb = a.ks + kv * a.cap;
-  const float* vsb = a.vs + kv * a.cap;
+  CacheBuffers cb;
+  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
+  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
+  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, cap * 4, kBufferConfig);
+  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, cap * 4, kBufferConfig);
   const int n = lane & 15;          // MFMA column: token within a 16-token tile / V slot
   const int g4 = lane >> 4;         // row group: quarter of the record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
   lo.code[0] = (unsigned)(n * 48 + 12 * g4);
   lo.code[1] = (unsigned)((16 + n) * 48 + 12 * g4);
-  lo.scale = (unsigned)(n + 16 * (g4 & 1));
+  lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
   const bool vscale = g4 >= 2;
 
   // Issue the first block's loads before the set-up so their latency overlaps it.
-  const int64_t step = (int64_t)kWaves * kBlock;
-  int64_t t0 = tok0 + (int64_t)wave * kBlock;
+  const int step = kWaves * kBlock;
+  int t0 = tok0 + wave * kBlock;
   BlockData bufA, bufB;
-  if (t0 < tok_end) load_block(bufA, kbase, vbase, ksb, vsb, t0, a.cap, lo, vscale);
+  if (t0 < tok_end) load_block(bufA, cb, t0, lo, vscale);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   WaveLoopSmem& ws = sm.loop[wave];
@@ -516,16 +514,14 @@ void decode_split_kernel(DecodeKArgs a) {
 
   // Two buffers in turn: the loads of the next block are in flight while a block is processed.
   while (t0 < tok_end) {
-    int64_t tn = t0 + step;
-    if (tn < tok_end) load_block(bufB, kbase, vbase, ksb, vsb, tn, a.cap, lo, vscale);
-    process_block(bufA, (int)((tok_end - t0) < kBlock ? (tok_end - t0) : kBlock), st, qop, c1, c2, ws, lane, n, g4,
-                  vw0, vw1, vrd, prd);
+    int tn = t0 + step;
+    if (tn < tok_end) load_block(bufB, cb, tn, lo, vscale);
+    process_block(bufA, min(tok_end - t0, kBlock), st, qop, c1, c2, ws, lane, n, g4, vw0, vw1, vrd, prd);
     t0 = tn;
     if (t0 >= tok_end) break;
     tn = t0 + step;
-    if (tn < tok_end) load_block(bufA, kbase, vbase, ksb, vsb, tn, a.cap, lo, vscale);
-    process_block(bufB, (int)((tok_end - t0) < kBlock ? (tok_end - t0) : kBlock), st, qop, c1, c2, ws, lane, n, g4,
-                  vw0, vw1, vrd, prd);
+    if (tn < tok_end) load_block(bufA, cb, tn, lo, vscale);
+    process_block(bufB, min(tok_end - t0, kBlock), st, qop, c1, c2, ws, lane, n, g4, vw0, vw1, vrd, prd);
     t0 = tn;
   }
 
