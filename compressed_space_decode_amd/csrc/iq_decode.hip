@@ -15,8 +15,8 @@
 //     swizzle, in-lane stages, then the 4x4 SO(4) blocks) and lays them out as
 //     the fp16 B operand of the QK product, hi and lo parts (q = hi + lo) in
 //     columns n and n+8 so the product carries ~22 bits;
-//   * loop over 32-token blocks, loads of block i+1 issued before block i is
-//     processed.  A lane loads 12 bytes (one quarter of a record) of one
+//   * loop over 32-token blocks; the loads of block i+1 are issued as soon as
+//     block i's codes are unpacked, and overlap the rest of block i.  A lane loads 12 bytes (one quarter of a record) of one
 //     token; one AND per pair of codes turns them into fp16 subnormals
 //     c * 2^(p-24) that the matrix cores multiply exactly, the 2^-p being
 //     folded into the query operand;
@@ -119,23 +119,28 @@ struct MergeSmem {
   float l[kWaves][8];
 };
 // Per-wave loop staging: unpacked V block [32 tokens][128 slots] fp16 in rows of 288 bytes,
-// P'' block [32 tokens][16 (head, part)] fp16, and the block's K/V scales.
+// the P'' block [32 tokens][16 (head, part)] fp16 in the last 32 bytes of the same rows, and
+// the block's K/V scales.
 constexpr int kVRow = 288;
+constexpr int kPOff = 256;          // P'' row t sits at byte t * kVRow + kPOff
 struct WaveLoopSmem {
   char v[kBlock * kVRow];
-  char p[kBlock * 32];
   float sc[64];
 };
-union DecodeSmem {
-  MergeSmem merge;
-  WaveLoopSmem loop[kWaves];
-};
 // Computed once per work-group by wave 0: the QK A operand in lane order, sum of q' per head,
-// and the operand exponent E.
+// and the operand exponent E.  Shares storage with the loop staging (a barrier separates them).
 struct SetupShared {
   uint4v qop[64][4];
   float qsum[8];
   int E;
+};
+union DecodeSmem {
+  MergeSmem merge;
+  WaveLoopSmem loop[kWaves];
+  struct {
+    WaveLoopSmem wave0;             // wave 0's set-up scratch lives in its staging rows
+    SetupShared shared;
+  } setup;
 };
 
 __device__ void build_block(const float* p, float* out16) {
@@ -229,9 +234,13 @@ __device__ __forceinline__ float row_sum(float x) {   // sum over the 16 lanes o
 
 typedef __attribute__((address_space(3))) short4v* lds_s4;
 
-__device__ __forceinline__ void process_block(const BlockData& cur, int rem, WaveState& st, const half8 (&qop)[4],
-                                              float c1, const float (&c2)[2], WaveLoopSmem& ws, int lane, int n,
-                                              int g4, unsigned vw0, unsigned vw1, unsigned vrd, unsigned prd) {
+// Processes the block in `cur` (tokens t0 ..), then refills `cur` with the block at t_next
+// (if any) as soon as the current codes are unpacked, so those loads overlap the rest.
+__device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_next, int tok_end,
+                                              const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
+                                              WaveState& st, const half8 (&qop)[4], float c1, const float (&c2)[2],
+                                              WaveLoopSmem& ws, int lane, int n, int g4, unsigned vw0,
+                                              unsigned vw1, unsigned vrd, unsigned prd) {
   ws.sc[lane] = cur.sc;
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
@@ -259,6 +268,8 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
     *reinterpret_cast<uint4*>(r0 + vw0 + 32) = make_uint4(u[8], u[9], u[10], u[11]);
     *reinterpret_cast<uint4*>(r0 + vw1 + 32) = make_uint4(u[12], u[13], u[14], u[15]);
   }
+  // ---- the codes are in registers / LDS now: refill the buffer with the next block ----
+  if (t_next < tok_end) load_block(cur, cb, t_next, lo, vscale);
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
   float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
@@ -319,13 +330,13 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
       h4[2 * j] = hi;
       h4[2 * j + 1] = (_Float16)(pp - (float)hi);
     }
-    *reinterpret_cast<short4v*>(ws.p + (16 * tt + n) * 32 + 8 * g4) = __builtin_bit_cast(short4v, h4);
+    *reinterpret_cast<short4v*>(vbytes + (16 * tt + n) * kVRow + kPOff + 8 * g4) = __builtin_bit_cast(short4v, h4);
   }
   __builtin_amdgcn_wave_barrier();
   // ---- PV: A = P'' (rows (head, part)), B = V; K slot e of row group g4 is token 4*g4 + e
   //      (e < 4) or 16 + 4*g4 + e - 4 (e >= 4), the same order for both operands ----
-  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd));
-  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd + 16 * 32));
+  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + prd));
+  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + prd + 16 * kVRow));
   const half8 pop = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
@@ -337,10 +348,9 @@ __device__ __forceinline__ void process_block(const BlockData& cur, int rem, Wav
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
-  __shared__ SetupShared ss;
   const int chunk_id = blockIdx.x;
   const int g = blockIdx.y / a.head_groups;
   const int hg = blockIdx.y % a.head_groups;
@@ -381,13 +391,13 @@ void decode_split_kernel(DecodeKArgs a) {
   // Issue the first block's loads before the set-up so their latency overlaps it.
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
-  BlockData bufA, bufB;
-  if (t0 < tok_end) load_block(bufA, cb, t0, lo, vscale);
+  BlockData buf;
+  if (t0 < tok_end) load_block(buf, cb, t0, lo, vscale);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
-  WaveLoopSmem& ws = sm.loop[wave];
+  SetupShared& ss = sm.setup.shared;
   if (wave == 0) {
-    float* scratch = reinterpret_cast<float*>(ws.v);         // 9 KB: wave 0's staging area, unused yet
+    float* scratch = reinterpret_cast<float*>(sm.setup.wave0.v);   // 9 KB of wave 0's staging rows
     float* qrot = scratch;                                   // [8][128]
     float* blk = scratch + 1024;                             // [32][16]
     if (lane < 32) build_block(rot + lane * 8, blk + lane * 16);
@@ -491,6 +501,8 @@ void decode_split_kernel(DecodeKArgs a) {
   for (int kb = 0; kb < 4; ++kb) qop[kb] = __builtin_bit_cast(half8, ss.qop[lane][kb]);
   const int E = ss.E;
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
+  __syncthreads();                   // the shared set-up area is staging space from here on
+  WaveLoopSmem& ws = sm.loop[wave];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
@@ -502,7 +514,7 @@ void decode_split_kernel(DecodeKArgs a) {
   const unsigned vw1 = (unsigned)(n * kVRow + 64 * g4 + 16 * (1 - vhalf_flip(n)));
   const int rrow = 4 * g4 + (n >> 2);
   const unsigned vrd = (unsigned)(rrow * kVRow + 8 * ((n & 3) ^ (2 * vhalf_flip(rrow))));
-  const unsigned prd = (unsigned)(rrow * 32 + 8 * (n & 3));
+  const unsigned prd = (unsigned)(rrow * kVRow + kPOff + 8 * (n & 3));
 
   WaveState st;
 #pragma unroll
@@ -514,14 +526,9 @@ void decode_split_kernel(DecodeKArgs a) {
 
   // Two buffers in turn: the loads of the next block are in flight while a block is processed.
   while (t0 < tok_end) {
-    int tn = t0 + step;
-    if (tn < tok_end) load_block(bufB, cb, tn, lo, vscale);
-    process_block(bufA, min(tok_end - t0, kBlock), st, qop, c1, c2, ws, lane, n, g4, vw0, vw1, vrd, prd);
-    t0 = tn;
-    if (t0 >= tok_end) break;
-    tn = t0 + step;
-    if (tn < tok_end) load_block(bufA, cb, tn, lo, vscale);
-    process_block(bufB, min(tok_end - t0, kBlock), st, qop, c1, c2, ws, lane, n, g4, vw0, vw1, vrd, prd);
+    const int tn = t0 + step;
+    process_block(buf, min(tok_end - t0, kBlock), tn, tok_end, cb, lo, vscale, st, qop, c1, c2, ws, lane, n, g4,
+                  vw0, vw1, vrd, prd);
     t0 = tn;
   }
 
@@ -669,18 +676,38 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 
 }  // namespace
 
+namespace {
+
+// Compute units of the current device (cached; 256, the MI355X count, if it cannot be queried).
+int device_cu_count() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      cached = cus;
+    else
+      cached = 256;
+  }
+  return cached;
+}
+
+}  // namespace
+
 DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t cache_cap) {
   DecodeGeometry geo{};
   const int G = n_q_heads / n_kv_heads;
   geo.head_groups = (G + 7) / 8;
-  // About 768 work-groups (3 resident per compute unit on 256 CUs: one round); chunks are a
-  // power-of-two multiple of 128 tokens in [256, 8192], and large enough that no row has more
-  // than kMaxChunks partials.
+  // One round of work-groups: 4 are resident per compute unit.  Each (sequence, KV head, head
+  // group) unit gets floor(slots / units) chunks (at least one); chunks are multiples of 128
+  // tokens (one step of the 4 waves), at least 256, and no row has more than kMaxChunks of them.
   const int64_t units = (int64_t)batch * n_kv_heads * geo.head_groups;
-  const int64_t want = (units * cache_cap + 767) / 768;
-  int64_t chunk = 256;
-  while (chunk < 8192 && chunk < want) chunk <<= 1;
-  while ((cache_cap + chunk - 1) / chunk > kMaxChunks) chunk <<= 1;
+  const int64_t slots = 4 * (int64_t)device_cu_count();
+  const int64_t per_unit = units >= slots ? 1 : slots / units;
+  int64_t chunk = (cache_cap + per_unit - 1) / per_unit;
+  chunk = (chunk + 127) / 128 * 128;
+  if (chunk < 256) chunk = 256;
+  while ((cache_cap + chunk - 1) / chunk > kMaxChunks) chunk += 128;
   geo.chunk = (int)chunk;
   geo.n_chunks = (int)((cache_cap + chunk - 1) / chunk);
   const int64_t parts = (int64_t)batch * n_q_heads * geo.n_chunks;
