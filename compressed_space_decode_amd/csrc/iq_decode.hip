@@ -7,28 +7,34 @@
 // once, V levels are summed in rotated space, and R^T is applied once per
 // output row.
 //
+// Record layout: one little-endian bit stream, code i at bits 3i..3i+2, so
+// bytes 3g..3g+2 hold the codes of coordinates 8g..8g+7 (group g).
+//
 // Kernel 1 (decode_split_kernel): one work-group of 4 waves per (sequence,
 // KV head, group of up to 8 query heads, chunk of tokens).  Each wave works
 // on its own, with no work-group barrier until the final merge:
-//   * set-up: the wave rotates the group's queries in registers (8 lanes per
-//     head, 16 coordinates per lane: cross-lane Hadamard stages through DPP /
-//     swizzle, in-lane stages, then the 4x4 SO(4) blocks) and lays them out as
-//     the fp16 B operand of the QK product, hi and lo parts (q = hi + lo) in
-//     columns n and n+8 so the product carries ~22 bits;
+//   * set-up (wave 0, shared through LDS): the group's queries are rotated in
+//     registers (8 lanes per head, 16 coordinates per lane: cross-lane
+//     Hadamard stages through DPP / swizzle, in-lane stages, then the 4x4
+//     SO(4) blocks) and laid out as the fp16 A operand of the QK product, hi
+//     and lo parts (q = hi + lo) in rows 2h and 2h+1, so the product carries
+//     ~22 bits;
 //   * loop over 32-token blocks; the loads of block i+1 are issued as soon as
-//     block i's codes are unpacked, and overlap the rest of block i.  A lane loads 12 bytes (one quarter of a record) of one
-//     token; one AND per pair of codes turns them into fp16 subnormals
-//     c * 2^(p-24) that the matrix cores multiply exactly, the 2^-p being
-//     folded into the query operand;
-//   * S^T[token][head,part] = codes x q' on v_mfma_f32_16x16x32_f16; the hi and
-//     lo columns are summed with one DPP add; online softmax in base 2;
+//     block i's codes are unpacked, and overlap the rest of block i;
+//   * codes become fp16 operands with one byte permute per three fields and
+//     one AND per pair of codes: a field at bit p of a 16-bit half is the fp16
+//     subnormal c * 2^(p-24) (p <= 7), multiplied exactly by the matrix cores;
+//     the 2^-p is folded into the other operand or undone at the end;
+//   * K: a lane loads one 12-byte quarter (4 groups) of one token, the B
+//     operand of S[head, part][token] = q' x codes (v_mfma_f32_16x16x32_f16);
+//     hi and lo rows are summed in-lane; online softmax in base 2;
 //   * lazy online softmax: the running max moves only when a score passes it
 //     by more than 8 (log2 units), so p <= 256; P'' = p * s_V * 16 / vlim
 //     (vlim a running power of two above every V scale seen) is split hi/lo
-//     in fp16 and staged through LDS as the A operand of the PV product;
-//   * V codes of the block are unpacked the same way into LDS ([token][slot]
-//     rows) and read back transposed with ds_read_b64_tr_b16 as the B operand
-//     of O[head,part][slot] += P'' x V;
+//     in fp16 and transposed through LDS into the A operand of the PV product;
+//   * V: lane (n, g4) loads group n (3 bytes) of 8 tokens, which is exactly
+//     the B operand column n of O[head, part][coordinate 8n + j] += P'' x V for
+//     the 8 tiles j: V never passes through LDS;
 //   * the 4 waves merge in LDS and write one (max, sum, o') partial.
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
@@ -52,31 +58,33 @@ constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running
 constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 
-// Coordinate (within a quarter) held by extraction slot s: the 16 words that
-// one quarter unpacks into carry coordinate (s >> 1) of half (s & 1).
-__device__ __forceinline__ int slot_coord(int s) { return 16 * (s & 1) + (s >> 1); }
-// Power of two carried by slot s: field position p gives the value c * 2^(p-24).
-__device__ __forceinline__ int slot_pow(int s) {
-  const int d = s >> 1;
-  if (d == 15) return 0;
-  const int j = d % 5;
-  return j == 0 ? 0 : j == 1 ? 3 : j == 2 ? 6 : j == 3 ? 0 : 3;
+// Field j (0..7) of a 24-bit group is taken from byte window j / 3 (bytes 0-1, 1-2 or 2-3 of the
+// group) at bit position field_pos(j) <= 7 of each 16-bit half.
+__device__ __forceinline__ constexpr int field_pos(int j) {
+  return j < 3 ? 3 * j : j < 6 ? 3 * j - 8 : 3 * j - 16;
 }
+__device__ __forceinline__ constexpr unsigned field_mask(int j) { return 0x00070007u << field_pos(j); }
 
-// Unpack one quarter (three 32-bit words) into 16 words of fp16 pairs.
-// Word W_k pairs field j of half 0 (low 16 bits) with field j of half 1.
+// K slot s (0..31) of a quarter: fp16 word s/2 of the unpacked quarter, half s%2.  Words 0..7 pair
+// groups 0 and 1 of the quarter (field = word), words 8..15 groups 2 and 3.
+__device__ __forceinline__ int slot_coord(int s) { return 8 * (2 * (s >> 4) + (s & 1)) + ((s >> 1) & 7); }
+__device__ __forceinline__ int slot_pow(int s) { return field_pos((s >> 1) & 7); }
+
+// Unpack one 12-byte quarter (groups 0..3, little-endian words w0..w2) into 16 words of fp16
+// pairs: word 8P + j holds field j of group 2P (low half) and of group 2P + 1 (high half).
 __device__ __forceinline__ void unpack_quarter(unsigned w0, unsigned w1, unsigned w2, unsigned o[16]) {
-  const unsigned w[3] = {w0, w1, w2};
+  // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick bytes of lo, 4-7 bytes of hi.
+  const unsigned win[2][3] = {
+      {__builtin_amdgcn_perm(w1, w0, 0x04030100u),    // bytes 0,1 | 3,4
+       __builtin_amdgcn_perm(w1, w0, 0x05040201u),    // bytes 1,2 | 4,5
+       __builtin_amdgcn_perm(w1, w0, 0x06050302u)},   // bytes 2,3 | 5,6
+      {__builtin_amdgcn_perm(w2, w1, 0x06050302u),    // bytes 6,7 | 9,10
+       __builtin_amdgcn_perm(w2, w1, 0x07060403u),    // bytes 7,8 | 10,11
+       __builtin_amdgcn_perm(w2, w1, 0x07070404u)}};  // byte 8 | byte 11 (upper bytes unused)
 #pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    o[5 * k + 0] = w[k] & 0x00070007u;
-    o[5 * k + 1] = w[k] & 0x00380038u;
-    o[5 * k + 2] = w[k] & 0x01C001C0u;
-    const unsigned sh = w[k] >> 9;
-    o[5 * k + 3] = sh & 0x00070007u;
-    o[5 * k + 4] = sh & 0x00380038u;
-  }
-  o[15] = ((w0 >> 15) & 0x00010001u) | ((w1 >> 14) & 0x00020002u) | ((w2 >> 13) & 0x00040004u);
+  for (int P = 0; P < 2; ++P)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[8 * P + j] = win[P][j / 3] & field_mask(j);
 }
 
 __device__ __forceinline__ half8 as_half8(unsigned a, unsigned b, unsigned c, unsigned d) {
@@ -118,18 +126,19 @@ struct MergeSmem {
   float m[kWaves][8];
   float l[kWaves][8];
 };
-// Per-wave loop staging: unpacked V block [32 tokens][128 slots] fp16 in rows of 288 bytes,
-// the P'' block [32 tokens][16 (head, part)] fp16 in the last 32 bytes of the same rows, and
-// the block's K/V scales.
-constexpr int kVRow = 288;
-constexpr int kPOff = 256;          // P'' row t sits at byte t * kVRow + kPOff
+// Per-wave loop staging: the P'' block [32 tokens][16 (head, part)] fp16 (32-byte rows) and the
+// block's K/V scales.
+constexpr int kPRow = 32;
 struct WaveLoopSmem {
-  char v[kBlock * kVRow];
+  char p[kBlock * kPRow];
   float sc[64];
 };
 // Computed once per work-group by wave 0: the QK A operand in lane order, sum of q' per head,
-// and the operand exponent E.  Shares storage with the loop staging (a barrier separates them).
-struct SetupShared {
+// and the operand exponent E, with wave 0's scratch.  Shares storage with the loop staging (a
+// barrier separates them).
+struct SetupSmem {
+  float qrot[8][128];
+  float blk[32][16];
   uint4v qop[64][4];
   float qsum[8];
   int E;
@@ -137,10 +146,7 @@ struct SetupShared {
 union DecodeSmem {
   MergeSmem merge;
   WaveLoopSmem loop[kWaves];
-  struct {
-    WaveLoopSmem wave0;             // wave 0's set-up scratch lives in its staging rows
-    SetupShared shared;
-  } setup;
+  SetupSmem setup;
 };
 
 __device__ void build_block(const float* p, float* out16) {
@@ -163,22 +169,21 @@ __device__ void build_block(const float* p, float* out16) {
     }
 }
 
-// V staging rows are 288 bytes apart (72 words: consecutive rows start 8 banks apart) and the
-// two 16-byte halves of each 32-byte sector are swapped in rows where bit 2 xor bit 3 of the row
-// is set.  With the token order of the PV product (rows 4*g4 + i/4 and 16 + 4*g4 + i/4), the
-// 16-byte row writes and the transposed 8-byte reads then hit distinct banks, and every read
-// address is a per-lane base plus an immediate.
-__device__ __forceinline__ int vhalf_flip(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+// Token order of the PV product: K slot e of row group g4 is token 4*g4 + e (e < 4) or
+// 16 + 4*g4 + e - 4 (e >= 4) of the block, for both operands.
+__device__ __forceinline__ constexpr int pv_token(int g4, int e) { return e < 4 ? 4 * g4 + e : 12 + 4 * g4 + e; }
 
 struct BlockData {
-  unsigned kw[2][3];
-  unsigned vw[2][3];
+  unsigned kw[2][3];      // K quarter g4 of tokens n and 16 + n
+  unsigned vw[8];         // V group n of token pv_token(g4, e)
   float sc;               // row group 0/1: K scale of token n / 16+n; 2/3: V scale of token n / 16+n
 };
 
-// Per-lane constant offsets of a 32-token block; the block base is a scalar buffer offset.
+// Per-lane constant offsets of a 32-token block; the block base plus a per-load constant is a
+// scalar buffer offset.
 struct LaneOffsets {
-  unsigned code[2];       // byte offset of this lane's quarter in tile tt (token 16*tt + n)
+  unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is +768)
+  unsigned vcode;         // byte offset of this lane's V group in token pv_token(g4, 0)
   unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
 };
 
@@ -197,11 +202,13 @@ __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb,
   const int so = t0 * 48;
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, lo.code[tt], so, 0);
-    const u3v vq = __builtin_amdgcn_raw_buffer_load_b96(cb.vc, lo.code[tt], so, 0);
+    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, lo.kcode, so + 768 * tt, 0);
     d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
-    d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
   }
+  // V: 4-byte loads at byte offset 3n of a record (unaligned); lane 15 loads bytes 44..47.
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    d.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(cb.vc, lo.vcode, so + 48 * pv_token(0, e), 0);
   // Both scale loads run in every lane (one 4-byte load each); a select keeps the resources uniform.
   const unsigned kscale = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, lo.scale, t0 * 4, 0);
   const unsigned vscale_v = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, lo.scale, t0 * 4, 0);
@@ -210,7 +217,7 @@ __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb,
 
 // Running state of one wave's online softmax.  Lane (n, g4) owns heads 2*g4 and 2*g4+1.
 struct WaveState {
-  floatx4 O[8];           // O[(head, part)][slot]: rows 4*g4 + r = (head 2*g4 + r/2, part r%2)
+  floatx4 O[8];           // O[j][(head, part)][n]: coordinate 8n + j, rows 4*g4 + r = (head 2*g4 + r/2, part r%2)
   float m_run[2];         // running max (log2 units), uniform over the 16 lanes of a row group
   float l_run[2];         // sum of p over this lane's tokens
   float ls_run[2];        // sum of P'' over this lane's tokens
@@ -234,13 +241,19 @@ __device__ __forceinline__ float row_sum(float x) {   // sum over the 16 lanes o
 
 typedef __attribute__((address_space(3))) short4v* lds_s4;
 
+// Byte selectors that pair the V group of two tokens into 16-bit windows 0, 1 and 2 (bytes 0-1,
+// 1-2, 2-3 of the group); lane 15's group sits one byte higher in its loaded word.
+struct VSelectors {
+  unsigned w[3];
+};
+
 // Processes the block in `cur` (tokens t0 ..), then refills `cur` with the block at t_next
 // (if any) as soon as the current codes are unpacked, so those loads overlap the rest.
 __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_next, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const half8 (&qop)[4], float c1, const float (&c2)[2],
-                                              WaveLoopSmem& ws, int lane, int n, int g4, unsigned vw0,
-                                              unsigned vw1, unsigned vrd, unsigned prd) {
+                                              WaveLoopSmem& ws, int lane, int n, int g4, const VSelectors& vsel,
+                                              unsigned pwr, unsigned prd) {
   ws.sc[lane] = cur.sc;
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
@@ -256,19 +269,13 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_nex
                                                   acc, 0, 0, 0);
     S[tt] = acc;
   }
-  // ---- V: unpack into the staging rows (read back transposed below) ----
-  char* vbytes = ws.v;
+  // ---- V: the three byte windows of each token pair (tokens pv_token(g4, 2i), (g4, 2i+1)) ----
+  unsigned vwin[4][3];
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    unsigned u[16];
-    unpack_quarter(cur.vw[tt][0], cur.vw[tt][1], cur.vw[tt][2], u);
-    char* r0 = vbytes + 16 * tt * kVRow;
-    *reinterpret_cast<uint4*>(r0 + vw0) = make_uint4(u[0], u[1], u[2], u[3]);
-    *reinterpret_cast<uint4*>(r0 + vw1) = make_uint4(u[4], u[5], u[6], u[7]);
-    *reinterpret_cast<uint4*>(r0 + vw0 + 32) = make_uint4(u[8], u[9], u[10], u[11]);
-    *reinterpret_cast<uint4*>(r0 + vw1 + 32) = make_uint4(u[12], u[13], u[14], u[15]);
-  }
-  // ---- the codes are in registers / LDS now: refill the buffer with the next block ----
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int w = 0; w < 3; ++w) vwin[i][w] = __builtin_amdgcn_perm(cur.vw[2 * i + 1], cur.vw[2 * i], vsel.w[w]);
+  // ---- the codes are in registers now: refill the buffer with the next block ----
   if (t_next < tok_end) load_block(cur, cb, t_next, lo, vscale);
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
@@ -330,20 +337,18 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_nex
       h4[2 * j] = hi;
       h4[2 * j + 1] = (_Float16)(pp - (float)hi);
     }
-    *reinterpret_cast<short4v*>(vbytes + (16 * tt + n) * kVRow + kPOff + 8 * g4) = __builtin_bit_cast(short4v, h4);
+    *reinterpret_cast<short4v*>(ws.p + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, h4);
   }
   __builtin_amdgcn_wave_barrier();
-  // ---- PV: A = P'' (rows (head, part)), B = V; K slot e of row group g4 is token 4*g4 + e
-  //      (e < 4) or 16 + 4*g4 + e - 4 (e >= 4), the same order for both operands ----
-  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + prd));
-  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + prd + 16 * kVRow));
+  // ---- PV: A = P'' (rows (head, part)) read transposed, B = V field j of the token pairs ----
+  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd));
+  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd + 16 * kPRow));
   const half8 pop = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
 #pragma unroll
-  for (int nt = 0; nt < 8; ++nt) {
-    const short4v lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + vrd + 32 * nt));
-    const short4v hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(vbytes + vrd + 16 * kVRow + 32 * nt));
-    const short8v both = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-    st.O[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, __builtin_bit_cast(half8, both), st.O[nt], 0, 0, 0);
+  for (int j = 0; j < 8; ++j) {
+    const unsigned m = field_mask(j);
+    const half8 vb = as_half8(vwin[0][j / 3] & m, vwin[1][j / 3] & m, vwin[2][j / 3] & m, vwin[3][j / 3] & m);
+    st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vb, st.O[j], 0, 0, 0);
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -380,13 +385,19 @@ void decode_split_kernel(DecodeKArgs a) {
   cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
   cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, cap * 4, kBufferConfig);
   cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, cap * 4, kBufferConfig);
-  const int n = lane & 15;          // MFMA column: token within a 16-token tile / V slot
-  const int g4 = lane >> 4;         // row group: quarter of the record; heads 2*g4, 2*g4+1
+  const int n = lane & 15;          // MFMA column: token within a 16-token tile / V group
+  const int g4 = lane >> 4;         // row group: quarter of the K record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
-  lo.code[0] = (unsigned)(n * 48 + 12 * g4);
-  lo.code[1] = (unsigned)((16 + n) * 48 + 12 * g4);
+  lo.kcode = (unsigned)(n * 48 + 12 * g4);
+  lo.vcode = (unsigned)(48 * pv_token(g4, 0) + (n == 15 ? 44 : 3 * n));
   lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
   const bool vscale = g4 >= 2;
+  VSelectors vsel;
+  if (n == 15) {
+    vsel.w[0] = 0x06050201u; vsel.w[1] = 0x07060302u; vsel.w[2] = 0x07070303u;
+  } else {
+    vsel.w[0] = 0x05040100u; vsel.w[1] = 0x06050201u; vsel.w[2] = 0x07060302u;
+  }
 
   // Issue the first block's loads before the set-up so their latency overlaps it.
   const int step = kWaves * kBlock;
@@ -395,12 +406,9 @@ void decode_split_kernel(DecodeKArgs a) {
   if (t0 < tok_end) load_block(buf, cb, t0, lo, vscale);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
-  SetupShared& ss = sm.setup.shared;
+  SetupSmem& ss = sm.setup;
   if (wave == 0) {
-    float* scratch = reinterpret_cast<float*>(sm.setup.wave0.v);   // 9 KB of wave 0's staging rows
-    float* qrot = scratch;                                   // [8][128]
-    float* blk = scratch + 1024;                             // [32][16]
-    if (lane < 32) build_block(rot + lane * 8, blk + lane * 16);
+    if (lane < 32) build_block(rot + lane * 8, ss.blk[lane]);
     const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
     float x[16];
     {
@@ -452,7 +460,7 @@ void decode_split_kernel(DecodeKArgs a) {
     float qamax = 0.f, qs = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* M = blk + (4 * qe + j) * 16;
+      const float* M = ss.blk[4 * qe + j];
       float y[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -460,7 +468,7 @@ void decode_split_kernel(DecodeKArgs a) {
                 M[4 * r + 3] * x[4 * j + 3]) * kInvSqrtD;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        qrot[qi * 128 + 16 * qe + 4 * j + r] = y[r];
+        ss.qrot[qi][16 * qe + 4 * j + r] = y[r];
         qamax = fmaxf(qamax, fabsf(y[r]));
         qs += y[r];
       }
@@ -488,7 +496,7 @@ void decode_split_kernel(DecodeKArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int s = 8 * kb + e;
-        const float v = ldexpf(qrot[head * 128 + 32 * g4 + slot_coord(s)], E - slot_pow(s));
+        const float v = ldexpf(ss.qrot[head][32 * g4 + slot_coord(s)], E - slot_pow(s));
         const _Float16 hi = (_Float16)v;
         hv[e] = part ? (_Float16)(v - (float)hi) : hi;
       }
@@ -501,20 +509,16 @@ void decode_split_kernel(DecodeKArgs a) {
   for (int kb = 0; kb < 4; ++kb) qop[kb] = __builtin_bit_cast(half8, ss.qop[lane][kb]);
   const int E = ss.E;
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
-  __syncthreads();                   // the shared set-up area is staging space from here on
+  __syncthreads();                   // the set-up area is staging space from here on
   WaveLoopSmem& ws = sm.loop[wave];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
   const float c2[2] = {a.sm_log2 * 3.5f * qsum0, a.sm_log2 * 3.5f * qsum1};
-  // LDS addresses: this lane's V staging writes (row n of each tile, sectors 2*g4 and 2*g4+1, the
-  // halves swapped in flipped rows), its transposed V reads (row 4*g4 + n/4, piece n%4) and its
-  // transposed P'' reads.  Tile 1 rows and the second read (+16 rows) keep the same flip.
-  const unsigned vw0 = (unsigned)(n * kVRow + 64 * g4 + 16 * vhalf_flip(n));
-  const unsigned vw1 = (unsigned)(n * kVRow + 64 * g4 + 16 * (1 - vhalf_flip(n)));
-  const int rrow = 4 * g4 + (n >> 2);
-  const unsigned vrd = (unsigned)(rrow * kVRow + 8 * ((n & 3) ^ (2 * vhalf_flip(rrow))));
-  const unsigned prd = (unsigned)(rrow * kVRow + kPOff + 8 * (n & 3));
+  // LDS addresses: this lane's P'' writes (token n of each tile, rows 4*g4..4*g4+3) and its
+  // transposed P'' reads (token row 4*g4 + n/4, piece n%4; tile 1 is 16 rows further).
+  const unsigned pwr = (unsigned)(n * kPRow + 8 * g4);
+  const unsigned prd = (unsigned)((4 * g4 + (n >> 2)) * kPRow + 8 * (n & 3));
 
   WaveState st;
 #pragma unroll
@@ -524,11 +528,10 @@ void decode_split_kernel(DecodeKArgs a) {
   st.ls_run[0] = st.ls_run[1] = 0.f;
   st.vexp = -200;
 
-  // Two buffers in turn: the loads of the next block are in flight while a block is processed.
   while (t0 < tok_end) {
     const int tn = t0 + step;
     process_block(buf, min(tok_end - t0, kBlock), tn, tok_end, cb, lo, vscale, st, qop, c1, c2, ws, lane, n, g4,
-                  vw0, vw1, vrd, prd);
+                  vsel, pwr, prd);
     t0 = tn;
   }
 
@@ -547,18 +550,17 @@ void decode_split_kernel(DecodeKArgs a) {
       sm.merge.l[wave][2 * g4 + j] = l_tot[j];
     }
   }
-  // o'[coord] = vlim/16 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row
+  // o'[coord] = vlim/16 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row; tile j column n is
+  // coordinate 8n + j, taken at bit position field_pos(j).
   {
     const float back = ldexpf(1.f / kPScale, st.vexp);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) {
-      const int slot = 16 * nt + n;          // quarter slot/32, extraction slot slot%32
-      const int qd = slot >> 5, s = slot & 31;
-      const int coord = 32 * qd + slot_coord(s);
-      const float up = ldexpf(1.f, 24 - slot_pow(s));
+    for (int j8 = 0; j8 < 8; ++j8) {
+      const int coord = 8 * n + j8;
+      const float up = (float)(1 << (24 - field_pos(j8)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        sm.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[nt][2 * j] + st.O[nt][2 * j + 1], up, -3.5f * ls_tot[j]);
+        sm.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
     }
   }
   __syncthreads();

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeLaunch a) {
   const float sg1 = (e & 1) ? -1.f : 1.f;
   const float sg2 = (e & 2) ? -1.f : 1.f;
   const float sg4 = (e & 4) ? -1.f : 1.f;
-  const int hh = e & 1;                           // half of the quarter
+  const int hh = e & 1;                           // odd lanes pass their two groups to lane e-1
   const int quarter = e >> 1;
 
   for (int step = 0; step < kTokPerGroup / kVecPerStep; ++step) {
@@ -185,29 +185,23 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(QuantizeLaunch a) {
         const float u = floorf(fmaf(y[i], rcp, 4.0f));
         c[i] = (unsigned)fminf(fmaxf(u, 0.f), 7.f);
       }
-      // Pack this half: word k holds codes 5k..5k+4 in bits 0..14 and bit k of
-      // code 15 in bit 15.  Words of the two halves interleave in memory.
-      unsigned w[3];
+      // Pack: the record is one little-endian bit stream with code i at bits 3i..3i+2, so this
+      // lane's 16 codes are the 6 bytes 6e..6e+5, two 24-bit groups of 8 codes.  Even lanes
+      // take their odd neighbour's groups and store the 12-byte quarter e/2.
+      unsigned g0 = 0, g1 = 0;
 #pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        unsigned acc = ((c[15] >> k) & 1u) << 15;
-#pragma unroll
-        for (int j = 0; j < 5; ++j) acc |= c[5 * k + j] << (3 * j);
-        w[k] = acc;
+      for (int k = 0; k < 8; ++k) {
+        g0 |= c[k] << (3 * k);
+        g1 |= c[8 + k] << (3 * k);
       }
-      unsigned out[3];
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        const unsigned other = dpp_xor1_u(w[k]);
-        out[k] = hh ? (other | (w[k] << 16)) : (w[k] | (other << 16));
-      }
+      const unsigned g2 = dpp_xor1_u(g0), g3 = dpp_xor1_u(g1);
       if (valid) {
         const int64_t rec = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset + t;
         if (hh == 0) {
           unsigned* dst = reinterpret_cast<unsigned*>(side.codes + rec * 48 + 12 * quarter);
-          dst[0] = out[0];
-          dst[1] = out[1];
-          dst[2] = out[2];
+          dst[0] = g0 | (g1 << 24);
+          dst[1] = (g1 >> 8) | (g2 << 16);
+          dst[2] = (g2 >> 16) | (g3 << 8);
         }
         if (e == 0) side.scales[rec] = scale;
       }

@@ -145,35 +145,26 @@ def dequantize_rotated(codes, scales):
 # Bit layout of a 48-byte record (Abstract: "packed 3-bit tensors"; the
 # layout itself is a reading).
 #
-# The record is four 12-byte quarters; quarter q holds coordinates
-# 32q..32q+31 as two halves of 16 (half h: coordinates 32q+16h..32q+16h+15).
-# A quarter is six little-endian 16-bit words u_0..u_5; word u_(2k+h)
-# (k = 0, 1, 2) belongs to half h:
-#   * its bits 3j..3j+2 hold the code of coordinate 32q + 16h + 5k + j (j < 5);
-#   * its bit 15 holds bit k of the code of coordinate 32q + 16h + 15.
+# The 128 codes form one little-endian bit stream of 384 bits: bit b of the
+# code of coordinate i is stream bit 3i + b, and byte k of the record holds
+# stream bits 8k..8k+7 (bit 8k + m is bit m of byte k).  Equivalently, every
+# 3 bytes 3g..3g+2 hold the 8 codes of coordinates 8g..8g+7 as the 24-bit
+# little-endian number sum_j c_(8g+j) 8^j.
 # --------------------------------------------------------------------------
-def _word_index(q, h, k):
-    return 12 * q + 2 * (2 * k + h)     # byte offset of word u_(2k+h) in quarter q
-
-
 def pack(codes):
     """uint8 codes [..., 128] (values 0..7) -> uint8 records [..., 48]."""
     c = np.asarray(codes)
     assert c.shape[-1] == D and np.all(c < LEVELS)
-    c = c.astype(np.uint32)
+    c = c.astype(np.uint8)
     lead = c.shape[:-1]
+    bits = np.zeros(lead + (3 * D,), dtype=np.uint8)        # the stream, one entry per bit
+    for i in range(D):
+        for b in range(3):
+            bits[..., 3 * i + b] = (c[..., i] >> b) & 1
     out = np.zeros(lead + (RECORD_BYTES,), dtype=np.uint8)
-    for q in range(4):
-        for h in range(2):
-            base = 32 * q + 16 * h
-            for k in range(3):
-                w = np.zeros(lead, dtype=np.uint32)
-                for j in range(5):
-                    w |= c[..., base + 5 * k + j] << np.uint32(3 * j)
-                w |= ((c[..., base + 15] >> np.uint32(k)) & np.uint32(1)) << np.uint32(15)
-                off = _word_index(q, h, k)
-                out[..., off] = w & 0xFF
-                out[..., off + 1] = w >> 8
+    for k in range(RECORD_BYTES):
+        for m in range(8):
+            out[..., k] |= bits[..., 8 * k + m] << m
     return out
 
 
@@ -181,19 +172,16 @@ def unpack(records):
     """uint8 records [..., 48] -> uint8 codes [..., 128]; inverse of pack."""
     r = np.asarray(records, dtype=np.uint8)
     assert r.shape[-1] == RECORD_BYTES
-    r = r.astype(np.uint32)
     lead = r.shape[:-1]
-    codes = np.zeros(lead + (D,), dtype=np.uint32)
-    for q in range(4):
-        for h in range(2):
-            base = 32 * q + 16 * h
-            for k in range(3):
-                off = _word_index(q, h, k)
-                w = r[..., off] | (r[..., off + 1] << np.uint32(8))
-                for j in range(5):
-                    codes[..., base + 5 * k + j] = (w >> np.uint32(3 * j)) & np.uint32(7)
-                codes[..., base + 15] |= ((w >> np.uint32(15)) & np.uint32(1)) << np.uint32(k)
-    return codes.astype(np.uint8)
+    bits = np.zeros(lead + (3 * D,), dtype=np.uint8)
+    for k in range(RECORD_BYTES):
+        for m in range(8):
+            bits[..., 8 * k + m] = (r[..., k] >> m) & 1
+    codes = np.zeros(lead + (D,), dtype=np.uint8)
+    for i in range(D):
+        for b in range(3):
+            codes[..., i] |= bits[..., 3 * i + b] << b
+    return codes
 
 
 # --------------------------------------------------------------------------

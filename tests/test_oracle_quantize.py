@@ -109,7 +109,8 @@ def test_quantize_error_bound():
     assert np.all(err <= s[:, None] / 2 * (1 + 1e-12))
 
 
-@pytest.mark.parametrize("name", ["all7", "all0", "all4", "mod8", "c127is5", "c70is3", "c21is6", "c15is6"])
+@pytest.mark.parametrize("name", ["all7", "all0", "all4", "mod8", "c127is5", "c70is3", "c21is6", "c15is6",
+                                  "c2is7", "c5is7"])
 def test_pack_golden_records(name):
     recs = _golden_records()
     codes = np.zeros(128, dtype=np.uint8)
@@ -127,6 +128,10 @@ def test_pack_golden_records(name):
         codes[21] = 6
     elif name == "c15is6":
         codes[15] = 6
+    elif name == "c2is7":
+        codes[2] = 7
+    elif name == "c5is7":
+        codes[5] = 7
     np.testing.assert_array_equal(oracle.pack(codes), recs[name])
     np.testing.assert_array_equal(oracle.unpack(recs[name]), codes)
 
