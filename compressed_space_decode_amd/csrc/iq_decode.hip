@@ -53,6 +53,8 @@ typedef unsigned uint4v __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 32;          // tokens per wave step
+constexpr int kWavesPerSimd = 3;    // occupancy the split kernel is built for (register budget)
+constexpr int kGroupsPerCU = kWavesPerSimd;   // one wave of each work-group per SIMD
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running max before a rescale
 constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
@@ -133,20 +135,24 @@ struct WaveLoopSmem {
   char p[kBlock * kPRow];
   float sc[64];
 };
-// Computed once per work-group by wave 0: the QK A operand in lane order, sum of q' per head,
-// and the operand exponent E, with wave 0's scratch.  Shares storage with the loop staging (a
-// barrier separates them).
+// Computed once per work-group by wave 0: sum of q' per head and the operand exponent E, with
+// wave 0's scratch.  Shares storage with the loop staging (a barrier separates them).
 struct SetupSmem {
   float qrot[8][128];
   float blk[32][16];
-  uint4v qop[64][4];
   float qsum[8];
   int E;
 };
-union DecodeSmem {
+union DecodeSmemU {
   MergeSmem merge;
   WaveLoopSmem loop[kWaves];
   SetupSmem setup;
+};
+// The QK A operand in lane order (the same for the 4 waves), built once and read from LDS for
+// every block, which keeps 16 registers per lane free for a second block in flight.
+struct DecodeSmem {
+  uint4v qop[4][64];
+  DecodeSmemU u;
 };
 
 __device__ void build_block(const float* p, float* out16) {
@@ -176,43 +182,59 @@ __device__ __forceinline__ constexpr int pv_token(int g4, int e) { return e < 4 
 struct BlockData {
   unsigned kw[2][3];      // K quarter g4 of tokens n and 16 + n
   unsigned vw[8];         // V group n of token pv_token(g4, e)
-  float sc;               // row group 0/1: K scale of token n / 16+n; 2/3: V scale of token n / 16+n
+  unsigned ksc, vsc;      // K and V scale bits of token n (row groups 0, 2) or 16 + n (1, 3)
 };
 
-// Per-lane constant offsets of a 32-token block; the block base plus a per-load constant is a
-// scalar buffer offset.
+// Per-lane constant byte offsets within a 32-token block.
 struct LaneOffsets {
   unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is +768)
   unsigned vcode;         // byte offset of this lane's V group in token pv_token(g4, 0)
   unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
 };
 
-// Raw buffer resources over one (sequence, KV head)'s codes and scales.  Loads past the
-// end of a buffer return zeros, so a block that reaches past the cache needs no clamping
-// (those tokens are masked out of the softmax anyway).
+// Raw buffer resources over one (sequence, KV head)'s codes and scales.  Every access puts its
+// whole offset in the range-checked part of the address, so one past the end of the slice reads
+// zeros without reaching memory (a partial last block needs no clamping: those tokens are masked
+// out of the softmax anyway).
 struct CacheBuffers {
   __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
 };
 
 constexpr int kBufferConfig = 0x00020000;   // raw (untyped) buffer, 32-bit data format
 
-__device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb, int t0, const LaneOffsets& lo,
-                                           bool vscale) {
+// Block base for a block that is not to be read: beyond every slice (capacity * 48 is validated
+// to stay below it), so its loads return zeros without reaching memory.
+constexpr unsigned kNoBlock = 0xF0000000u;
+
+// Keeps v in a register as an opaque value, so per-load constants added to it stay immediate
+// offsets instead of becoming separate loop-invariant registers.
+__device__ __forceinline__ unsigned opaque(unsigned v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Issues the loads of the block at token t0, or, if t0 is not below tok_end, loads that read
+// zeros without a memory access.  The whole offset is in the range-checked part of the buffer
+// address (vector offset plus immediate), so tokens past the end of the slice read as zeros too.
+__device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb, int t0, int tok_end,
+                                           const LaneOffsets& lo) {
   typedef unsigned u3v __attribute__((ext_vector_type(3)));
-  const int so = t0 * 48;
+  const bool in = t0 < tok_end;                                      // uniform
+  const unsigned base = in ? (unsigned)t0 * 48u : kNoBlock;
+  const unsigned ko = opaque(lo.kcode + base), vo = opaque(lo.vcode + base);
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, lo.kcode, so + 768 * tt, 0);
+    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, ko + 768 * tt, 0, 0);
     d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
   }
   // V: 4-byte loads at byte offset 3n of a record (unaligned); lane 15 loads bytes 44..47.
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    d.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(cb.vc, lo.vcode, so + 48 * pv_token(0, e), 0);
-  // Both scale loads run in every lane (one 4-byte load each); a select keeps the resources uniform.
-  const unsigned kscale = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, lo.scale, t0 * 4, 0);
-  const unsigned vscale_v = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, lo.scale, t0 * 4, 0);
-  d.sc = __uint_as_float(vscale ? vscale_v : kscale);
+  for (int e = 0; e < 8; ++e) d.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(cb.vc, vo + 48 * pv_token(0, e), 0, 0);
+  // Both scale loads run in every lane (keeps the resources uniform); the block's consumer picks
+  // one, so nothing here waits for the loads.
+  const unsigned so = lo.scale + (in ? (unsigned)t0 * 4u : kNoBlock);
+  d.ksc = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, so, 0, 0);
+  d.vsc = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, so, 0, 0);
 }
 
 // Running state of one wave's online softmax.  Lane (n, g4) owns heads 2*g4 and 2*g4+1.
@@ -247,14 +269,15 @@ struct VSelectors {
   unsigned w[3];
 };
 
-// Processes the block in `cur` (tokens t0 ..), then refills `cur` with the block at t_next
-// (if any) as soon as the current codes are unpacked, so those loads overlap the rest.
-__device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_next, int tok_end,
+// Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
+// t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
+// past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
+__device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
-                                              WaveState& st, const half8 (&qop)[4], float c1, const float (&c2)[2],
+                                              WaveState& st, const uint4v (&qop)[4][64], float c1, const float (&c2)[2],
                                               WaveLoopSmem& ws, int lane, int n, int g4, const VSelectors& vsel,
                                               unsigned pwr, unsigned prd) {
-  ws.sc[lane] = cur.sc;
+  ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
 #pragma unroll
@@ -264,7 +287,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_nex
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qop[kb],
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[kb][lane]),
                                                   as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
                                                   acc, 0, 0, 0);
     S[tt] = acc;
@@ -275,8 +298,11 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_nex
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int w = 0; w < 3; ++w) vwin[i][w] = __builtin_amdgcn_perm(cur.vw[2 * i + 1], cur.vw[2 * i], vsel.w[w]);
-  // ---- the codes are in registers now: refill the buffer with the next block ----
-  if (t_next < tok_end) load_block(cur, cb, t_next, lo, vscale);
+  // ---- the codes are in registers now: refill the buffer.  The scheduling barrier keeps the
+  //      loads behind the last reads of the old contents, so they land in the same registers
+  //      (no copies, and no waits for them, at the loop back-edge). ----
+  __builtin_amdgcn_sched_barrier(0);
+  load_block(cur, cb, t_refill, tok_end, lo);
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
   float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
@@ -353,7 +379,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_nex
   __builtin_amdgcn_wave_barrier();
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
   const int chunk_id = blockIdx.x;
@@ -399,14 +425,11 @@ void decode_split_kernel(DecodeKArgs a) {
     vsel.w[0] = 0x05040100u; vsel.w[1] = 0x06050201u; vsel.w[2] = 0x07060302u;
   }
 
-  // Issue the first block's loads before the set-up so their latency overlaps it.
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
-  BlockData buf;
-  if (t0 < tok_end) load_block(buf, cb, t0, lo, vscale);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
-  SetupSmem& ss = sm.setup;
+  SetupSmem& ss = sm.u.setup;
   if (wave == 0) {
     if (lane < 32) build_block(rot + lane * 8, ss.blk[lane]);
     const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
@@ -500,17 +523,14 @@ void decode_split_kernel(DecodeKArgs a) {
         const _Float16 hi = (_Float16)v;
         hv[e] = part ? (_Float16)(v - (float)hi) : hi;
       }
-      ss.qop[lane][kb] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+      sm.qop[kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
     }
   }
   __syncthreads();
-  half8 qop[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) qop[kb] = __builtin_bit_cast(half8, ss.qop[lane][kb]);
   const int E = ss.E;
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
   __syncthreads();                   // the set-up area is staging space from here on
-  WaveLoopSmem& ws = sm.loop[wave];
+  WaveLoopSmem& ws = sm.u.loop[wave];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
@@ -528,11 +548,26 @@ void decode_split_kernel(DecodeKArgs a) {
   st.ls_run[0] = st.ls_run[1] = 0.f;
   st.vexp = -200;
 
-  while (t0 < tok_end) {
-    const int tn = t0 + step;
-    process_block(buf, min(tok_end - t0, kBlock), tn, tok_end, cb, lo, vscale, st, qop, c1, c2, ws, lane, n, g4,
-                  vsel, pwr, prd);
-    t0 = tn;
+  // The first three blocks' loads are issued after the set-up: the set-up's own loads and waits
+  // sit in a branch, and issuing these behind it keeps the count of loads in flight exact.
+  BlockData buf, buf2, buf3;
+  load_block(buf, cb, t0, tok_end, lo);
+  load_block(buf2, cb, t0 + step, tok_end, lo);
+  load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
+  // Three buffers in turn, each refilled three blocks ahead: while block i is processed, blocks
+  // i+1 and i+2 are in flight and block i+3's loads are issued once block i is unpacked.
+  while (t0 < tok_end) {            // uniform
+    process_block(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                  lane, n, g4, vsel, pwr, prd);
+    t0 += step;
+    if (t0 >= tok_end) break;
+    process_block(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                  lane, n, g4, vsel, pwr, prd);
+    t0 += step;
+    if (t0 >= tok_end) break;
+    process_block(buf3, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                  lane, n, g4, vsel, pwr, prd);
+    t0 += step;
   }
 
   // ---------------- per-wave results ----------------
@@ -546,8 +581,8 @@ void decode_split_kernel(DecodeKArgs a) {
   if (n == 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      sm.merge.m[wave][2 * g4 + j] = st.m_run[j];
-      sm.merge.l[wave][2 * g4 + j] = l_tot[j];
+      sm.u.merge.m[wave][2 * g4 + j] = st.m_run[j];
+      sm.u.merge.l[wave][2 * g4 + j] = l_tot[j];
     }
   }
   // o'[coord] = vlim/16 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row; tile j column n is
@@ -560,7 +595,7 @@ void decode_split_kernel(DecodeKArgs a) {
       const float up = (float)(1 << (24 - field_pos(j8)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        sm.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
+        sm.u.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
     }
   }
   __syncthreads();
@@ -569,14 +604,14 @@ void decode_split_kernel(DecodeKArgs a) {
     const int hrow = idx >> 7, d = idx & 127;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.merge.m[w][hrow]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hrow]);
     float L = 0.f, acc = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.merge.m[w][hrow];
+      const float mw = sm.u.merge.m[w][hrow];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * sm.merge.l[w][hrow];
-      acc += f * sm.merge.o[w][hrow][d];
+      L += f * sm.u.merge.l[w][hrow];
+      acc += f * sm.u.merge.o[w][hrow][d];
     }
     const int64_t pidx = ((int64_t)b * a.Hq + h0 + hrow) * a.n_chunks + chunk_id;
     a.part_o[pidx * 128 + d] = acc;
@@ -700,11 +735,11 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   DecodeGeometry geo{};
   const int G = n_q_heads / n_kv_heads;
   geo.head_groups = (G + 7) / 8;
-  // One round of work-groups: 4 are resident per compute unit.  Each (sequence, KV head, head
+  // One round of work-groups: kGroupsPerCU are resident per compute unit.  Each (sequence, KV head, head
   // group) unit gets floor(slots / units) chunks (at least one); chunks are multiples of 128
   // tokens (one step of the 4 waves), at least 256, and no row has more than kMaxChunks of them.
   const int64_t units = (int64_t)batch * n_kv_heads * geo.head_groups;
-  const int64_t slots = 4 * (int64_t)device_cu_count();
+  const int64_t slots = kGroupsPerCU * (int64_t)device_cu_count();
   const int64_t per_unit = units >= slots ? 1 : slots / units;
   int64_t chunk = (cache_cap + per_unit - 1) / per_unit;
   chunk = (chunk + 127) / 128 * 128;
