@@ -111,8 +111,10 @@ extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64
 namespace {
 
 // The decode kernels address one (sequence, KV head)'s codes through a buffer resource with a
-// 32-bit byte range, and token indices are 32-bit.
-constexpr int64_t kMaxCacheCap = 0xFFFFFFFFll / 48;
+// 32-bit byte range and mark blocks that must not be read with the offset 0xF0000000, which has
+// to lie past every slice: cache_cap * 48 stays below it with a 64-token margin (83,886,016
+// tokens).
+constexpr int64_t kMaxCacheCap = 0xF0000000ll / 48 - 64;
 
 int check_decode_sizes(const char* fn, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap) {
   if (batch < 1 || batch > 65535 || n_q_heads < 1 || n_kv_heads < 1 || cache_cap < 1) {

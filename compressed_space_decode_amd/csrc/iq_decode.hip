@@ -391,7 +391,7 @@ void decode_split_kernel(DecodeKArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
 
   // Token indices are 32-bit and a sequence's codes fit one buffer resource (the capacity is
-  // validated: cap * 48 < 2^32): uniform token arithmetic stays on the scalar unit.
+  // validated: cap * 48 < 0xF0000000): uniform token arithmetic stays on the scalar unit.
   const int cap = (int)a.cap;
   int len = cap;
   if (a.seq_lens) {

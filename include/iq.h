@@ -152,7 +152,7 @@ int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  *   workspace    device buffer of at least iq_decode_workspace_bytes(...)
  *                bytes, 256-byte aligned, used only during the call.
  * Errors: IQ_EINVAL (NULL pointers, sizes < 1, n_q_heads % n_kv_heads != 0,
- * cache_cap > (2^32 - 1) / 48 = 89478485, negative stride, misaligned
+ * cache_cap > 83886016 (= 0xF0000000 / 48 - 64), negative stride, misaligned
  * pointers: q 16 bytes, the rest 4), IQ_EWORKSPACE,
  * IQ_EUNSUPPORTED, IQ_EHIP.
  */

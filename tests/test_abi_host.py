@@ -102,6 +102,7 @@ def _dec(**kw):
     (dict(Hq=6, Hkv=4), binding.IQ_EINVAL),
     (dict(B=0), binding.IQ_EINVAL),
     (dict(cap=0), binding.IQ_EINVAL),
+    (dict(cap=83886017), binding.IQ_EINVAL),     # cache_cap * 48 must stay below 0xF0000000 - 64 * 48
     (dict(q=None), binding.IQ_EINVAL),
     (dict(vs=None), binding.IQ_EINVAL),
     (dict(rs=-1), binding.IQ_EINVAL),
@@ -122,3 +123,5 @@ def test_workspace_bytes():
     assert (n - 256) % (130 * 4) == 0
     assert iq.lib().iq_decode_workspace_bytes(1, 6, 4, 100) == binding.IQ_EINVAL
     assert iq.decode_workspace_bytes(16, 32, 8, 32768) >= iq.decode_workspace_bytes(1, 32, 8, 32768)
+    assert iq.decode_workspace_bytes(1, 32, 4, 83886016) > 0          # the largest capacity
+    assert iq.lib().iq_decode_workspace_bytes(1, 32, 4, 83886017) == binding.IQ_EINVAL
