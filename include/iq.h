@@ -32,13 +32,11 @@
  *   quantizer        x' = R x; s = max|x'| / 3.5 (fp32, one per vector);
  *                    code = clamp(floor(x'/s + 4), 0, 7); level s*(c-3.5);
  *                    a zero vector gives s = 0 and all codes 4.
- *   code record      48 bytes per vector: four 12-byte quarters, quarter q
- *                    holds coordinates 32q..32q+31 in two halves of 16
- *                    (half h = 32q+16h .. 32q+16h+15) as six little-endian
- *                    16-bit words u_0..u_5; word u_(2k+h), k = 0..2, belongs
- *                    to half h: its bits 3j..3j+2 hold coordinate
- *                    32q+16h+5k+j (j<5) and its bit 15 holds bit k of
- *                    coordinate 32q+16h+15.
+ *   code record      48 bytes per vector, one little-endian bit stream:
+ *                    bit b of the code of coordinate i is stream bit 3i + b,
+ *                    and byte k holds stream bits 8k..8k+7 (bit 8k + m is
+ *                    bit m of byte k).  Bytes 3g..3g+2 hold the codes of
+ *                    coordinates 8g..8g+7 as sum_j c_(8g+j) * 8^j.
  *   KV cache         codes uint8[n_seq][n_heads][cache_cap][48] and scales
  *                    float[n_seq][n_heads][cache_cap], contiguous.
  */
