@@ -14,11 +14,16 @@ attended per second, summed over layers, each position covering all 4 KV
 heads.  The roofline object is for the decode call (split-K kernel plus its
 small combine kernel), timed with HIP events on the stream it runs on; its
 algorithmic bytes are the packed K/V codes and scales read, 104 bytes per
-(token, KV head).  Extra fields report a single-layer decode call and the
-bulk prefill quantization (48 layers x 4 KV heads x 32768 tokens, K and V
-Student-t(3), bf16) against the same roofline.
+(token, KV head); `traffic` is the HBM bytes per call from the committed
+rocprofv3 counter runs (profiles/decode_traffic.json), reported only while the
+decode kernel source is the one those counters were taken on.  Extra fields
+report a single-layer decode call, the GQA 8K and ragged-batch decode shapes,
+and the bulk prefill quantization (48 layers x 4 KV heads x 32768 tokens, K
+and V Student-t(3), bf16) against the same roofline.  The default warm-up
+(800 untimed steps) lets the GPU clocks settle before timing.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -32,16 +37,31 @@ sys.path.insert(0, ROOT)
 LAYERS, HQ, HKV, T, D = 48, 32, 4, 32768, 128
 BYTES_PER_TOKEN_HEAD = 2 * (48 + 4)          # K and V: 48-byte record + fp32 scale
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs, or None
+    when the decode kernel source has changed since those counters were taken."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=800, help="untimed steps first (lets the clocks settle)")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-other-shapes", action="store_true", help="skip the gqa8k and ragged decode timings")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
@@ -166,6 +186,41 @@ def main():
     single = {"ms": t_decode1 * 1e3, "GBs": T * HKV * BYTES_PER_TOKEN_HEAD / t_decode1 / 1e9,
               "kv_tokens_per_s": T / t_decode1}
 
+    # ---------------- the other decode shapes: GQA at 8K and the ragged batch ----------------
+    others = {}
+    if not args.no_other_shapes:
+        for name in ("gqa8k", "ragged"):
+            wo = W.decode_workload(name)
+            Bo, Hkvo, To = wo["k"].shape[:3]
+            Hqo = wo["q"].shape[1]
+            ko, vo = bf16(wo["k"]), bf16(wo["v"])
+            roto = torch.from_numpy(wo["params"]).to(dev)
+            kco = torch.empty((Bo, Hkvo, To, 48), dtype=torch.uint8, device=dev)
+            vco = torch.empty_like(kco)
+            kso = torch.empty((Bo, Hkvo, To), dtype=torch.float32, device=dev)
+            vso = torch.empty_like(kso)
+            iq.quantize_kv(ko, vo, roto, kco, kso, vco, vso)
+            del ko, vo
+            qo = bf16(wo["q"])
+            lo = torch.from_numpy(wo["seq_lens"]).to(dev)
+            outo = torch.empty((Bo, Hqo, D), dtype=torch.float32, device=dev)
+            wso = torch.empty(iq.decode_workspace_bytes(Bo, Hqo, Hkvo, To), dtype=torch.uint8, device=dev)
+
+            def dec_o():
+                iq.decode_attention(qo, kco, kso, vco, vso, roto, seq_lens=lo, out=outo, workspace=wso)
+
+            for _ in range(args.warmup // 4):
+                dec_o()
+            t_o = time_calls(dec_o, max(20, args.steps // 4), stream)
+            toks = int(wo["seq_lens"].sum())
+            others[name] = {"batch": int(Bo), "n_q_heads": int(Hqo), "n_kv_heads": int(Hkvo), "cache_cap": int(To),
+                            "kv_tokens": toks, "ms": t_o * 1e3, "kv_tokens_per_s": toks / t_o,
+                            "GBs": toks * Hkvo * BYTES_PER_TOKEN_HEAD / t_o / 1e9,
+                            "frac_of_hbm_peak": toks * Hkvo * BYTES_PER_TOKEN_HEAD / t_o / 1e9 / HBM_PEAK_GBS}
+            log("%s decode %.1f us, %.0f GB/s" % (name, t_o * 1e6, others[name]["GBs"]))
+            del kco, vco, kso, vso, wso, wo
+        torch.cuda.empty_cache()
+
     # ---------------- bulk prefill quantization ----------------
     prefill = None
     if not args.no_prefill:
@@ -242,12 +297,13 @@ def main():
                    "layers": L, "batch": 1, "n_q_heads": HQ, "n_kv_heads": HKV, "context": T,
                    "head_dim": D, "kv_bits": 3},
         "roofline": {"bound": "hbm", "achieved": decode_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": decode_gbs / HBM_PEAK_GBS, "traffic": None,
+                     "frac": decode_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "iq_decode_attention (decode_split_kernel + combine_kernel)",
                      "algorithmic_bytes_per_launch": decode_bytes, "avg_launch_us": t_decode * 1e6},
         "decode_ms": t_decode * 1e3,
         "append_ms": t_append * 1e3,
         "single_layer_decode": single,
+        "other_decode_shapes": others,
         "prefill_quantize": prefill,
         "cpu_baseline": cpu,
     }

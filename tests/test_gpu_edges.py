@@ -106,7 +106,7 @@ def test_quantize_zero_tokens_is_noop():
     assert torch.all(kc == 0xFF)
 
 
-def _decode_case(rng, B, Hq, Hkv, cap, lens, qdtype="bf16", sm=0.0, shared=False):
+def _decode_case(rng, B, Hq, Hkv, cap, lens, qdtype="bf16", sm=0.0, shared=False, workspace=None):
     k = rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32) * 1.5
     v = rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)
     q = rng.standard_normal((B, Hq, 128)).astype(np.float32) * 2.0
@@ -121,7 +121,7 @@ def _decode_case(rng, B, Hq, Hkv, cap, lens, qdtype="bf16", sm=0.0, shared=False
     qin = W.f32_to_bf16_bits(q) if qdtype == "bf16" else q
     lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = iq.decode_attention(P.torch_input(qin, qdtype), kc, ks, vc, vs, rot, seq_lens=lens_t, sm_scale=sm,
-                              shared_rot=shared)
+                              shared_rot=shared, workspace=workspace)
     torch.cuda.synchronize()
     pfull = np.broadcast_to(params, (B, Hkv, 32, 8)) if shared else params
     ref = oracle.decode_attention(W.to_f64(qin, qdtype), oracle.unpack(kc.cpu().numpy()), ks.cpu().numpy(),
@@ -157,3 +157,14 @@ def test_decode_single_token_is_its_value():
     rng = np.random.default_rng(12)
     out, ref = _decode_case(rng, 1, 4, 1, 64, [1])
     P.check_output(out, ref, "len=1")
+
+
+def test_decode_workspace_reused_across_calls():
+    # One workspace (never cleared, initially garbage) serves consecutive calls of different
+    # lengths, including an empty sequence: nothing from an earlier call leaks into a later one.
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, cap = 3, 16, 2, 6000
+    ws = torch.full((iq.decode_workspace_bytes(B, Hq, Hkv, cap),), 0x7F, dtype=torch.uint8, device="cuda")
+    for lens in ([6000, 3000, 17], [1, 0, 5999], [4096, 4097, 128]):
+        out, ref = _decode_case(rng, B, Hq, Hkv, cap, lens, workspace=ws)
+        P.check_output(out, ref, what="workspace reuse lens=%s" % lens)
