@@ -6,6 +6,6 @@ Method: "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
 Compressed-Space Attention" (arXiv 2608.08081), Abstract.
 """
 from .iq import (  # noqa: F401
-    IQError, make_rotation, quantize_kv, decode_workspace_bytes, decode_attention,
+    IQError, make_rotation, quantize_kv, decode_workspace_bytes, decode_attention, decode_attention_append,
     lib, LIB_PATH, HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS,
 )

@@ -203,3 +203,76 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
   }
   return IQ_OK;
 }
+
+extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,
+                                          int32_t new_dtype, int64_t new_stride_seq, int64_t new_stride_head,
+                                          const int32_t* positions, uint8_t* k_codes, float* k_scales,
+                                          uint8_t* v_codes, float* v_scales, const float* rot,
+                                          int64_t rot_stride_batch, int32_t batch, int32_t n_q_heads,
+                                          int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out,
+                                          void* workspace, int64_t workspace_bytes, int32_t head_dim, int32_t bits,
+                                          void* stream) {
+  static const char* fn = "iq_decode_attention_append";
+  iq::clear_error();
+  int rc = check_dims(fn, head_dim, bits);
+  if (rc) return rc;
+  if ((q_dtype != IQ_F32 && q_dtype != IQ_BF16) || (new_dtype != IQ_F32 && new_dtype != IQ_BF16)) {
+    iq::set_error("%s: unknown dtype (q %d, new %d)", fn, q_dtype, new_dtype);
+    return IQ_EUNSUPPORTED;
+  }
+  rc = check_decode_sizes(fn, batch, n_q_heads, n_kv_heads, cache_cap);
+  if (rc) return rc;
+  if (!q || !k_new || !v_new || !positions || !k_codes || !k_scales || !v_codes || !v_scales || !rot || !out) {
+    iq::set_error("%s: a required pointer is NULL", fn);
+    return IQ_EINVAL;
+  }
+  if (rot_stride_batch < 0 || new_stride_seq < 0 || new_stride_head < 0) {
+    iq::set_error("%s: strides must be >= 0", fn);
+    return IQ_EINVAL;
+  }
+  const int64_t vec_align = new_dtype == IQ_BF16 ? 8 : 4;   // 16 bytes
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (new_stride_seq % vec_align) || (new_stride_head % vec_align)) {
+    iq::set_error("%s: k_new and v_new must be 16-byte aligned with strides a multiple of 16 bytes", fn);
+    return IQ_EINVAL;
+  }
+  if (!aligned(k_codes, 4) || !aligned(v_codes, 4) || !aligned(k_scales, 4) || !aligned(v_scales, 4) ||
+      !aligned(rot, 4) || !aligned(out, 4) || !aligned(q, 16) || !aligned(positions, 4)) {
+    iq::set_error("%s: misaligned pointer", fn);
+    return IQ_EINVAL;
+  }
+  const iq::DecodeGeometry geo = iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap);
+  if (!workspace || workspace_bytes < geo.workspace_bytes || !aligned(workspace, 256)) {
+    iq::set_error("%s: workspace must be 256-byte aligned and hold %lld bytes (got %lld)", fn,
+                  (long long)geo.workspace_bytes, (long long)workspace_bytes);
+    return IQ_EWORKSPACE;
+  }
+  iq::DecodeLaunch a{};
+  a.q = q;
+  a.q_bf16 = q_dtype == IQ_BF16;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.v_codes = v_codes;
+  a.v_scales = v_scales;
+  a.rot = rot;
+  a.rot_stride_batch = rot_stride_batch;
+  a.seq_lens = nullptr;
+  a.batch = batch;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.cache_cap = cache_cap;
+  a.sm_scale = sm_scale;
+  a.out = out;
+  a.workspace = workspace;
+  a.positions = positions;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_bf16 = new_dtype == IQ_BF16;
+  a.new_stride_seq = new_stride_seq;
+  a.new_stride_head = new_stride_head;
+  const hipError_t err = iq::launch_decode(a, geo, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
+    return IQ_EHIP;
+  }
+  return IQ_OK;
+}

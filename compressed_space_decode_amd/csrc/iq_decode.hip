@@ -40,6 +40,7 @@
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
 // blocks followed by the Hadamard transform).
 #include "iq_internal.h"
+#include "iq_vector.h"
 
 namespace iq {
 namespace {
@@ -121,6 +122,12 @@ struct DecodeKArgs {
   float sm_log2;          // softmax scale times log2(e)
   float* part_o;          // [B][Hq][n_chunks][128]
   float* part_ml;         // [B][Hq][n_chunks][2]  (max in log2 units, sum)
+  // fused append (positions != NULL): new token of sequence b written at positions[b]
+  const int32_t* positions;
+  const void* k_new;
+  const void* v_new;
+  int new_bf16;
+  int64_t new_stride_seq, new_stride_head;
 };
 
 struct MergeSmem {
@@ -274,9 +281,9 @@ struct VSelectors {
 // past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
 __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
-                                              WaveState& st, const uint4v (&qop)[4][64], float c1, const float (&c2)[2],
-                                              WaveLoopSmem& ws, int lane, int n, int g4, const VSelectors& vsel,
-                                              unsigned pwr, unsigned prd) {
+                                              WaveState& st, const uint4v (&qop)[4][64], float c1,
+                                              const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
+                                              const VSelectors& vsel, unsigned pwr, unsigned prd) {
   ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
@@ -379,6 +386,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   __builtin_amdgcn_wave_barrier();
 }
 
+template <bool kAppend>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
@@ -394,7 +402,12 @@ void decode_split_kernel(DecodeKArgs a) {
   // validated: cap * 48 < 0xF0000000): uniform token arithmetic stays on the scalar unit.
   const int cap = (int)a.cap;
   int len = cap;
-  if (a.seq_lens) {
+  int pos = -1;                      // fused append: position of the new token (-1: none)
+  if (kAppend) {
+    const int p = a.positions[b];
+    pos = (p >= 0 && p < cap) ? p : -1;
+    len = pos + 1;                   // a position outside the cache skips the sequence
+  } else if (a.seq_lens) {
     const int l = a.seq_lens[b];
     len = l < 0 ? 0 : (l > cap ? cap : l);
   }
@@ -526,6 +539,36 @@ void decode_split_kernel(DecodeKArgs a) {
       sm.qop[kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
     }
   }
+  // ---------------- fused append (wave 1 of the chunk that holds the new token) ----------------
+  // The new K (lanes 0-7) and V (lanes 8-15) vectors of this KV head are rotated, quantised and
+  // packed as by the quantize kernel and stored into the cache.  The barrier below makes the
+  // stores visible to the whole work-group, and every load of the cache is issued after it.
+  if (kAppend && pos >= tok0 && pos < tok_end && wave == 1) {
+    const int side = (lane >> 3) & 1, e = lane & 7;
+    float* fold = &sm.u.merge.o[2][0][0];   // [32][16] folded blocks; clear of wave 0's set-up data
+    if (lane < 32) vec::build_folded_block(rot + lane * 8, fold + lane * 16);
+    __builtin_amdgcn_wave_barrier();
+    const float (&F)[4][16] = *reinterpret_cast<const float(*)[4][16]>(fold + 64 * e);
+    float x[16];
+    const void* src = side ? a.v_new : a.k_new;
+    const int64_t off = (int64_t)b * a.new_stride_seq + (int64_t)g * a.new_stride_head + 16 * e;
+    if (a.new_bf16)
+      vec::load16<true>(src, off, lane < 16, x);
+    else
+      vec::load16<false>(src, off, lane < 16, x);
+    unsigned g0, g1, w[3];
+    const float scale = vec::quantize8(x, F, e, g0, g1);
+    vec::quarter_words(g0, g1, w);
+    if (lane < 16) {
+      const int64_t rec = kv * a.cap + pos;
+      if ((e & 1) == 0) {
+        unsigned* dst = reinterpret_cast<unsigned*>(const_cast<uint8_t*>(side ? a.vc : a.kc) + rec * 48 + 6 * e);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) dst[i] = w[i];
+      }
+      if (e == 0) const_cast<float*>(side ? a.vs : a.ks)[rec] = scale;
+    }
+  }
   __syncthreads();
   const int E = ss.E;
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
@@ -628,6 +671,7 @@ struct CombineArgs {
   const float* rot;
   int64_t rot_stride_b;
   const int32_t* seq_lens;
+  const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
   int Hq, G;
   int64_t cap;
   int chunk, n_chunks;
@@ -646,7 +690,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   const int g = h / a.G;
   const int d = threadIdx.x;
   int64_t len = a.cap;
-  if (a.seq_lens) {
+  if (a.positions) {
+    const int64_t p = a.positions[b];
+    len = (p >= 0 && p < a.cap) ? p + 1 : 0;
+  } else if (a.seq_lens) {
     const int64_t l = a.seq_lens[b];
     len = l < 0 ? 0 : (l > a.cap ? a.cap : l);
   }
@@ -779,8 +826,17 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.sm_log2 = sm * kLog2e;
   k.part_o = part_o;
   k.part_ml = part_ml;
+  k.positions = a.positions;
+  k.k_new = a.k_new;
+  k.v_new = a.v_new;
+  k.new_bf16 = a.new_bf16;
+  k.new_stride_seq = a.new_stride_seq;
+  k.new_stride_head = a.new_stride_head;
   const dim3 grid1((unsigned)geo.n_chunks, (unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)a.batch);
-  hipLaunchKernelGGL(decode_split_kernel, grid1, dim3(kThreads), 0, stream, k);
+  if (a.positions)
+    hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, grid1, dim3(kThreads), 0, stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
@@ -790,6 +846,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.rot = a.rot;
   c.rot_stride_b = a.rot_stride_batch;
   c.seq_lens = a.seq_lens;
+  c.positions = a.positions;
   c.Hq = a.n_q_heads;
   c.G = G;
   c.cap = a.cache_cap;

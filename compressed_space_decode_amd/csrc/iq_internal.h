@@ -45,6 +45,14 @@ struct DecodeLaunch {
   float sm_scale;
   float* out;
   void* workspace;
+  // Fused append (iq_decode_attention_append): when positions is not NULL, sequence b's new
+  // K/V vectors are quantised into the cache at positions[b] and the lengths are positions + 1
+  // (seq_lens is then unused).
+  const int32_t* positions;
+  const void* k_new;
+  const void* v_new;
+  int new_bf16;
+  int64_t new_stride_seq, new_stride_head;   // elements
 };
 
 // Split-K geometry shared by the workspace query and the launch.

@@ -28,6 +28,9 @@ SIGNATURES = {
     "iq_decode_workspace_bytes": (_I64, [_I32, _I32, _I32, _I64]),
     "iq_decode_attention": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                            _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
+    "iq_decode_attention_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
+                                                  _I64, _I32, _I32, _I32, _I64, _F, _P, _P, _I64, _I32, _I32,
+                                                  _P]),
 }
 
 
@@ -166,5 +169,47 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         HEAD_DIM, BITS, _stream(q))
+    _check(rc)
+    return out
+
+
+def decode_attention_append(q, k_new, v_new, positions, k_codes, k_scales, v_codes, v_scales, rot, sm_scale=0.0,
+                            out=None, workspace=None, shared_rot=False):
+    """One decode step with the new token appended in the same launch: k_new / v_new
+    [B][Hkv][128] (cuda f32/bf16, last dim contiguous) are quantised into the cache at
+    positions[b] (int32 [B] on the device; outside [0, cap) skips the sequence) and
+    attention covers tokens 0..positions[b].  Other arguments as decode_attention.
+    Returns out float32 [B][Hq][128]."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    if d != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B][Hq][128]")
+    for t in (k_new, v_new):
+        if tuple(t.shape) != (B, Hkv, HEAD_DIM) or t.stride(2) != 1:
+            raise ValueError("k_new / v_new must be [B][Hkv][128] with contiguous coordinates")
+    if k_new.stride() != v_new.stride() or k_new.dtype != v_new.dtype:
+        raise ValueError("k_new and v_new must share strides and dtype")
+    for t in (k_codes, k_scales, v_codes, v_scales, rot):
+        if not t.is_contiguous():
+            raise ValueError("cache and rotation tensors must be contiguous")
+    for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
+        if tuple(c.shape) != (B, Hkv, cap, RECORD_BYTES) or tuple(sc.shape) != (B, Hkv, cap):
+            raise ValueError("caches must be [B][Hkv][cap][48] codes and [B][Hkv][cap] scales")
+    if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
+        raise ValueError("rot has the wrong number of values")
+    if positions.numel() != B or positions.dtype != torch.int32 or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous int32 tensor with one entry per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, Hq, Hkv, cap)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    rc = lib().iq_decode_attention_append(
+        q.data_ptr(), _dtype_code(q), k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new),
+        k_new.stride(0), k_new.stride(1), positions.data_ptr(),
+        k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(), v_scales.data_ptr(), rot.data_ptr(),
+        0 if shared_rot else Hkv * ROT_PARAMS, B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), HEAD_DIM, BITS, _stream(q))
     _check(rc)
     return out

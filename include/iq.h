@@ -164,6 +164,42 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
                         void* workspace, int64_t workspace_bytes,
                         int32_t head_dim, int32_t bits, void* stream);
 
+/*
+ * iq_decode_attention_append -- one decode step with the step's new token
+ * appended in the same launch.  Source: Abstract (quantised KV written as
+ * packed 3-bit tensors, attention computed on them).  For every sequence b
+ * and KV head g, the new key and value vectors k_new[b][g], v_new[b][g] are
+ * rotated, quantised and written into the cache at token positions[b]
+ * (exactly as iq_quantize_kv would), and attention then covers tokens
+ * 0 .. positions[b], the new one included.  The result equals
+ * iq_quantize_kv of that token followed by iq_decode_attention with
+ * seq_lens = positions + 1.
+ *   k_new, v_new   [batch][n_kv_heads][128], new_dtype IQ_F32 or IQ_BF16,
+ *                  element strides new_stride_seq and new_stride_head (the
+ *                  128 coordinates contiguous), 16-byte aligned with strides
+ *                  a multiple of 16 bytes.
+ *   positions      device int32[batch], ragged: each sequence has its own.
+ *                  A position outside [0, cache_cap) skips the sequence:
+ *                  nothing is written and its output rows are zeros.
+ *   k_codes ...    the cache (written at the new positions, read below them).
+ *   other arguments as in iq_decode_attention; the workspace size is the
+ *   same (iq_decode_workspace_bytes).
+ * Errors: as iq_decode_attention, plus IQ_EINVAL for NULL k_new / v_new /
+ * positions, negative or misaligned strides; IQ_EUNSUPPORTED for an
+ * unknown new_dtype.
+ */
+int iq_decode_attention_append(const void* q, int32_t q_dtype,
+                               const void* k_new, const void* v_new, int32_t new_dtype,
+                               int64_t new_stride_seq, int64_t new_stride_head,
+                               const int32_t* positions,
+                               uint8_t* k_codes, float* k_scales,
+                               uint8_t* v_codes, float* v_scales,
+                               const float* rot, int64_t rot_stride_batch,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int64_t cache_cap, float sm_scale, float* out,
+                               void* workspace, int64_t workspace_bytes,
+                               int32_t head_dim, int32_t bits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

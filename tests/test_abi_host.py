@@ -25,7 +25,8 @@ def _declared():
 
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
-                                  "iq_decode_workspace_bytes", "iq_decode_attention"])
+                                  "iq_decode_workspace_bytes", "iq_decode_attention",
+                                  "iq_decode_attention_append"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -114,6 +115,37 @@ def _dec(**kw):
 def test_decode_validation(kw, code):
     assert _dec(**kw) == code
     assert binding.last_error().startswith("iq_decode_attention")
+
+
+def _app(**kw):
+    args = dict(q=FAKE, qd=1, kn=FAKE, vn=FAKE, nd=1, nss=256, nsh=128, pos=FAKE, kc=FAKE, ks=FAKE, vc=FAKE,
+                vs=FAKE, rot=FAKE, rs=0, B=1, Hq=8, Hkv=2, cap=1000, sm=0.0, out=FAKE, ws=FAKE, wsb=16,
+                hd=128, bits=3)
+    args.update(kw)
+    return iq.lib().iq_decode_attention_append(
+        args["q"], args["qd"], args["kn"], args["vn"], args["nd"], args["nss"], args["nsh"], args["pos"],
+        args["kc"], args["ks"], args["vc"], args["vs"], args["rot"], args["rs"], args["B"], args["Hq"], args["Hkv"],
+        args["cap"], args["sm"], args["out"], args["ws"], args["wsb"], args["hd"], args["bits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), binding.IQ_EWORKSPACE),             # everything valid but the 16-byte workspace
+    (dict(hd=64), binding.IQ_EUNSUPPORTED),
+    (dict(nd=7), binding.IQ_EUNSUPPORTED),
+    (dict(qd=7), binding.IQ_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), binding.IQ_EINVAL),
+    (dict(kn=None), binding.IQ_EINVAL),
+    (dict(vn=None), binding.IQ_EINVAL),
+    (dict(pos=None), binding.IQ_EINVAL),
+    (dict(kn=FAKE + 8), binding.IQ_EINVAL),      # new vectors must be 16-byte aligned
+    (dict(nsh=4), binding.IQ_EINVAL),            # 8 bytes of bf16: not a multiple of 16 bytes
+    (dict(nss=-8), binding.IQ_EINVAL),
+    (dict(pos=FAKE + 2), binding.IQ_EINVAL),
+    (dict(cap=83886017), binding.IQ_EINVAL),
+])
+def test_decode_append_validation(kw, code):
+    assert _app(**kw) == code
+    assert binding.last_error().startswith("iq_decode_attention_append")
 
 
 def test_workspace_bytes():
