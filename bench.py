@@ -2,25 +2,25 @@
 
 One step is one decode step of a 48-layer model whose every layer has the
 long-context shape (batch 1, 32 query heads, 4 KV heads, head_dim 128, 32768
-cached tokens, bf16 K/V/Q drawn as in the long32k workload): the new token's
-K and V of all layers are rotated, quantized and packed into the caches
-(iq_quantize_kv, one call), then attention of all layers runs on the packed
-caches (iq_decode_attention, one layer-stacked call: layers are passed as
-batch entries, each with its own rotation).  Inputs are resident in HBM
-before the timed region.
+cached tokens, bf16 K/V/Q drawn as in the long32k workload): one
+iq_decode_attention_append launch rotates, quantizes and packs the new token's
+K and V of every layer into the caches and runs attention of all layers on
+the packed caches (layers are passed as batch entries, each with its own
+rotation).  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is KV tokens/s: cached token positions
 attended per second, summed over layers, each position covering all 4 KV
-heads.  The roofline object is for the decode call (split-K kernel plus its
-small combine kernel), timed with HIP events on the stream it runs on; its
-algorithmic bytes are the packed K/V codes and scales read, 104 bytes per
-(token, KV head); `traffic` is the HBM bytes per call from the committed
-rocprofv3 counter runs (profiles/decode_traffic.json), reported only while the
-decode kernel source is the one those counters were taken on.  Extra fields
-report a single-layer decode call, the GQA 8K and ragged-batch decode shapes,
-and the bulk prefill quantization (48 layers x 4 KV heads x 32768 tokens, K
-and V Student-t(3), bf16) against the same roofline.  The default warm-up
-(800 untimed steps) lets the GPU clocks settle before timing.
+heads.  The roofline object is for that launch (the split-K kernel with the
+append, plus its small combine kernel), timed with HIP events on the stream
+it runs on; its algorithmic bytes are the packed K/V codes and scales read,
+104 bytes per (token, KV head), plus the new tokens read and written.
+`traffic` is the HBM bytes per launch from the committed rocprofv3 counter
+runs (profiles/decode_traffic.json), reported only while the decode kernel
+source is the one those counters were taken on.  Extra fields report the
+decode alone, the append then decode as two launches, a single-layer decode,
+the GQA 8K and ragged-batch decode shapes, and the bulk prefill quantization
+(48 layers x 4 KV heads x 32768 tokens, K and V Student-t(3), bf16).  The
+default warm-up (800 untimed steps) lets the GPU clocks settle before timing.
 """
 import argparse
 import hashlib
@@ -67,7 +67,7 @@ def parse():
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--decode-only", action="store_true",
-                    help="only the timed decode steps (for counter runs); prints the JSON line")
+                    help="only the timed steps (for counter runs); prints a short JSON line")
     return ap.parse_args()
 
 
@@ -140,17 +140,21 @@ def main():
     lens = torch.full((L,), T, dtype=torch.int32, device=dev)
     out = torch.empty((L, HQ, D), dtype=torch.float32, device=dev)
     ws = torch.empty(iq.decode_workspace_bytes(L, HQ, HKV, T), dtype=torch.uint8, device=dev)
-    k_new = k_all[:, :, T - 1:T]              # the step's new token: position T-1 of every layer
-    v_new = v_all[:, :, T - 1:T]
+    k_new = k_all[:, :, T - 1]                # the step's new token: position T-1 of every layer
+    v_new = v_all[:, :, T - 1]                # [L][Hkv][128] views
+    positions = torch.full((L,), T - 1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
 
+    def step():                               # one launch: append the new token, then attend
+        iq.decode_attention_append(q, k_new, v_new, positions, kc, ks, vc, vs, rot, out=out, workspace=ws)
+
     def append():
-        iq.quantize_kv(k_new, v_new, rot, kc, ks, vc, vs, tok_offset=T - 1)
+        iq.quantize_kv(k_new[:, :, None], v_new[:, :, None], rot, kc, ks, vc, vs, tok_offset=T - 1)
 
     def decode():
         iq.decode_attention(q, kc, ks, vc, vs, rot, seq_lens=lens, out=out, workspace=ws)
 
-    def step():
+    def two_calls():
         append()
         decode()
 
@@ -161,15 +165,17 @@ def main():
     t_step = time_calls(step, args.steps, stream)
     t_decode = time_calls(decode, args.steps, stream)
     t_append = time_calls(append, args.steps, stream)
-    log("step %.1f us (decode %.1f us, append %.1f us)" % (t_step * 1e6, t_decode * 1e6, t_append * 1e6))
+    t_two = time_calls(two_calls, args.steps, stream)
+    log("step %.1f us (decode alone %.1f us, append alone %.1f us, append then decode %.1f us)" %
+        (t_step * 1e6, t_decode * 1e6, t_append * 1e6, t_two * 1e6))
 
     decode_bytes = L * T * HKV * BYTES_PER_TOKEN_HEAD
-    decode_gbs = decode_bytes / t_decode / 1e9
+    step_bytes = decode_bytes + L * HKV * 2 * (2 * D + 48 + 4)   # + the new K/V: bf16 read, record written
+    step_gbs = step_bytes / t_step / 1e9
     tokens_per_step = L * T
 
     if args.decode_only:
-        print(json.dumps({"decode_us": t_decode * 1e6, "step_us": t_step * 1e6,
-                          "decode_GBs": decode_bytes / t_decode / 1e9}), flush=True)
+        print(json.dumps({"step_us": t_step * 1e6, "decode_us": t_decode * 1e6, "step_GBs": step_gbs}), flush=True)
         return
 
     # single-layer decode call (the one-layer shape, unadjusted)
@@ -292,16 +298,17 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "long32k decode step x%d layers (per layer: batch 1, 32 query / 4 KV heads, "
-                               "head_dim 128, 32768 cached tokens, bf16 inputs, 3-bit packed KV; append the new "
-                               "token's K/V, then layer-stacked decode attention)" % L,
+                               "head_dim 128, 32768 cached tokens, bf16 inputs, 3-bit packed KV; the new token's "
+                               "K/V appended and layer-stacked decode attention in one launch)" % L,
                    "layers": L, "batch": 1, "n_q_heads": HQ, "n_kv_heads": HKV, "context": T,
                    "head_dim": D, "kv_bits": 3},
-        "roofline": {"bound": "hbm", "achieved": decode_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": decode_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "kernel": "iq_decode_attention (decode_split_kernel + combine_kernel)",
-                     "algorithmic_bytes_per_launch": decode_bytes, "avg_launch_us": t_decode * 1e6},
-        "decode_ms": t_decode * 1e3,
-        "append_ms": t_append * 1e3,
+        "roofline": {"bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": step_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "kernel": "iq_decode_attention_append (decode_split_kernel with the append, combine_kernel)",
+                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": t_step * 1e6},
+        "decode_only": {"ms": t_decode * 1e3, "GBs": decode_bytes / t_decode / 1e9},
+        "append_then_decode_ms": t_two * 1e3,
+        "append_alone_ms": t_append * 1e3,
         "single_layer_decode": single,
         "other_decode_shapes": others,
         "prefill_quantize": prefill,
