@@ -672,23 +672,25 @@ struct CombineArgs {
   int64_t rot_stride_b;
   const int32_t* seq_lens;
   const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
-  int Hq, G;
+  int Hq, G, head_groups;
   int64_t cap;
   int chunk, n_chunks;
   float* out;
 };
 
+// Most chunks per row; bounds the combine's LDS.
 constexpr int kMaxChunks = 1024;
 
+// One work-group (2 waves) per (sequence, query head): log-sum-exp merge of the chunk partials with
+// one output coordinate per thread and independent loads, then o = R^T o' = H (blockdiag M_b^T) o'
+// by one wave (8 lanes, 16 coordinates each, as in the query set-up of the split kernel).
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   __shared__ float y[128];
   __shared__ float mats[32][16];
   __shared__ float wgt[kMaxChunks];
-  __shared__ float red[128];
-  const int bh = blockIdx.x;
-  const int b = bh / a.Hq, h = bh % a.Hq;
-  const int g = h / a.G;
-  const int d = threadIdx.x;
+  __shared__ float inv_l;
+  const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int64_t len = a.cap;
   if (a.positions) {
     const int64_t p = a.positions[b];
@@ -697,65 +699,79 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     const int64_t l = a.seq_lens[b];
     len = l < 0 ? 0 : (l > a.cap ? a.cap : l);
   }
-  float* outp = a.out + (int64_t)bh * 128;
-  if (len == 0) {
-    outp[d] = 0.f;
+  float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
+  if (len == 0) {                       // an empty sequence attends to nothing
+    outp[tid] = 0.f;
     return;
   }
   const int nvalid = (int)((len + a.chunk - 1) / a.chunk);
-  const float* ml = a.part_ml + (int64_t)bh * a.n_chunks * 2;
-  const float* po = a.part_o + (int64_t)bh * a.n_chunks * 128;
-  const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
-  if (d < 32) build_block(rot + d * 8, mats[d]);
-  float M = -INFINITY;
-  for (int c = d; c < nvalid; c += 128) M = fmaxf(M, ml[2 * c]);
-  red[d] = M;
-  __syncthreads();
-  for (int st = 64; st > 0; st >>= 1) {
-    if (d < st) red[d] = fmaxf(red[d], red[d + st]);
-    __syncthreads();
+  const float* ml = a.part_ml + ((int64_t)b * a.Hq + h) * a.n_chunks * 2;
+  if (wave == 0) {                      // weights 2^(m_c - M) and 1/L
+    float M = -INFINITY;
+    for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, wave_xor(M, m));
+    float L = 0.f;
+    for (int c = lane; c < nvalid; c += 64) {
+      const float e = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+      wgt[c] = e;
+      L = fmaf(e, ml[2 * c + 1], L);
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) L += wave_xor(L, m);
+    if (lane == 0) inv_l = 1.f / L;
+  } else if (lane < 32) {               // the SO(4) blocks of this head's KV head
+    build_block(a.rot + b * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
   }
-  M = red[0];
   __syncthreads();
-  float Lp = 0.f;
-  for (int c = d; c < nvalid; c += 128) {
-    const float f = __builtin_amdgcn_exp2f(ml[2 * c] - M);
-    wgt[c] = f;
-    Lp += f * ml[2 * c + 1];
+  {
+    const float* po = a.part_o + ((int64_t)b * a.Hq + h) * a.n_chunks * 128 + tid;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int c = 0;
+    for (; c + 8 <= nvalid; c += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(wgt[c + u], po[(int64_t)(c + u) * 128], acc[u]);
+    }
+    for (; c < nvalid; ++c) acc[0] = fmaf(wgt[c], po[(int64_t)c * 128], acc[0]);
+    y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
   }
-  red[d] = Lp;
   __syncthreads();
-  for (int st = 64; st > 0; st >>= 1) {
-    if (d < st) red[d] += red[d + st];
-    __syncthreads();
+  if (wave == 0) {
+    const int qe = lane & 7;            // 16-coordinate slice; lanes 8..63 repeat lanes 0..7
+    const float* yr = y + 16 * qe;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {       // transposed SO(4) blocks 4qe .. 4qe+3
+      const float* M4 = mats[4 * qe + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        x[4 * j + i] = M4[i] * yr[4 * j] + M4[4 + i] * yr[4 * j + 1] + M4[8 + i] * yr[4 * j + 2] +
+                       M4[12 + i] * yr[4 * j + 3];
+    }
+    const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i & m) == 0) {
+          const float u = x[i], v = x[i + m];
+          x[i] = u + v;
+          x[i + m] = u - v;
+        }
+    if (lane < 8) {
+      float4* op = reinterpret_cast<float4*>(outp + 16 * qe);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        op[i] = make_float4(x[4 * i] * kInvSqrtD, x[4 * i + 1] * kInvSqrtD, x[4 * i + 2] * kInvSqrtD,
+                            x[4 * i + 3] * kInvSqrtD);
+    }
   }
-  const float L = red[0];
-  float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-  int c = 0;
-  for (; c + 4 <= nvalid; c += 4) {
-    acc0 += wgt[c] * po[(int64_t)c * 128 + d];
-    acc1 += wgt[c + 1] * po[(int64_t)(c + 1) * 128 + d];
-    acc2 += wgt[c + 2] * po[(int64_t)(c + 2) * 128 + d];
-    acc3 += wgt[c + 3] * po[(int64_t)(c + 3) * 128 + d];
-  }
-  for (; c < nvalid; ++c) acc0 += wgt[c] * po[(int64_t)c * 128 + d];
-  y[d] = ((acc0 + acc1) + (acc2 + acc3)) / L;
-  __syncthreads();
-  // Transposed blocks: z[4bb + i] = sum_k M_bb[k][i] o'[4bb + k].
-  const int bb = d >> 2, i = d & 3;
-  const float* M4 = mats[bb];
-  const float zi = M4[i] * y[4 * bb] + M4[4 + i] * y[4 * bb + 1] + M4[8 + i] * y[4 * bb + 2] +
-                   M4[12 + i] * y[4 * bb + 3];
-  __syncthreads();
-  y[d] = zi;
-  __syncthreads();
-  for (int m = 1; m < 128; m <<= 1) {
-    const float self = y[d], other = y[d ^ m];
-    __syncthreads();
-    y[d] = (d & m) ? (other - self) : (self + other);
-    __syncthreads();
-  }
-  outp[d] = y[d] * kInvSqrtD;
 }
 
 }  // namespace
@@ -789,9 +805,10 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   const int64_t slots = kGroupsPerCU * (int64_t)device_cu_count();
   const int64_t per_unit = units >= slots ? 1 : slots / units;
   int64_t chunk = (cache_cap + per_unit - 1) / per_unit;
+  const int64_t min_chunk = (cache_cap + kMaxChunks - 1) / kMaxChunks;
+  if (chunk < min_chunk) chunk = min_chunk;
   chunk = (chunk + 127) / 128 * 128;
   if (chunk < 256) chunk = 256;
-  while ((cache_cap + chunk - 1) / chunk > kMaxChunks) chunk += 128;
   geo.chunk = (int)chunk;
   geo.n_chunks = (int)((cache_cap + chunk - 1) / chunk);
   const int64_t parts = (int64_t)batch * n_q_heads * geo.n_chunks;
@@ -849,6 +866,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.positions = a.positions;
   c.Hq = a.n_q_heads;
   c.G = G;
+  c.head_groups = geo.head_groups;
   c.cap = a.cache_cap;
   c.chunk = geo.chunk;
   c.n_chunks = geo.n_chunks;
