@@ -279,6 +279,7 @@ struct VSelectors {
 // Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
 // t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
 // past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
+template <bool kRefill>
 __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], float c1,
@@ -308,8 +309,10 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   // ---- the codes are in registers now: refill the buffer.  The scheduling barrier keeps the
   //      loads behind the last reads of the old contents, so they land in the same registers
   //      (no copies, and no waits for them, at the loop back-edge). ----
-  __builtin_amdgcn_sched_barrier(0);
-  load_block(cur, cb, t_refill, tok_end, lo);
+  if (kRefill) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_block(cur, cb, t_refill, tok_end, lo);
+  }
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
   float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
@@ -596,20 +599,21 @@ void decode_split_kernel(DecodeKArgs a) {
   BlockData buf, buf2, buf3;
   load_block(buf, cb, t0, tok_end, lo);
   load_block(buf2, cb, t0 + step, tok_end, lo);
-  load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
-  // Three buffers in turn, each refilled three blocks ahead: while block i is processed, blocks
-  // i+1 and i+2 are in flight and block i+3's loads are issued once block i is unpacked.
+  // Three buffers: the first two are refilled three blocks ahead once their codes are unpacked;
+  // the third is loaded at the top of each round of three blocks.  So the buffers carried around
+  // the loop were refilled one or two blocks before its back-edge, never just before it.
   while (t0 < tok_end) {            // uniform
-    process_block(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
-                  lane, n, g4, vsel, pwr, prd);
+    load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
+    process_block<true>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+                        ws, lane, n, g4, vsel, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
-                  lane, n, g4, vsel, pwr, prd);
+    process_block<true>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+                        ws, lane, n, g4, vsel, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block(buf3, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws,
-                  lane, n, g4, vsel, pwr, prd);
+    process_block<false>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
+                         n, g4, vsel, pwr, prd);
     t0 += step;
   }
 
