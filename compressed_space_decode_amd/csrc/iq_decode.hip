@@ -248,9 +248,12 @@ __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb,
 struct WaveState {
   floatx4 O[8];           // O[j][(head, part)][n]: coordinate 8n + j, rows 4*g4 + r = (head 2*g4 + r/2, part r%2)
   float m_run[2];         // running max (log2 units), uniform over the 16 lanes of a row group
+  float thr[2];           // m_run + kHeadroom: a score above it moves the running max
   float l_run[2];         // sum of p over this lane's tokens
   float ls_run[2];        // sum of P'' over this lane's tokens
   int vexp;               // vlim = 2^vexp is above every V scale seen; -200: none yet
+  float vlim;             // 2^vexp (0 before the first block)
+  float pmul;             // kPScale / vlim
 };
 
 __device__ __forceinline__ float row_max(float x) {   // max over the 16 lanes of a row (DPP row_ror)
@@ -328,19 +331,20 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   }
   // Lazy rescaling: the running max only moves when a score exceeds it by more than kHeadroom
   // (so p <= 2^kHeadroom), or when a V scale reaches the running power-of-two bound.
-  const float vlim = ldexpf(1.f, st.vexp);
-  const bool vgrow_l = (sv0 >= vlim) || (sv1 >= vlim);
-  const bool grow_l = (z[0][0] > st.m_run[0] + kHeadroom) || (z[0][1] > st.m_run[0] + kHeadroom) ||
-                      (z[1][0] > st.m_run[1] + kHeadroom) || (z[1][1] > st.m_run[1] + kHeadroom);
-  if (__any(grow_l || vgrow_l)) {
-    const float vmax = row_max(fmaxf(sv0, sv1));              // same in every row: wave-uniform
+  const float svmax = fmaxf(sv0, sv1);
+  const bool grow_l = (fmaxf(z[0][0], z[0][1]) > st.thr[0]) | (fmaxf(z[1][0], z[1][1]) > st.thr[1]) |
+                      (svmax >= st.vlim);
+  if (__any(grow_l)) {
+    const float vmax = row_max(svmax);                         // same in every row: wave-uniform
     float ratio = 1.f;
-    if (vmax >= vlim) {
+    if (vmax >= st.vlim) {
       int ex;
       frexpf(vmax, &ex);                                       // vmax < 2^ex
       ex = ex < -60 ? -60 : ex;
       ratio = st.vexp == -200 ? 0.f : ldexpf(1.f, st.vexp - ex);
       st.vexp = ex;
+      st.vlim = ldexpf(1.f, ex);
+      st.pmul = ldexpf(kPScale, -ex);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -349,6 +353,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
       st.l_run[j] *= alpha;
       st.ls_run[j] *= alpha * ratio;
       st.m_run[j] = m_new;
+      st.thr[j] = m_new + kHeadroom;
       const float f = alpha * ratio;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
@@ -358,8 +363,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
     }
   }
   // ---- probabilities; P'' = p s_V 16 / vlim split hi/lo into the P staging rows ----
-  const float pmul = ldexpf(kPScale, -st.vexp);
-  const float svm[2] = {sv0 * pmul, sv1 * pmul};
+  const float svm[2] = {sv0 * st.pmul, sv1 * st.pmul};
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     _Float16 h4[4];
@@ -590,9 +594,12 @@ void decode_split_kernel(DecodeKArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) st.O[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
   st.m_run[0] = st.m_run[1] = -INFINITY;
+  st.thr[0] = st.thr[1] = -INFINITY;
   st.l_run[0] = st.l_run[1] = 0.f;
   st.ls_run[0] = st.ls_run[1] = 0.f;
   st.vexp = -200;
+  st.vlim = 0.f;                     // the first block always rescales
+  st.pmul = 0.f;
 
   // The first three blocks' loads are issued after the set-up: the set-up's own loads and waits
   // sit in a branch, and issuing these behind it keeps the count of loads in flight exact.
