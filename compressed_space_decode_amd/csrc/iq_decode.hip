@@ -32,9 +32,11 @@
 //     by more than 8 (log2 units), so p <= 256; P'' = p * s_V * 16 / vlim
 //     (vlim a running power of two above every V scale seen) is split hi/lo
 //     in fp16 and transposed through LDS into the A operand of the PV product;
-//   * V: lane (n, g4) loads group n (3 bytes) of 8 tokens, which is exactly
-//     the B operand column n of O[head, part][coordinate 8n + j] += P'' x V for
-//     the 8 tiles j: V never passes through LDS;
+//   * V: lanes load 12-byte quarters like K (16 tokens x 4 quarters per load,
+//     768 contiguous bytes), chosen so that a 4x4 transpose inside each quad of
+//     lanes (two DPP exchange rounds) leaves lane (n, g4) with group n of its 8
+//     tokens: exactly the B operand column n of O[head, part][coordinate 8n + j]
+//     += P'' x V for the 8 tiles j.  V never passes through LDS;
 //   * the 4 waves merge in LDS and write one (max, sum, o') partial.
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
@@ -188,14 +190,14 @@ __device__ __forceinline__ constexpr int pv_token(int g4, int e) { return e < 4 
 
 struct BlockData {
   unsigned kw[2][3];      // K quarter g4 of tokens n and 16 + n
-  unsigned vw[8];         // V group n of token pv_token(g4, e)
+  unsigned vw[2][3];      // V quarter (lane >> 2) & 3 of tokens 16t + 4 g4 + (lane & 3), t = 0, 1
   unsigned ksc, vsc;      // K and V scale bits of token n (row groups 0, 2) or 16 + n (1, 3)
 };
 
 // Per-lane constant byte offsets within a 32-token block.
 struct LaneOffsets {
   unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is +768)
-  unsigned vcode;         // byte offset of this lane's V group in token pv_token(g4, 0)
+  unsigned vcode;         // byte offset of this lane's V quarter (token 4 g4 + (lane & 3); +768 for t = 1)
   unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
 };
 
@@ -234,9 +236,11 @@ __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb,
     const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, ko + 768 * tt, 0, 0);
     d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
   }
-  // V: 4-byte loads at byte offset 3n of a record (unaligned); lane 15 loads bytes 44..47.
 #pragma unroll
-  for (int e = 0; e < 8; ++e) d.vw[e] = __builtin_amdgcn_raw_buffer_load_b32(cb.vc, vo + 48 * pv_token(0, e), 0, 0);
+  for (int tt = 0; tt < 2; ++tt) {
+    const u3v vq = __builtin_amdgcn_raw_buffer_load_b96(cb.vc, vo + 768 * tt, 0, 0);
+    d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
+  }
   // Both scale loads run in every lane (keeps the resources uniform); the block's consumer picks
   // one, so nothing here waits for the loads.
   const unsigned so = lo.scale + (in ? (unsigned)t0 * 4u : kNoBlock);
@@ -273,11 +277,29 @@ __device__ __forceinline__ float row_sum(float x) {   // sum over the 16 lanes o
 
 typedef __attribute__((address_space(3))) short4v* lds_s4;
 
-// Byte selectors that pair the V group of two tokens into 16-bit windows 0, 1 and 2 (bytes 0-1,
-// 1-2, 2-3 of the group); lane 15's group sits one byte higher in its loaded word.
-struct VSelectors {
-  unsigned w[3];
-};
+// 4x4 transpose of words inside each quad of lanes: lane x (= lane & 3) ends with g[c] equal to
+// the g[x] that lane c of its quad held (two exchange rounds: partners x ^ 1, then x ^ 2).
+__device__ __forceinline__ unsigned dpp_xor1_u(unsigned x) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ unsigned dpp_xor2_u(unsigned x) {
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
+}
+__device__ __forceinline__ void quad_transpose(unsigned g[4], int lane) {
+  const bool odd = lane & 1, upper = lane & 2;
+  unsigned r0 = dpp_xor1_u(odd ? g[0] : g[1]), r1 = dpp_xor1_u(odd ? g[2] : g[3]);
+  g[0] = odd ? r0 : g[0];
+  g[1] = odd ? g[1] : r0;
+  g[2] = odd ? r1 : g[2];
+  g[3] = odd ? g[3] : r1;
+  r0 = dpp_xor2_u(upper ? g[0] : g[2]);
+  r1 = dpp_xor2_u(upper ? g[1] : g[3]);
+  g[0] = upper ? r0 : g[0];
+  g[1] = upper ? r1 : g[1];
+  g[2] = upper ? g[2] : r0;
+  g[3] = upper ? g[3] : r1;
+}
+
 
 // Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
 // t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
@@ -287,7 +309,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], float c1,
                                               const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
-                                              const VSelectors& vsel, unsigned pwr, unsigned prd) {
+                                              unsigned pwr, unsigned prd) {
   ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
@@ -303,12 +325,26 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
                                                   acc, 0, 0, 0);
     S[tt] = acc;
   }
-  // ---- V: the three byte windows of each token pair (tokens pv_token(g4, 2i), (g4, 2i+1)) ----
+  // ---- V: each lane holds quarter y = (lane >> 2) & 3 (groups 4y..4y+3) of the tokens
+  //      16t + 4 g4 + x, x = lane & 3; a 4x4 transpose inside each quad of lanes leaves lane x with
+  //      group 4y + x = n of the quad's four tokens, in token order: B operand column n in the
+  //      token order of the PV product.  Then the three byte windows of each token pair. ----
   unsigned vwin[4][3];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int tt = 0; tt < 2; ++tt) {
+    unsigned gq[4];                                                  // group k in bytes 0..2
+    gq[0] = cur.vw[tt][0];
+    gq[1] = __builtin_amdgcn_alignbyte(cur.vw[tt][1], cur.vw[tt][0], 3);
+    gq[2] = __builtin_amdgcn_alignbyte(cur.vw[tt][2], cur.vw[tt][1], 2);
+    gq[3] = cur.vw[tt][2] >> 8;
+    quad_transpose(gq, lane);
 #pragma unroll
-    for (int w = 0; w < 3; ++w) vwin[i][w] = __builtin_amdgcn_perm(cur.vw[2 * i + 1], cur.vw[2 * i], vsel.w[w]);
+    for (int p = 0; p < 2; ++p) {                                    // tokens 2p and 2p + 1 of the quad
+      vwin[2 * tt + p][0] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x05040100u);   // bytes 0-1
+      vwin[2 * tt + p][1] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x06050201u);   // bytes 1-2
+      vwin[2 * tt + p][2] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x07060302u);   // bytes 2-3
+    }
+  }
   // ---- the codes are in registers now: refill the buffer.  The scheduling barrier keeps the
   //      loads behind the last reads of the old contents, so they land in the same registers
   //      (no copies, and no waits for them, at the loop back-edge). ----
@@ -435,15 +471,9 @@ void decode_split_kernel(DecodeKArgs a) {
   const int g4 = lane >> 4;         // row group: quarter of the K record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
   lo.kcode = (unsigned)(n * 48 + 12 * g4);
-  lo.vcode = (unsigned)(48 * pv_token(g4, 0) + (n == 15 ? 44 : 3 * n));
+  lo.vcode = (unsigned)(48 * (4 * g4 + (lane & 3)) + 12 * ((lane >> 2) & 3));
   lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
   const bool vscale = g4 >= 2;
-  VSelectors vsel;
-  if (n == 15) {
-    vsel.w[0] = 0x06050201u; vsel.w[1] = 0x07060302u; vsel.w[2] = 0x07070303u;
-  } else {
-    vsel.w[0] = 0x05040100u; vsel.w[1] = 0x06050201u; vsel.w[2] = 0x07060302u;
-  }
 
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
@@ -612,15 +642,15 @@ void decode_split_kernel(DecodeKArgs a) {
   while (t0 < tok_end) {            // uniform
     load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
     process_block<true>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, vsel, pwr, prd);
+                        ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<true>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, vsel, pwr, prd);
+                        ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<false>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
-                         n, g4, vsel, pwr, prd);
+                         n, g4, pwr, prd);
     t0 += step;
   }
 
