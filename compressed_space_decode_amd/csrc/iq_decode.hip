@@ -10,19 +10,23 @@
 // Record layout: one little-endian bit stream, code i at bits 3i..3i+2, so
 // bytes 3g..3g+2 hold the codes of coordinates 8g..8g+7 (group g).
 //
-// Kernel 1 (decode_split_kernel): one work-group of 4 waves per (sequence,
-// KV head, group of up to 8 query heads, chunk of tokens).  Each wave works
-// on its own, with no work-group barrier until the final merge:
+// Kernel 1 (decode_split_kernel): one work-group of 4 waves per (KV head,
+// group of up to 8 query heads, (sequence, chunk of tokens) pair).  The chunk
+// size is chosen on the device from the sequence lengths so that one round of
+// work-groups covers the whole batch, ragged or not (plan_chunks).  Each wave
+// works on its own, with no work-group barrier until the final merge:
 //   * set-up (wave 0, shared through LDS): the group's queries are rotated in
 //     registers (8 lanes per head, 16 coordinates per lane: cross-lane
 //     Hadamard stages through DPP / swizzle, in-lane stages, then the 4x4
 //     SO(4) blocks) and laid out as the fp16 A operand of the QK product, hi
 //     and lo parts (q = hi + lo) in rows 2h and 2h+1, so the product carries
 //     ~22 bits;
-//   * loop over 32-token blocks; the loads of block i+1 are issued as soon as
-//     block i's codes are unpacked, and overlap the rest of block i;
-//   * codes become fp16 operands with one byte permute per three fields and
-//     one AND per pair of codes: a field at bit p of a 16-bit half is the fp16
+//   * with the fused append, wave 1 of the work-group whose chunk holds the
+//     new token rotates, quantises and stores its K and V records first;
+//   * loop over 32-token blocks with three blocks in flight: a buffer is
+//     refilled three blocks ahead as soon as its codes are unpacked;
+//   * codes become fp16 operands with byte permutes that pick 32-bit windows
+//     and one AND per pair of codes: a field at bit p of a 16-bit half is the fp16
 //     subnormal c * 2^(p-24) (p <= 7), multiplied exactly by the matrix cores;
 //     the 2^-p is folded into the other operand or undone at the end;
 //   * K: a lane loads one 12-byte quarter (4 groups) of one token, the B
@@ -62,6 +66,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running max before a rescale
 constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
+constexpr int kMaxChunks = 1024;    // most chunks of one sequence (the combine's LDS weights)
 
 // Field j (0..7) of a 24-bit group is taken from byte window j / 3 (bytes 0-1, 1-2 or 2-3 of the
 // group) at bit position field_pos(j) <= 7 of each 16-bit half.
@@ -118,12 +123,14 @@ struct DecodeKArgs {
   const float* rot;
   int64_t rot_stride_b;
   const int32_t* seq_lens;
-  int Hq, Hkv, G, head_groups;
+  int batch, Hq, Hkv, G, head_groups;
   int64_t cap;
-  int chunk, n_chunks;
+  int target;             // most (sequence, chunk) pairs per (KV head, head group) column
   float sm_log2;          // softmax scale times log2(e)
-  float* part_o;          // [B][Hq][n_chunks][128]
-  float* part_ml;         // [B][Hq][n_chunks][2]  (max in log2 units, sum)
+  int* plan;              // [0]: chunk size; [64 + b]: index of sequence b's first chunk
+  int x_max;              // grid width: work items per column
+  float* part_o;          // [Hq][x_max][128], x = index of the (sequence, chunk) pair
+  float* part_ml;         // [Hq][x_max][2]  (max in log2 units, sum)
   // fused append (positions != NULL): new token of sequence b written at positions[b]
   const int32_t* positions;
   const void* k_new;
@@ -131,6 +138,164 @@ struct DecodeKArgs {
   int new_bf16;
   int64_t new_stride_seq, new_stride_head;
 };
+
+// ---------------- split of the context into chunks ----------------
+// The sequences' lengths decide the chunk size, so that ragged batches fill the GPU as evenly as
+// full ones: every work-group computes the same plan from the lengths (no extra launch, no host
+// round trip).  Chunks are multiples of 128 tokens (one step of the 4 waves), at least 256.
+struct LenSource {
+  const int32_t* positions;   // fused append: length = position + 1 (0 outside the cache)
+  const int32_t* seq_lens;    // else the given lengths clamped to [0, cap]; NULL: every length cap
+  int cap, batch;
+};
+
+__device__ __forceinline__ int len_at(const LenSource& s, int i) {
+  if (i >= s.batch) return 0;
+  if (s.positions) {
+    const int p = s.positions[i];
+    return (p >= 0 && p < s.cap) ? p + 1 : 0;
+  }
+  if (s.seq_lens) {
+    const int l = s.seq_lens[i];
+    return l < 0 ? 0 : (l > s.cap ? s.cap : l);
+  }
+  return s.cap;
+}
+
+__device__ __forceinline__ long long chunk_round(long long v) {   // up to a multiple of 128, >= 256
+  v = (v + 127) / 128 * 128;
+  return v < 256 ? 256 : v;
+}
+
+// Inclusive prefix sum over the 64 lanes: row shifts 1, 2, 4, 8 scan each row of 16 lanes, then
+// row_bcast:15 adds row 0's total into rows 1 and 3 and row_bcast:31 adds rows 0-1 into rows 2-3.
+// Lanes without a source take the `old` operand, 0.
+__device__ __forceinline__ int wave_scan_add(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31, rows 2 and 3
+  return x;
+}
+// Running maximum of non-negative values in the same pattern; lane 63 holds the wave's maximum.
+__device__ __forceinline__ int wave_scan_max(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false));
+  x = max(x, __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false));
+  return x;
+}
+__device__ __forceinline__ int lane63(int x) { return __builtin_amdgcn_readlane(x, 63); }
+
+// Sum over sequences of ceil(len / c).  `l0` is this lane's length of sequences 0..63.
+__device__ __forceinline__ long long count_chunks(const LenSource& s, int l0, int c, int lane) {
+  long long n = 0;
+  for (int base = 0; base < s.batch; base += 64) {
+    const int l = base == 0 ? l0 : len_at(s, base + lane);
+    n += lane63(wave_scan_add((l + c - 1) / c));
+  }
+  return n;
+}
+
+struct ChunkPlan {
+  int chunk;    // tokens per chunk
+  int b;        // sequence of work item x (-1: x is past the last chunk)
+  int j;        // chunk of that sequence
+  int len;      // its length
+};
+
+// Work item x of a plan with chunk size c: chunk x - first(b) of the sequence b with
+// first(b) <= x < first(b + 1), chunks numbered sequence by sequence.  `incl` is the inclusive scan
+// of this lane's chunk count n over the 64 sequences base..base+63 (plus the earlier ones).
+__device__ __forceinline__ bool locate(ChunkPlan& p, int base, int batch, int x, int incl, int n, int l) {
+  const unsigned long long mask = __ballot(incl > x);
+  if (!mask) return false;
+  const int f = __builtin_ctzll(mask);
+  if (base + f < batch) {
+    p.b = base + f;
+    p.j = x - __builtin_amdgcn_readlane(incl - n, f);
+    p.len = __builtin_amdgcn_readlane(l, f);
+  }
+  return true;
+}
+
+// The smallest chunk size c (within the rounding above) whose number of chunks, summed over the
+// sequences, is at most `target`, so one round of work-groups covers the batch; then the
+// sequence and chunk of work item x.  Wave-uniform; every wave of the work-group computes it.
+// Bounds used: sum ceil(l / c) <= 128 units / c + nz (units = sum ceil(l / 128), nz = sequences
+// with tokens), so c >= 128 units / (target - nz) meets the target when target > nz; otherwise
+// one chunk per sequence.
+__device__ ChunkPlan plan_chunks(const LenSource& s, int target, int x, int lane) {
+  const int l0 = len_at(s, lane);
+  ChunkPlan p{256, -1, -1, 0};
+  if (s.batch <= 64) {                 // one sequence per lane; 32-bit (units <= 64 * 2^20)
+    const int units = lane63(wave_scan_add((l0 + 127) >> 7));
+    const int nz = __builtin_popcountll(__ballot(l0 > 0));
+    const int cmax = (int)chunk_round(lane63(wave_scan_max(l0)));
+    const int q = (int)(((unsigned)units + target - 1) / (unsigned)target);
+    int c = q >= (cmax >> 7) ? cmax : (int)chunk_round((long long)q * 128);
+    int n = (l0 + c - 1) / c;
+    int incl = wave_scan_add(n);
+    if (lane63(incl) > target) {       // too many chunks: search between the bounds
+      if (target > nz) {
+        int lo = c;
+        const unsigned qh = ((unsigned)units + (target - nz) - 1) / (unsigned)(target - nz);
+        int hi = qh >= (unsigned)(cmax >> 7) ? cmax : (int)chunk_round((long long)qh * 128);
+        while (hi - lo > 128) {
+          const int mid = lo + (hi - lo) / 256 * 128;
+          if (lane63(wave_scan_add((l0 + mid - 1) / mid)) <= target) hi = mid; else lo = mid;
+        }
+        c = hi;
+      } else {
+        c = cmax;
+      }
+      n = (l0 + c - 1) / c;
+      incl = wave_scan_add(n);
+    }
+    p.chunk = c;
+    locate(p, 0, s.batch, x, incl, n, l0);
+    return p;
+  }
+  // any batch size: 64 sequences per pass, 64-bit sums
+  long long units = 0;
+  int nz = 0, maxl = 0;
+  for (int base = 0; base < s.batch; base += 64) {
+    const int l = base == 0 ? l0 : len_at(s, base + lane);
+    units += lane63(wave_scan_add((l + 127) >> 7));
+    nz += __builtin_popcountll(__ballot(l > 0));
+    maxl = max(maxl, lane63(wave_scan_max(l)));
+  }
+  const long long cmax = chunk_round(maxl);
+  long long c = chunk_round((units + target - 1) / target * 128);
+  if (c < cmax && count_chunks(s, l0, (int)c, lane) > target) {
+    if (target > nz) {
+      long long lo = c, hi = chunk_round((units + (target - nz) - 1) / (target - nz) * 128);
+      if (hi > cmax) hi = cmax;
+      while (hi - lo > 128) {
+        const long long mid = lo + (hi - lo) / 256 * 128;
+        if (count_chunks(s, l0, (int)mid, lane) <= target) hi = mid; else lo = mid;
+      }
+      c = hi;
+    } else {
+      c = cmax;
+    }
+  }
+  if (c > cmax) c = cmax;
+  p.chunk = (int)c;
+  int offset = 0;
+  for (int base = 0; base < s.batch; base += 64) {
+    const int l = base == 0 ? l0 : len_at(s, base + lane);
+    const int n = (l + p.chunk - 1) / p.chunk;
+    const int incl = wave_scan_add(n) + offset;
+    if (locate(p, base, s.batch, x, incl, n, l)) return p;
+    offset = lane63(incl);
+  }
+  return p;
+}
 
 struct MergeSmem {
   float o[kWaves][8][128];
@@ -433,10 +598,9 @@ template <bool kAppend>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
-  const int chunk_id = blockIdx.x;
+  const int x = blockIdx.x;          // (sequence, chunk) pair
   const int g = blockIdx.y / a.head_groups;
   const int hg = blockIdx.y % a.head_groups;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
@@ -444,19 +608,21 @@ void decode_split_kernel(DecodeKArgs a) {
   // Token indices are 32-bit and a sequence's codes fit one buffer resource (the capacity is
   // validated: cap * 48 < 0xF0000000): uniform token arithmetic stays on the scalar unit.
   const int cap = (int)a.cap;
-  int len = cap;
-  int pos = -1;                      // fused append: position of the new token (-1: none)
-  if (kAppend) {
-    const int p = a.positions[b];
-    pos = (p >= 0 && p < cap) ? p : -1;
-    len = pos + 1;                   // a position outside the cache skips the sequence
-  } else if (a.seq_lens) {
-    const int l = a.seq_lens[b];
-    len = l < 0 ? 0 : (l > cap ? cap : l);
+  const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch};
+  const ChunkPlan plan = plan_chunks(src, a.target, x, lane);
+  if (plan.b < 0) return;                                    // uniform: past the last chunk
+  const int b = plan.b;
+  const int len = plan.len;          // > 0
+  // the combine reads the plan from here
+  if (tid == 0 && blockIdx.y == 0) {
+    if (x == 0) a.plan[0] = plan.chunk;
+    if (plan.j == 0) a.plan[64 + b] = x;
   }
-  const int tok0 = chunk_id * a.chunk;
-  if (tok0 >= len) return;                                   // uniform
-  const int tok_end = (tok0 + a.chunk < len) ? tok0 + a.chunk : len;
+  // fused append: the new token sits at len - 1 (a position outside the cache gave length 0)
+  const int pos = kAppend ? len - 1 : -1;
+  const int tok0 = plan.j * plan.chunk;
+  if (tok0 >= len) return;                                   // uniform; never taken
+  const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
   const int h0 = g * a.G + hg * 8;
   const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
   const int64_t kv = (int64_t)b * a.Hkv + g;
@@ -697,7 +863,7 @@ void decode_split_kernel(DecodeKArgs a) {
       L += f * sm.u.merge.l[w][hrow];
       acc += f * sm.u.merge.o[w][hrow][d];
     }
-    const int64_t pidx = ((int64_t)b * a.Hq + h0 + hrow) * a.n_chunks + chunk_id;
+    const int64_t pidx = (int64_t)(h0 + hrow) * a.x_max + x;
     a.part_o[pidx * 128 + d] = acc;
     if (d == 0) {
       a.part_ml[pidx * 2] = M;
@@ -709,18 +875,16 @@ void decode_split_kernel(DecodeKArgs a) {
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
+  const int* plan;              // written by the split kernel: chunk size, first chunk per sequence
   const float* rot;
   int64_t rot_stride_b;
   const int32_t* seq_lens;
   const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
-  int Hq, G, head_groups;
+  int Hq, G;
   int64_t cap;
-  int chunk, n_chunks;
+  int x_max;                    // partial rows per query head
   float* out;
 };
-
-// Most chunks per row; bounds the combine's LDS.
-constexpr int kMaxChunks = 1024;
 
 // One work-group (2 waves) per (sequence, query head): log-sum-exp merge of the chunk partials with
 // one output coordinate per thread and independent loads, then o = R^T o' = H (blockdiag M_b^T) o'
@@ -732,21 +896,20 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   __shared__ float inv_l;
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int64_t len = a.cap;
-  if (a.positions) {
-    const int64_t p = a.positions[b];
-    len = (p >= 0 && p < a.cap) ? p + 1 : 0;
-  } else if (a.seq_lens) {
-    const int64_t l = a.seq_lens[b];
-    len = l < 0 ? 0 : (l > a.cap ? a.cap : l);
-  }
+  // the plan is read together with the length (both entries exist for every sequence; they are
+  // used only when the sequence has tokens, and then the split kernel wrote them)
+  const int chunk = a.plan[0];
+  const int x0 = a.plan[64 + b];
+  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq}, b);
   float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
   if (len == 0) {                       // an empty sequence attends to nothing
     outp[tid] = 0.f;
     return;
   }
-  const int nvalid = (int)((len + a.chunk - 1) / a.chunk);
-  const float* ml = a.part_ml + ((int64_t)b * a.Hq + h) * a.n_chunks * 2;
+  int nvalid = (len + chunk - 1) / chunk;         // <= kMaxChunks and x0 + nvalid <= x_max by the
+  nvalid = min(nvalid, min(kMaxChunks, a.x_max - x0));   // plan; the bound keeps every read in range
+  const int64_t first = (int64_t)h * a.x_max + x0;   // partial row of chunk 0; chunks are adjacent
+  const float* ml = a.part_ml + first * 2;
   if (wave == 0) {                      // weights 2^(m_c - M) and 1/L
     float M = -INFINITY;
     for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c]);
@@ -766,7 +929,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   }
   __syncthreads();
   {
-    const float* po = a.part_o + ((int64_t)b * a.Hq + h) * a.n_chunks * 128 + tid;
+    const float* po = a.part_o + first * 128 + tid;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int c = 0;
     for (; c + 8 <= nvalid; c += 8) {
@@ -839,28 +1002,31 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   DecodeGeometry geo{};
   const int G = n_q_heads / n_kv_heads;
   geo.head_groups = (G + 7) / 8;
-  // One round of work-groups: kGroupsPerCU are resident per compute unit.  Each (sequence, KV head, head
-  // group) unit gets floor(slots / units) chunks (at least one); chunks are multiples of 128
-  // tokens (one step of the 4 waves), at least 256, and no row has more than kMaxChunks of them.
-  const int64_t units = (int64_t)batch * n_kv_heads * geo.head_groups;
+  // One round of work-groups: kGroupsPerCU are resident per compute unit, and each (KV head, head
+  // group) column of the grid gets `target` of them.  The kernels pick the chunk size from the
+  // lengths so that the batch's chunks number at most `target` per column (or one per sequence when
+  // the batch has more sequences than that): x_max = max(target, batch) work items per column.
+  const int64_t columns = (int64_t)n_kv_heads * geo.head_groups;
   const int64_t slots = kGroupsPerCU * (int64_t)device_cu_count();
-  const int64_t per_unit = units >= slots ? 1 : slots / units;
-  int64_t chunk = (cache_cap + per_unit - 1) / per_unit;
-  const int64_t min_chunk = (cache_cap + kMaxChunks - 1) / kMaxChunks;
-  if (chunk < min_chunk) chunk = min_chunk;
-  chunk = (chunk + 127) / 128 * 128;
-  if (chunk < 256) chunk = 256;
-  geo.chunk = (int)chunk;
-  geo.n_chunks = (int)((cache_cap + chunk - 1) / chunk);
-  const int64_t parts = (int64_t)batch * n_q_heads * geo.n_chunks;
-  geo.workspace_bytes = parts * 128 * 4 + parts * 2 * 4 + 256;
+  int64_t target = slots / columns;
+  // never more work items than the batch can have chunks (256 tokens at least)
+  const int64_t most = (int64_t)batch * ((cache_cap + 255) / 256);
+  if (target > most) target = most;
+  if (target < 1) target = 1;
+  if (target > kMaxChunks) target = kMaxChunks;
+  geo.target = (int)target;
+  geo.x_max = (int)(target > batch ? target : batch);
+  geo.plan_bytes = 256 + ((int64_t)batch * 4 + 255) / 256 * 256;
+  const int64_t parts = (int64_t)geo.x_max * n_q_heads;
+  geo.workspace_bytes = geo.plan_bytes + parts * 128 * 4 + parts * 2 * 4;
   return geo;
 }
 
 hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipStream_t stream) {
   const int G = a.n_q_heads / a.n_kv_heads;
-  const int64_t parts = (int64_t)a.batch * a.n_q_heads * geo.n_chunks;
-  float* part_o = static_cast<float*>(a.workspace);
+  const int64_t parts = (int64_t)geo.x_max * a.n_q_heads;
+  int* plan = static_cast<int*>(a.workspace);
+  float* part_o = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + geo.plan_bytes);
   float* part_ml = part_o + parts * 128;
   const float sm = a.sm_scale > 0.f ? a.sm_scale : kInvSqrtD;
 
@@ -874,14 +1040,16 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.rot = a.rot;
   k.rot_stride_b = a.rot_stride_batch;
   k.seq_lens = a.seq_lens;
+  k.batch = a.batch;
   k.Hq = a.n_q_heads;
   k.Hkv = a.n_kv_heads;
   k.G = G;
   k.head_groups = geo.head_groups;
   k.cap = a.cache_cap;
-  k.chunk = geo.chunk;
-  k.n_chunks = geo.n_chunks;
+  k.target = geo.target;
   k.sm_log2 = sm * kLog2e;
+  k.plan = plan;
+  k.x_max = geo.x_max;
   k.part_o = part_o;
   k.part_ml = part_ml;
   k.positions = a.positions;
@@ -890,7 +1058,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_bf16 = a.new_bf16;
   k.new_stride_seq = a.new_stride_seq;
   k.new_stride_head = a.new_stride_head;
-  const dim3 grid1((unsigned)geo.n_chunks, (unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)a.batch);
+  const dim3 grid1((unsigned)geo.x_max, (unsigned)(a.n_kv_heads * geo.head_groups), 1u);
   if (a.positions)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
   else
@@ -901,16 +1069,15 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   CombineArgs c{};
   c.part_o = part_o;
   c.part_ml = part_ml;
+  c.plan = plan;
   c.rot = a.rot;
   c.rot_stride_b = a.rot_stride_batch;
   c.seq_lens = a.seq_lens;
   c.positions = a.positions;
   c.Hq = a.n_q_heads;
   c.G = G;
-  c.head_groups = geo.head_groups;
   c.cap = a.cache_cap;
-  c.chunk = geo.chunk;
-  c.n_chunks = geo.n_chunks;
+  c.x_max = geo.x_max;
   c.out = a.out;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.batch * a.n_q_heads)), dim3(128), 0, stream, c);
   return hipGetLastError();

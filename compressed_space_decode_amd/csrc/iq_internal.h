@@ -57,9 +57,10 @@ struct DecodeLaunch {
 
 // Split-K geometry shared by the workspace query and the launch.
 struct DecodeGeometry {
-  int chunk;          // tokens per work-group (multiple of 128)
-  int n_chunks;       // ceil(cache_cap / chunk)
   int head_groups;    // ceil(G / 8): query heads are processed 8 at a time
+  int target;         // chunks per (KV head, head group) column the kernels aim for
+  int x_max;          // grid width: most (sequence, chunk) pairs per column
+  int64_t plan_bytes; // workspace head: chunk size and first chunk of each sequence
   int64_t workspace_bytes;
 };
 

@@ -117,9 +117,12 @@ int iq_quantize_kv(const void* k, const void* v, int32_t dtype,
 
 /*
  * iq_decode_workspace_bytes -- device workspace that iq_decode_attention
- * needs for its split-K partial results with these sizes (the split size
- * is chosen by the library from the same arguments).  Negative IQ_E* code
- * on invalid sizes.
+ * (and iq_decode_attention_append) needs with these sizes on the current
+ * device: the split plan (chunk size and each sequence's first chunk) and
+ * the split-K partial results.  The kernels choose the chunk size on the
+ * device from the sequence lengths, so that the batch's chunks fill one
+ * round of work-groups; the bound depends only on these sizes and the
+ * device's compute-unit count.  Negative IQ_E* code on invalid sizes.
  */
 int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                   int32_t n_kv_heads, int64_t cache_cap);

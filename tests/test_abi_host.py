@@ -151,8 +151,14 @@ def test_decode_append_validation(kw, code):
 def test_workspace_bytes():
     n = iq.decode_workspace_bytes(1, 32, 4, 32768)
     assert n > 0
-    # partials: (o' [128] + max + sum) floats per (sequence, query head, chunk)
-    assert (n - 256) % (130 * 4) == 0
+    # a plan head (256 bytes, then one int per sequence rounded up to 256 bytes), then partials:
+    # (o' [128] + max + sum) floats per (work item, query head)
+    assert (n - 512) % (130 * 4 * 32) == 0
+    n16 = iq.decode_workspace_bytes(16, 32, 8, 32768)
+    assert (n16 - 512) % (130 * 4 * 32) == 0
+    n100 = iq.decode_workspace_bytes(100, 8, 8, 1000)
+    assert (n100 - 256 - 512) % (130 * 4 * 8) == 0
+    assert (n100 - 768) // (130 * 4 * 8) >= 100             # at least one work item per sequence
     assert iq.lib().iq_decode_workspace_bytes(1, 6, 4, 100) == binding.IQ_EINVAL
     assert iq.decode_workspace_bytes(16, 32, 8, 32768) >= iq.decode_workspace_bytes(1, 32, 8, 32768)
     assert iq.decode_workspace_bytes(1, 32, 4, 83886016) > 0          # the largest capacity

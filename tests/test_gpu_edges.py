@@ -168,3 +168,20 @@ def test_decode_workspace_reused_across_calls():
     for lens in ([6000, 3000, 17], [1, 0, 5999], [4096, 4097, 128]):
         out, ref = _decode_case(rng, B, Hq, Hkv, cap, lens, workspace=ws)
         P.check_output(out, ref, what="workspace reuse lens=%s" % lens)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,cap,zero_frac", [
+    (16, 32, 8, 5000, 0.0),     # ragged: the chunk size is searched for, one round of work-groups
+    (70, 8, 2, 700, 0.2),       # more than 64 sequences, a fifth of them empty
+    (100, 64, 2, 300, 0.0),     # more sequences than work items per column: one chunk per sequence
+])
+def test_decode_chunk_plan_over_ragged_batches(B, Hq, Hkv, cap, zero_frac):
+    # The kernels size the chunks from the lengths; every (sequence, chunk) pair must be covered
+    # exactly once, so each sequence's output matches the oracle.
+    rng = np.random.default_rng(B * 1000 + cap)
+    lens = rng.integers(1, cap + 1, size=B)
+    lens[rng.random(B) < zero_frac] = 0
+    lens[0] = cap
+    out, ref = _decode_case(rng, B, Hq, Hkv, cap, [int(n) for n in lens])
+    P.check_output(out, ref, "chunk plan B=%d Hq=%d Hkv=%d cap=%d" % (B, Hq, Hkv, cap))
+    assert np.all(out[lens == 0] == 0)
