@@ -129,6 +129,7 @@ struct DecodeKArgs {
   float sm_log2;          // softmax scale times log2(e)
   int* plan;              // [0]: chunk size; [64 + b]: index of sequence b's first chunk
   int x_max;              // grid width: work items per column
+  int guess_per_seq;      // chunks per sequence when every length is cap (a guess, see below)
   float* part_o;          // [Hq][x_max][128], x = index of the (sequence, chunk) pair
   float* part_ml;         // [Hq][x_max][2]  (max in log2 units, sum)
   // fused append (positions != NULL): new token of sequence b written at positions[b]
@@ -149,18 +150,18 @@ struct LenSource {
   int cap, batch;
 };
 
-__device__ __forceinline__ int len_at(const LenSource& s, int i) {
+// The stored value for sequence i (a position or a length; 0 when there is none), then its length.
+__device__ __forceinline__ int len_raw(const LenSource& s, int i) {
+  const int32_t* src = s.positions ? s.positions : s.seq_lens;
+  return (src != nullptr && i < s.batch) ? src[i] : 0;
+}
+__device__ __forceinline__ int len_of(const LenSource& s, int i, int raw) {
   if (i >= s.batch) return 0;
-  if (s.positions) {
-    const int p = s.positions[i];
-    return (p >= 0 && p < s.cap) ? p + 1 : 0;
-  }
-  if (s.seq_lens) {
-    const int l = s.seq_lens[i];
-    return l < 0 ? 0 : (l > s.cap ? s.cap : l);
-  }
+  if (s.positions) return (raw >= 0 && raw < s.cap) ? raw + 1 : 0;
+  if (s.seq_lens) return raw < 0 ? 0 : (raw > s.cap ? s.cap : raw);
   return s.cap;
 }
+__device__ __forceinline__ int len_at(const LenSource& s, int i) { return len_of(s, i, len_raw(s, i)); }
 
 __device__ __forceinline__ long long chunk_round(long long v) {   // up to a multiple of 128, >= 256
   v = (v + 127) / 128 * 128;
@@ -229,8 +230,7 @@ __device__ __forceinline__ bool locate(ChunkPlan& p, int base, int batch, int x,
 // Bounds used: sum ceil(l / c) <= 128 units / c + nz (units = sum ceil(l / 128), nz = sequences
 // with tokens), so c >= 128 units / (target - nz) meets the target when target > nz; otherwise
 // one chunk per sequence.
-__device__ ChunkPlan plan_chunks(const LenSource& s, int target, int x, int lane) {
-  const int l0 = len_at(s, lane);
+__device__ ChunkPlan plan_chunks(const LenSource& s, int l0, int target, int x, int lane) {
   ChunkPlan p{256, -1, -1, 0};
   if (s.batch <= 64) {                 // one sequence per lane; 32-bit (units <= 64 * 2^20)
     const int units = lane63(wave_scan_add((l0 + 127) >> 7));
@@ -329,7 +329,7 @@ struct DecodeSmem {
   DecodeSmemU u;
 };
 
-__device__ void build_block(const float* p, float* out16) {
+__device__ __forceinline__ void build_block(const float* p, float* out16) {
   float l0 = p[0], l1 = p[1], l2 = p[2], l3 = p[3];
   float r0 = p[4], r1 = p[5], r2 = p[6], r3 = p[7];
   const float nl = 1.0f / sqrtf(l0 * l0 + l1 * l1 + l2 * l2 + l3 * l3);
@@ -594,13 +594,44 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   __builtin_amdgcn_wave_barrier();
 }
 
+// Wave 0's set-up loads for sequence b: this lane's 16 query coordinates (head h0 + lane/8, slice
+// lane%8; raw bf16 pairs in q0-q1 or fp32 words in q0-q3) and the 8 rotation parameters of SO(4)
+// block lane%32.
+struct SetupLoads {
+  uint4 q0, q1, q2, q3;
+  float4 r0, r1;
+};
+__device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, int g, int h0, int nh, int lane) {
+  SetupLoads v;
+  const int qi = lane >> 3, qe = lane & 7;
+  const int64_t off = ((int64_t)b * a.Hq + h0 + (qi < nh ? qi : 0)) * 128 + 16 * qe;
+  if (a.q_bf16) {
+    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+    v.q0 = qp[0];
+    v.q1 = qp[1];
+    v.q2 = v.q3 = make_uint4(0u, 0u, 0u, 0u);
+  } else {
+    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + off);
+    v.q0 = qp[0];
+    v.q1 = qp[1];
+    v.q2 = qp[2];
+    v.q3 = qp[3];
+  }
+  const float* rq = a.rot + b * a.rot_stride_b + (int64_t)g * 256 + (lane & 31) * 8;
+  v.r0 = make_float4(rq[0], rq[1], rq[2], rq[3]);
+  v.r1 = make_float4(rq[4], rq[5], rq[6], rq[7]);
+  return v;
+}
+
 template <bool kAppend>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
-  const int x = blockIdx.x;          // (sequence, chunk) pair
-  const int g = blockIdx.y / a.head_groups;
-  const int hg = blockIdx.y % a.head_groups;
+  // blockIdx.x: (KV head, head group) column, so consecutive work-groups take the columns of one
+  // work item (measured slightly faster than the transposed order)
+  const int x = blockIdx.y;          // (sequence, chunk) pair
+  const int g = blockIdx.x / a.head_groups;
+  const int hg = blockIdx.x % a.head_groups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
@@ -608,13 +639,28 @@ void decode_split_kernel(DecodeKArgs a) {
   // Token indices are 32-bit and a sequence's codes fit one buffer resource (the capacity is
   // validated: cap * 48 < 0xF0000000): uniform token arithmetic stays on the scalar unit.
   const int cap = (int)a.cap;
+  const int h0 = g * a.G + hg * 8;
+  const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
+  // Wave 0's set-up loads are issued before the plan is known, for the sequence that work item x
+  // belongs to when every length is cap (the common case), and issued again only if the plan
+  // says otherwise: the query and rotation loads then overlap the plan.
+  // (the lengths are loaded first: memory loads complete in order, so the plan then waits for
+  // them alone)
   const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch};
-  const ChunkPlan plan = plan_chunks(src, a.target, x, lane);
+  const int raw0 = len_raw(src, lane);                       // sequences 0..63
+  int b_guess = x / a.guess_per_seq;
+  if (b_guess > a.batch - 1) b_guess = a.batch - 1;
+  // (every wave issues them, so that all waves have the same loads in flight when the plan waits
+  // for the lengths; only wave 0 uses them)
+  SetupLoads sl = load_setup(a, b_guess, g, h0, nh, lane);
+  const int l0 = len_of(src, lane, raw0);
+  const ChunkPlan plan = plan_chunks(src, l0, a.target, x, lane);
   if (plan.b < 0) return;                                    // uniform: past the last chunk
   const int b = plan.b;
+  if (wave == 0 && b != b_guess) sl = load_setup(a, b, g, h0, nh, lane);   // uniform
   const int len = plan.len;          // > 0
   // the combine reads the plan from here
-  if (tid == 0 && blockIdx.y == 0) {
+  if (tid == 0 && blockIdx.x == 0) {
     if (x == 0) a.plan[0] = plan.chunk;
     if (plan.j == 0) a.plan[64 + b] = x;
   }
@@ -623,8 +669,6 @@ void decode_split_kernel(DecodeKArgs a) {
   const int tok0 = plan.j * plan.chunk;
   if (tok0 >= len) return;                                   // uniform; never taken
   const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
-  const int h0 = g * a.G + hg * 8;
-  const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
   const int64_t kv = (int64_t)b * a.Hkv + g;
   const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
 
@@ -647,27 +691,27 @@ void decode_split_kernel(DecodeKArgs a) {
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   SetupSmem& ss = sm.u.setup;
   if (wave == 0) {
-    if (lane < 32) build_block(rot + lane * 8, ss.blk[lane]);
+    if (lane < 32) {
+      const float rp[8] = {sl.r0.x, sl.r0.y, sl.r0.z, sl.r0.w, sl.r1.x, sl.r1.y, sl.r1.z, sl.r1.w};
+      build_block(rp, ss.blk[lane]);
+    }
     const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
     float x[16];
     {
       const bool have = qi < nh;
-      const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * qe;
       if (a.q_bf16) {
-        const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-        const uint4 u0 = qp[0], u1 = qp[1];
-        const unsigned w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        const unsigned w[8] = {sl.q0.x, sl.q0.y, sl.q0.z, sl.q0.w, sl.q1.x, sl.q1.y, sl.q1.z, sl.q1.w};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           x[2 * i] = __uint_as_float(w[i] << 16);
           x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
         }
       } else {
-        const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
+        const uint4 qv[4] = {sl.q0, sl.q1, sl.q2, sl.q3};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float4 v = qp[i];
-          x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
+          x[4 * i] = __uint_as_float(qv[i].x); x[4 * i + 1] = __uint_as_float(qv[i].y);
+          x[4 * i + 2] = __uint_as_float(qv[i].z); x[4 * i + 3] = __uint_as_float(qv[i].w);
         }
       }
       if (!have) {
@@ -1016,6 +1060,16 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   if (target > kMaxChunks) target = kMaxChunks;
   geo.target = (int)target;
   geo.x_max = (int)(target > batch ? target : batch);
+  // chunks per sequence when every length is cap, by the kernels' first estimate of the chunk size
+  // (the kernels use it only to start their set-up loads early)
+  {
+    const int64_t units = (int64_t)batch * ((cache_cap + 127) / 128);
+    int64_t c = (units + target - 1) / target * 128;
+    const int64_t cmax = (cache_cap + 127) / 128 * 128 < 256 ? 256 : (cache_cap + 127) / 128 * 128;
+    if (c < 256) c = 256;
+    if (c > cmax) c = cmax;
+    geo.guess_per_seq = (int)((cache_cap + c - 1) / c);
+  }
   geo.plan_bytes = 256 + ((int64_t)batch * 4 + 255) / 256 * 256;
   const int64_t parts = (int64_t)geo.x_max * n_q_heads;
   geo.workspace_bytes = geo.plan_bytes + parts * 128 * 4 + parts * 2 * 4;
@@ -1050,6 +1104,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.sm_log2 = sm * kLog2e;
   k.plan = plan;
   k.x_max = geo.x_max;
+  k.guess_per_seq = geo.guess_per_seq;
   k.part_o = part_o;
   k.part_ml = part_ml;
   k.positions = a.positions;
@@ -1058,7 +1113,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_bf16 = a.new_bf16;
   k.new_stride_seq = a.new_stride_seq;
   k.new_stride_head = a.new_stride_head;
-  const dim3 grid1((unsigned)geo.x_max, (unsigned)(a.n_kv_heads * geo.head_groups), 1u);
+  const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)geo.x_max, 1u);
   if (a.positions)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
   else

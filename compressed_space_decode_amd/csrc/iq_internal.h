@@ -60,6 +60,7 @@ struct DecodeGeometry {
   int head_groups;    // ceil(G / 8): query heads are processed 8 at a time
   int target;         // chunks per (KV head, head group) column the kernels aim for
   int x_max;          // grid width: most (sequence, chunk) pairs per column
+  int guess_per_seq;  // chunks per sequence when every length is cap (>= 1)
   int64_t plan_bytes; // workspace head: chunk size and first chunk of each sequence
   int64_t workspace_bytes;
 };
