@@ -17,6 +17,10 @@ docstring).  Parity status of each function:
     quantize, pack, unpack, decode_attention, make_rotation: pinned by
     tests/test_oracle_*.py (closed forms, textbook identities, brute force,
     hand-derived golden bytes, published generator test vectors).
+  * diagnostics.isotropy_stats (the isotropy measures of the rotation and
+    its variants): pinned by tests/test_oracle_diagnostics.py (closed-form
+    kurtosis values, a hand-worked quantization error, independent
+    butterfly / Hamilton-product transforms, a permutation test).
   * The *choice* of reading (Hadamard ordering, quaternion convention,
     quantizer levels, bit layout) cannot be pinned by the pages; parity is
     against these readings.
@@ -27,4 +31,5 @@ from .isoquant import (  # noqa: F401
     block_matrix, rotation_matrix, rotate, quantize, dequantize_rotated,
     pack, unpack, decode_attention, dense_attention_on_dequantized,
 )
+from . import diagnostics  # noqa: F401
 from .rotation_gen import splitmix64, make_rotation  # noqa: F401
