@@ -62,6 +62,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-other-shapes", action="store_true", help="skip the gqa8k and ragged decode timings")
+    ap.add_argument("--no-isotropy", action="store_true", help="skip the isotropy diagnostics")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
@@ -98,6 +99,22 @@ def time_calls(fn, iters, stream):
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / iters
+
+
+def isotropy_summary(iq, W, x, rot, seed):
+    """The isotropy statistics of x [S][H][T][128] under every transform, summarised over the
+    heads: mean and largest per-coordinate kurtosis, mean 3-bit quantization error (relative) and
+    mean peak-to-average power ratio."""
+    import torch
+    S, H = x.shape[:2]
+    dense = torch.from_numpy(W.dense_rotations(seed, S * H)).to(x.device)
+    out = {}
+    for mode in iq.TRANSFORMS:
+        st = iq.isotropy_stats(x, mode, rot=rot, dense=dense).cpu().numpy().reshape(S * H, -1)
+        out[mode] = {"kurtosis_mean": float(st[:, 0:128].mean()), "kurtosis_max": float(st[:, 0:128].max()),
+                     "vector_kurtosis": float(st[:, 256].mean()), "rel_quant_mse": float(st[:, 257].mean()),
+                     "papr": float(st[:, 258].mean())}
+    return out
 
 
 def time_graph(fn, per_graph, replays, stream):
@@ -226,6 +243,9 @@ def main():
 
     # ---------------- the other decode shapes: GQA at 8K and the ragged batch ----------------
     others = {}
+    iso_quality = {}
+    if not args.no_isotropy:
+        iso_quality["long32k"] = isotropy_summary(iq, W, k_all[:1], rot[:1], seed=100)
     if not args.no_other_shapes:
         for name in ("gqa8k", "ragged"):
             wo = W.decode_workload(name)
@@ -238,6 +258,8 @@ def main():
             kso = torch.empty((Bo, Hkvo, To), dtype=torch.float32, device=dev)
             vso = torch.empty_like(kso)
             iq.quantize_kv(ko, vo, roto, kco, kso, vco, vso)
+            if not args.no_isotropy:
+                iso_quality[name] = isotropy_summary(iq, W, ko, roto, seed=len(iso_quality))
             del ko, vo
             qo = bf16(wo["q"])
             lo = torch.from_numpy(wo["seq_lens"]).to(dev)
@@ -264,6 +286,7 @@ def main():
 
     # ---------------- bulk prefill quantization ----------------
     prefill = None
+    iso_timing = None
     if not args.no_prefill:
         del k_all, v_all
         torch.cuda.empty_cache()
@@ -293,6 +316,24 @@ def main():
                    "GBs": qbytes / t_q / 1e9, "frac_of_hbm_peak": qbytes / t_q / 1e9 / HBM_PEAK_GBS,
                    "vectors_per_s": LAYERS * HKV * T * 2 / t_q}
         log("prefill quantize %.2f ms, %.0f GB/s" % (t_q * 1e3, prefill["GBs"]))
+        if not args.no_isotropy:
+            iso_quality["prefill"] = isotropy_summary(iq, W, pk[:1], prot[:1], seed=101)
+            # throughput of the statistics kernels over the 48-layer K (bf16), per transform
+            pdense = torch.from_numpy(W.dense_rotations(102, LAYERS * HKV)).to(dev)
+            st_buf = torch.empty((LAYERS, HKV, iq.N_STATS), dtype=torch.float64, device=dev)
+            ws_iso = torch.empty(iq.isotropy_workspace_bytes(LAYERS, HKV, T), dtype=torch.uint8, device=dev)
+            iso_bytes = LAYERS * HKV * T * D * 2
+            iso_timing = {}
+            for mode in iq.TRANSFORMS:
+                def iso_fn(mode=mode):
+                    iq.isotropy_stats(pk, mode, rot=prot, dense=pdense, stats=st_buf, workspace=ws_iso)
+                iso_fn()
+                torch.cuda.synchronize()
+                t_i = time_calls(iso_fn, 10 if mode == "dense" else 20, stream)
+                iso_timing[mode] = {"ms": t_i * 1e3, "GBs": iso_bytes / t_i / 1e9,
+                                    "frac_of_hbm_peak": iso_bytes / t_i / 1e9 / HBM_PEAK_GBS}
+                log("isotropy stats (%s) %.2f ms, %.0f GB/s" % (mode, t_i * 1e3, iso_bytes / t_i / 1e9))
+            del pdense, ws_iso
 
     # ---------------- CPU oracle baseline ----------------
     cpu = None
@@ -347,6 +388,10 @@ def main():
         "single_layer_decode": single,
         "other_decode_shapes": others,
         "prefill_quantize": prefill,
+        "isotropy": None if args.no_isotropy else {
+            "timing": {"workload": "K of prefill 48x4x32768 bf16 Student-t(3), stats per (layer, head)",
+                       "by_transform": iso_timing},
+            "quality": iso_quality},
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

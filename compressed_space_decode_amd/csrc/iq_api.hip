@@ -276,3 +276,86 @@ extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const 
   }
   return IQ_OK;
 }
+
+extern "C" int64_t iq_isotropy_workspace_bytes(int64_t n_seq, int32_t n_heads, int64_t n_tokens) {
+  iq::clear_error();
+  if (n_seq < 1 || n_seq > 65535 || n_heads < 1 || n_heads > 65535 || n_tokens < 0 || n_tokens > (int64_t)1 << 40) {
+    iq::set_error("iq_isotropy_workspace_bytes: need 1 <= n_seq, n_heads <= 65535 and 0 <= n_tokens <= 2^40");
+    return IQ_EINVAL;
+  }
+  return iq::diag_workspace_bytes(n_seq, n_heads, n_tokens);
+}
+
+extern "C" int iq_isotropy_stats(const void* x, int32_t dtype, int64_t n_seq, int32_t n_heads, int64_t n_tokens,
+                                 int64_t stride_seq, int64_t stride_head, int64_t stride_tok, int32_t transform,
+                                 const float* rot, int64_t rot_stride_seq, const float* dense,
+                                 int64_t dense_stride_seq, double* stats, void* workspace, int64_t workspace_bytes,
+                                 void* stream) {
+  static const char* fn = "iq_isotropy_stats";
+  iq::clear_error();
+  if (dtype != IQ_F32 && dtype != IQ_BF16) {
+    iq::set_error("%s: unknown dtype %d", fn, dtype);
+    return IQ_EUNSUPPORTED;
+  }
+  if (transform < IQ_T_NONE || transform > IQ_T_DENSE) {
+    iq::set_error("%s: unknown transform %d", fn, transform);
+    return IQ_EUNSUPPORTED;
+  }
+  if (n_seq < 1 || n_seq > 65535 || n_heads < 1 || n_heads > 65535 || n_tokens < 0 || n_tokens > (int64_t)1 << 40) {
+    iq::set_error("%s: need 1 <= n_seq, n_heads <= 65535 and 0 <= n_tokens <= 2^40", fn);
+    return IQ_EINVAL;
+  }
+  if (stats == nullptr || !aligned(stats, 8)) {
+    iq::set_error("%s: stats is NULL or not 8-byte aligned", fn);
+    return IQ_EINVAL;
+  }
+  if (n_tokens > 0 && x == nullptr) {
+    iq::set_error("%s: x is NULL", fn);
+    return IQ_EINVAL;
+  }
+  if ((transform == IQ_T_SO4 || transform == IQ_T_WHT_SO4) && (rot == nullptr || rot_stride_seq < 0 || !aligned(rot, 4))) {
+    iq::set_error("%s: this transform needs rot (4-byte aligned, rot_stride_seq >= 0)", fn);
+    return IQ_EINVAL;
+  }
+  if (transform == IQ_T_DENSE && (dense == nullptr || dense_stride_seq < 0 || !aligned(dense, 4))) {
+    iq::set_error("%s: IQ_T_DENSE needs dense (4-byte aligned, dense_stride_seq >= 0)", fn);
+    return IQ_EINVAL;
+  }
+  if (stride_seq < 0 || stride_head < 0 || stride_tok < 0) {
+    iq::set_error("%s: a stride is negative", fn);
+    return IQ_EINVAL;
+  }
+  const int64_t vec_align = dtype == IQ_BF16 ? 8 : 4;   // 16 bytes
+  if ((stride_seq % vec_align) || (stride_head % vec_align) || (stride_tok % vec_align) || (x && !aligned(x, 16))) {
+    iq::set_error("%s: x must be 16-byte aligned with strides a multiple of 16 bytes", fn);
+    return IQ_EINVAL;
+  }
+  const int64_t need = iq::diag_workspace_bytes(n_seq, n_heads, n_tokens);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) {
+    iq::set_error("%s: workspace must be 256-byte aligned and hold %lld bytes (got %lld)", fn, (long long)need,
+                  (long long)workspace_bytes);
+    return IQ_EWORKSPACE;
+  }
+  iq::DiagLaunch a{};
+  a.x = x;
+  a.bf16 = dtype == IQ_BF16;
+  a.n_seq = n_seq;
+  a.n_heads = n_heads;
+  a.n_tokens = n_tokens;
+  a.stride_seq = stride_seq;
+  a.stride_head = stride_head;
+  a.stride_tok = stride_tok;
+  a.mode = transform;
+  a.rot = rot;
+  a.rot_stride_seq = rot_stride_seq;
+  a.dense = dense;
+  a.dense_stride_seq = dense_stride_seq;
+  a.stats = stats;
+  a.workspace = workspace;
+  const hipError_t err = iq::launch_diag(a, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
+    return IQ_EHIP;
+  }
+  return IQ_OK;
+}

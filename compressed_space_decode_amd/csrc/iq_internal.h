@@ -30,6 +30,26 @@ struct QuantizeLaunch {
 
 hipError_t launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
 
+// Isotropy statistics of one set of vectors after a transform (iq_isotropy_stats).
+struct DiagLaunch {
+  const void* x;
+  int bf16;
+  int64_t n_seq;
+  int n_heads;
+  int64_t n_tokens;
+  int64_t stride_seq, stride_head, stride_tok;   // elements
+  int mode;                                      // IQ_T_*
+  const float* rot;
+  int64_t rot_stride_seq;                        // floats
+  const float* dense;
+  int64_t dense_stride_seq;                      // floats
+  double* stats;                                 // [n_seq][n_heads][IQ_N_STATS]
+  void* workspace;
+};
+
+int64_t diag_workspace_bytes(int64_t n_seq, int n_heads, int64_t n_tokens);
+hipError_t launch_diag(const DiagLaunch& a, hipStream_t stream);
+
 struct DecodeLaunch {
   const void* q;
   int q_bf16;

@@ -28,6 +28,28 @@ __device__ __forceinline__ unsigned dpp_xor1_u(unsigned x) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
 }
 
+// SO(4) block b as a row-major 4x4 matrix: M_b = L(qL) * Rm(conj(qR)) with the quaternions
+// normalised first (the block acts as v -> qL v conj(qR) on coordinates 4b..4b+3).
+__device__ inline void build_so4_block(const float* p, float* out16) {
+  float l0 = p[0], l1 = p[1], l2 = p[2], l3 = p[3];
+  float r0 = p[4], r1 = p[5], r2 = p[6], r3 = p[7];
+  const float nl = 1.0f / sqrtf(l0 * l0 + l1 * l1 + l2 * l2 + l3 * l3);
+  const float nr = 1.0f / sqrtf(r0 * r0 + r1 * r1 + r2 * r2 + r3 * r3);
+  l0 *= nl; l1 *= nl; l2 *= nl; l3 *= nl;
+  r0 *= nr; r1 *= nr; r2 *= nr; r3 *= nr;
+  const float L[4][4] = {{l0, -l1, -l2, -l3}, {l1, l0, -l3, l2}, {l2, l3, l0, -l1}, {l3, -l2, l1, l0}};
+  const float C[4][4] = {{r0, r1, r2, r3}, {-r1, r0, -r3, r2}, {-r2, r3, r0, -r1}, {-r3, -r2, r1, r0}};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc = fmaf(L[i][m], C[m][j], acc);
+      out16[i * 4 + j] = acc;
+    }
+}
+
 // Folded block b: F = M_b * H_4 / sqrt(128), M_b = L(qL) * Rm(conj(qR)) with the quaternions
 // normalised first.  H_128 = (I_32 (x) H_4)(H_32 (x) I_4), so the two finest Hadamard stages act
 // inside the aligned blocks of four and fold into them.

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_PKG, "libiq.so")
 IQ_OK, IQ_EINVAL, IQ_EUNSUPPORTED, IQ_EWORKSPACE, IQ_EHIP = 0, -1, -2, -3, -4
 IQ_F32, IQ_BF16 = 0, 1
 HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS = 128, 3, 48, 256
+TRANSFORMS = {"none": 0, "wht": 1, "so4": 2, "wht_so4": 3, "dense": 4}   # IQ_T_*
+N_STATS = 260
 
 # (name, restype, argtypes) of every entry point declared in include/iq.h
 _P = ctypes.c_void_p
@@ -31,6 +33,9 @@ SIGNATURES = {
     "iq_decode_attention_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
                                                   _I64, _I32, _I32, _I32, _I64, _F, _P, _P, _I64, _I32, _I32,
                                                   _P]),
+    "iq_isotropy_workspace_bytes": (_I64, [_I64, _I32, _I64]),
+    "iq_isotropy_stats": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64,
+                                         _P, _P, _I64, _P]),
 }
 
 
@@ -213,3 +218,45 @@ def decode_attention_append(q, k_new, v_new, positions, k_codes, k_scales, v_cod
         workspace.data_ptr(), workspace.numel() * workspace.element_size(), HEAD_DIM, BITS, _stream(q))
     _check(rc)
     return out
+
+
+def isotropy_workspace_bytes(n_seq, n_heads, n_tokens):
+    n = lib().iq_isotropy_workspace_bytes(int(n_seq), int(n_heads), int(n_tokens))
+    if n < 0:
+        raise IQError(int(n), last_error())
+    return int(n)
+
+
+def isotropy_stats(x, transform, rot=None, dense=None, shared=False, stats=None, workspace=None):
+    """Statistics of y = T x over the tokens of every (sequence, head) of x
+    [n_seq][n_heads][n_tokens][128] (cuda, f32/bf16, last dim contiguous), for a transform in
+    TRANSFORMS.  rot: float32 [n_seq][n_heads][32][8] ("so4", "wht_so4"); dense: float32
+    [n_seq][n_heads][128][128] ("dense"); with shared=True both drop the n_seq dimension.
+    Returns float64 [n_seq][n_heads][260] on the device (layout in include/iq.h)."""
+    import torch
+    n_seq, n_heads, n_tokens, d = x.shape
+    if d != HEAD_DIM or x.stride(3) != 1:
+        raise ValueError("x must be [n_seq][n_heads][n_tokens][128] with contiguous coordinates")
+    mode = TRANSFORMS[transform]
+    per = n_heads if shared else n_seq * n_heads
+    rot_ptr, rot_stride, dense_ptr, dense_stride = None, 0, None, 0
+    if transform in ("so4", "wht_so4"):
+        if rot is None or rot.numel() != per * ROT_PARAMS or not rot.is_contiguous() or rot.dtype != torch.float32:
+            raise ValueError("rot must be a contiguous float32 tensor of %d values" % (per * ROT_PARAMS))
+        rot_ptr, rot_stride = rot.data_ptr(), 0 if shared else n_heads * ROT_PARAMS
+    if transform == "dense":
+        if (dense is None or dense.numel() != per * HEAD_DIM * HEAD_DIM or not dense.is_contiguous()
+                or dense.dtype != torch.float32):
+            raise ValueError("dense must be a contiguous float32 tensor of %d values" % (per * HEAD_DIM * HEAD_DIM))
+        dense_ptr, dense_stride = dense.data_ptr(), 0 if shared else n_heads * HEAD_DIM * HEAD_DIM
+    if stats is None:
+        stats = torch.empty((n_seq, n_heads, N_STATS), dtype=torch.float64, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(isotropy_workspace_bytes(n_seq, n_heads, n_tokens), dtype=torch.uint8,
+                                device=x.device)
+    rc = lib().iq_isotropy_stats(
+        x.data_ptr() if n_tokens else None, _dtype_code(x), n_seq, n_heads, n_tokens,
+        x.stride(0), x.stride(1), x.stride(2), mode, rot_ptr, rot_stride, dense_ptr, dense_stride,
+        stats.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
+    _check(rc)
+    return stats

@@ -60,6 +60,16 @@ def rotation_params(rng, n):
     return g.reshape(n, 32, 8).astype(np.float32)
 
 
+def dense_rotations(seed, n):
+    """float32 [n][128][128] random rotations for the dense-rotation comparison: Haar-distributed
+    orthogonal matrices (QR of a Gaussian matrix with the signs of R's diagonal moved into Q),
+    drawn from SeedSequence([6, seed])."""
+    rng = np.random.default_rng(np.random.SeedSequence([6, int(seed)]))
+    a = rng.standard_normal((n, D, D))
+    q, r = np.linalg.qr(a)
+    return (q * np.sign(np.diagonal(r, axis1=-2, axis2=-1))[:, None, :]).astype(np.float32)
+
+
 def _as_dtype(x, dtype):
     if dtype == "bf16":
         return f32_to_bf16_bits(x)

@@ -203,6 +203,66 @@ int iq_decode_attention_append(const void* q, int32_t q_dtype,
                                void* workspace, int64_t workspace_bytes,
                                int32_t head_dim, int32_t bits, void* stream);
 
+/*
+ * Isotropy diagnostics.  Source: Abstract (the Walsh-Hadamard transform
+ * followed by block-diagonal SO(4) rotations is applied so that every
+ * vector's coordinates look alike before 3-bit scalar quantization with one
+ * scale per vector).  These calls measure that effect for the method's
+ * transform and the variants it is compared with.
+ */
+enum {
+  IQ_T_NONE = 0,      /* y = x */
+  IQ_T_WHT = 1,       /* y = H x (normalised Sylvester Walsh-Hadamard) */
+  IQ_T_SO4 = 2,       /* y = blockdiag(M_b) x (the SO(4) blocks alone) */
+  IQ_T_WHT_SO4 = 3,   /* y = blockdiag(M_b) H x (the method's rotation) */
+  IQ_T_DENSE = 4      /* y = T x with a caller-given 128x128 matrix T */
+};
+enum { IQ_N_STATS = 260 };
+
+/*
+ * iq_isotropy_workspace_bytes -- device workspace iq_isotropy_stats needs
+ * for these sizes (partial sums of every 256 tokens).  Negative IQ_E* code
+ * on invalid sizes.
+ */
+int64_t iq_isotropy_workspace_bytes(int64_t n_seq, int32_t n_heads, int64_t n_tokens);
+
+/*
+ * iq_isotropy_stats -- statistics of y = T x over the tokens of every
+ * (sequence, head).
+ *   x            [n_seq][n_heads][n_tokens][128] (element strides; the last
+ *                dimension contiguous), dtype IQ_F32 or IQ_BF16, 16-byte
+ *                aligned with strides a multiple of 16 bytes.
+ *   transform    IQ_T_*.
+ *   rot          SO(4) params of (s,h) at rot + s*rot_stride_seq + h*256
+ *                (IQ_T_SO4, IQ_T_WHT_SO4; otherwise unused and may be NULL).
+ *   dense        row-major T of (s,h) at dense + s*dense_stride_seq +
+ *                h*16384 (IQ_T_DENSE; otherwise unused and may be NULL).
+ *   stats        double [n_seq][n_heads][IQ_N_STATS]:
+ *                  [0:128]   kurtosis m4/m2^2 of each coordinate of y over
+ *                            the tokens (population central moments);
+ *                  [128:256] variance m2 of each coordinate;
+ *                  [256]     kurtosis of each vector's 128 entries, averaged
+ *                            over the tokens;
+ *                  [257]     3-bit quantization error of y (the quantizer
+ *                            above), sum |y - y_hat|^2 / sum |y|^2;
+ *                  [258]     peak-to-average power ratio 128 max_i y_i^2 /
+ *                            |y|^2, averaged over the nonzero vectors;
+ *                  [259]     n_tokens.
+ *                A variance at most 1e-9 times the mean square of the same
+ *                values counts as zero, and its kurtosis is reported as 0;
+ *                a zero denominator gives 0; n_tokens = 0 gives all zeros.
+ *   workspace    device buffer of at least iq_isotropy_workspace_bytes(...)
+ *                bytes, 256-byte aligned, used only during the call.
+ * Errors: IQ_EINVAL (NULL pointers, sizes out of range, negative strides,
+ * misalignment, a missing rot or dense for the transform), IQ_EUNSUPPORTED
+ * (dtype or transform), IQ_EWORKSPACE, IQ_EHIP.
+ */
+int iq_isotropy_stats(const void* x, int32_t dtype, int64_t n_seq, int32_t n_heads, int64_t n_tokens,
+                      int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
+                      int32_t transform, const float* rot, int64_t rot_stride_seq,
+                      const float* dense, int64_t dense_stride_seq,
+                      double* stats, void* workspace, int64_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
                                   "iq_decode_workspace_bytes", "iq_decode_attention",
-                                  "iq_decode_attention_append"])
+                                  "iq_decode_attention_append", "iq_isotropy_workspace_bytes",
+                                  "iq_isotropy_stats"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -163,3 +164,44 @@ def test_workspace_bytes():
     assert iq.decode_workspace_bytes(16, 32, 8, 32768) >= iq.decode_workspace_bytes(1, 32, 8, 32768)
     assert iq.decode_workspace_bytes(1, 32, 4, 83886016) > 0          # the largest capacity
     assert iq.lib().iq_decode_workspace_bytes(1, 32, 4, 83886017) == binding.IQ_EINVAL
+
+
+def _iso(**kw):
+    args = dict(x=FAKE, dt=1, S=2, H=4, T=1000, ss=4 * 1000 * 128, sh=1000 * 128, st=128, tr=3, rot=FAKE, rs=1024,
+                dense=None, ds=0, stats=FAKE, ws=FAKE, wsb=1 << 30)
+    args.update(kw)
+    return iq.lib().iq_isotropy_stats(args["x"], args["dt"], args["S"], args["H"], args["T"], args["ss"], args["sh"],
+                                      args["st"], args["tr"], args["rot"], args["rs"], args["dense"], args["ds"],
+                                      args["stats"], args["ws"], args["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), binding.IQ_EUNSUPPORTED),
+    (dict(tr=5), binding.IQ_EUNSUPPORTED),
+    (dict(tr=-1), binding.IQ_EUNSUPPORTED),
+    (dict(S=0), binding.IQ_EINVAL),
+    (dict(H=70000), binding.IQ_EINVAL),
+    (dict(T=-1), binding.IQ_EINVAL),
+    (dict(stats=None), binding.IQ_EINVAL),
+    (dict(stats=FAKE + 4), binding.IQ_EINVAL),       # doubles: 8-byte aligned
+    (dict(x=None), binding.IQ_EINVAL),
+    (dict(rot=None), binding.IQ_EINVAL),              # the method's transform needs the SO(4) params
+    (dict(tr=2, rs=-1), binding.IQ_EINVAL),
+    (dict(tr=4), binding.IQ_EINVAL),                  # dense transform without a matrix
+    (dict(st=100), binding.IQ_EINVAL),                # not a multiple of 16 bytes
+    (dict(x=FAKE + 8), binding.IQ_EINVAL),
+    (dict(ws=None), binding.IQ_EWORKSPACE),
+    (dict(wsb=1000), binding.IQ_EWORKSPACE),
+    (dict(ws=FAKE + 128), binding.IQ_EWORKSPACE),
+])
+def test_isotropy_validation(kw, code):
+    assert _iso(**kw) == code
+    assert binding.last_error().startswith("iq_isotropy_stats")
+
+
+def test_isotropy_workspace_bytes():
+    # y_ref [128] plus (4 moments x 128 + 8 scalars) floats per 256 tokens, per (sequence, head)
+    n = iq.isotropy_workspace_bytes(2, 3, 1000)
+    assert n == 2 * 3 * (128 + 4 * (4 * 128 + 8)) * 4 + 256
+    assert iq.isotropy_workspace_bytes(1, 1, 0) == 128 * 4 + 256
+    assert iq.lib().iq_isotropy_workspace_bytes(0, 1, 10) == binding.IQ_EINVAL
