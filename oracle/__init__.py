@@ -14,7 +14,8 @@ full-precision KV state.
 Every step the pages leave open is a documented reading (see each function's
 docstring).  Parity status of each function:
   * hadamard, quat_left, quat_right, block_matrix, rotation_matrix,
-    quantize, pack, unpack, decode_attention, make_rotation: pinned by
+    quantize, pack, unpack, decode_attention, multi_token_attention,
+    make_rotation: pinned by
     tests/test_oracle_*.py (closed forms, textbook identities, brute force,
     hand-derived golden bytes, published generator test vectors).
   * diagnostics.isotropy_stats (the isotropy measures of the rotation and
@@ -29,7 +30,7 @@ from .isoquant import (  # noqa: F401
     D, NBLK, LEVELS, RECORD_BYTES,
     bf16_bits_to_f64, hadamard, quat_left, quat_right, quat_conj,
     block_matrix, rotation_matrix, rotate, quantize, dequantize_rotated,
-    pack, unpack, decode_attention, dense_attention_on_dequantized,
+    pack, unpack, decode_attention, multi_token_attention, dense_attention_on_dequantized,
 )
 from . import diagnostics  # noqa: F401
 from .rotation_gen import splitmix64, make_rotation  # noqa: F401

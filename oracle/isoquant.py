@@ -229,6 +229,31 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, params, seq_lens,
     return out
 
 
+def multi_token_attention(q, k_codes, k_scales, v_codes, v_scales, params, seq_lens,
+                          sm_scale=None):
+    """Attention of several new query tokens per sequence on the packed cache, fp64.
+
+    Shapes: q [B][Q][Hq][128]; the cache as in decode_attention; seq_lens [B]
+    counts the cached tokens including the Q new ones, which are the last Q
+    positions.  Returns float64 [B][Q][Hq][128].
+
+    Reading (the paper's execution model applied to more than one query, as
+    in chunked prefill or checking several drafted tokens at once): query
+    token i of sequence b sits at position seq_lens[b] - Q + i and attends
+    causally to positions 0 .. seq_lens[b] - Q + i; a token whose position is
+    below 0 sees nothing and gets zeros.  Each token's result is a decode
+    step with that length.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Q = q.shape[:2]
+    out = np.zeros(q.shape)
+    for i in range(Q):
+        lens = np.maximum(np.asarray(seq_lens, dtype=np.int64) - Q + i + 1, 0)
+        out[:, i] = decode_attention(q[:, i], k_codes, k_scales, v_codes, v_scales, params, lens,
+                                     sm_scale=sm_scale)
+    return out
+
+
 def dense_attention_on_dequantized(q, k_codes, k_scales, v_codes, v_scales, params,
                                    seq_lens, sm_scale=None):
     """The same attention computed the conventional way: dequantize K and V,

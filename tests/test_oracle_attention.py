@@ -141,3 +141,47 @@ def test_retrieval_of_a_planted_key_survives_quantization_in_oracle():
     R = oracle.rotation_matrix(p[0, 0])
     z = oracle.dequantize_rotated(kc, ks) @ (R @ q[0, 0])
     assert int(np.argmax(z)) == pos
+
+
+def test_multi_token_attention_matches_masked_torch_sdpa():
+    # Q new tokens at the last Q positions, each attending to the positions up to its own:
+    # PyTorch's fp64 attention with an explicit boolean mask on the dequantized, unrotated K/V.
+    rng = np.random.default_rng(30)
+    T, Q = 23, 4
+    _, kc, ks, vc, vs, p, _ = _case(rng, B=2, Hq=4, Hkv=2, T=T)
+    q = rng.standard_normal((2, Q, 4, 128))
+    lens = np.array([T, 15])
+    out = oracle.multi_token_attention(q, kc, ks, vc, vs, p, lens)
+    for b in range(2):
+        n = lens[b]
+        mask = torch.tensor(np.arange(T)[None, :] <= (n - Q + np.arange(Q))[:, None])
+        for g in range(2):
+            R = oracle.rotation_matrix(p[b, g])
+            khat = torch.tensor(oracle.dequantize_rotated(kc[b, g], ks[b, g]) @ R)
+            vhat = torch.tensor(oracle.dequantize_rotated(vc[b, g], vs[b, g]) @ R)
+            for h in range(2 * g, 2 * g + 2):
+                qq = torch.tensor(q[b, :, h])[None, None]
+                ref = torch.nn.functional.scaled_dot_product_attention(
+                    qq, khat[None, None], vhat[None, None], attn_mask=mask)[0, 0].numpy()
+                np.testing.assert_allclose(out[b, :, h], ref, rtol=1e-10, atol=1e-12)
+
+
+def test_multi_token_attention_special_cases():
+    rng = np.random.default_rng(31)
+    q1, kc, ks, vc, vs, p, lens = _case(rng, B=2, Hq=4, Hkv=2, T=20, lens=[20, 9])
+    # one query token is a decode step
+    one = oracle.multi_token_attention(q1[:, None], kc, ks, vc, vs, p, lens)
+    np.testing.assert_array_equal(one[:, 0], oracle.decode_attention(q1, kc, ks, vc, vs, p, lens))
+    # a token never sees later positions: changing them leaves it unchanged
+    Q = 3
+    q = rng.standard_normal((2, Q, 4, 128))
+    base = oracle.multi_token_attention(q, kc, ks, vc, vs, p, lens)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[0, :, 19] = 7 - kc2[0, :, 19]                 # the last position: only the last token sees it
+    vc2[0, :, 19] = 7 - vc2[0, :, 19]
+    moved = oracle.multi_token_attention(q, kc2, ks, vc2, vs, p, lens)
+    np.testing.assert_array_equal(moved[0, :Q - 1], base[0, :Q - 1])
+    assert not np.allclose(moved[0, Q - 1], base[0, Q - 1])
+    # positions below zero (a sequence shorter than Q) see nothing
+    short = oracle.multi_token_attention(q, kc, ks, vc, vs, p, np.array([2, 9]))
+    assert np.all(short[0, 0] == 0) and np.any(short[0, 1] != 0)
