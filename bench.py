@@ -241,6 +241,28 @@ def main():
               "eager_ms": t_eager1 * 1e3}
     log("single-layer decode %.1f us from graph replays (%.1f us eager)" % (t_decode1 * 1e6, t_eager1 * 1e6))
 
+    # ---------------- several query tokens per sequence on the same 48-layer cache ----------------
+    multi = {}
+    if not args.no_other_shapes:
+        for Qm in (4, 16):
+            qm = bf16(W.multi_token_queries(L, Qm, HQ))
+            outm = torch.empty((L, Qm, HQ, D), dtype=torch.float32, device=dev)
+            wsm = torch.empty(iq.decode_workspace_bytes(L * Qm, HQ, HKV, T), dtype=torch.uint8, device=dev)
+
+            def dec_m():
+                iq.decode_attention_multi(qm, kc, ks, vc, vs, rot, seq_lens=lens, out=outm, workspace=wsm)
+
+            for _ in range(20):
+                dec_m()
+            t_m = time_calls(dec_m, max(20, args.steps // 8), stream)
+            flops = 2 * 2 * L * Qm * HQ * T * D       # QK and PV multiply-adds, causal tail ignored
+            multi["q%d" % Qm] = {"query_tokens": Qm, "ms": t_m * 1e3, "kv_tokens_per_s": L * T / t_m,
+                                 "query_token_kv_per_s": L * T * Qm / t_m,
+                                 "GBs_packed_cache": decode_bytes / t_m / 1e9, "TFLOPs": flops / t_m / 1e12}
+            log("multi-token decode Q=%d: %.1f us, %.0f GB/s of packed cache, %.1f TFLOP/s" %
+                (Qm, t_m * 1e6, decode_bytes / t_m / 1e9, flops / t_m / 1e12))
+            del qm, outm, wsm
+
     # ---------------- the other decode shapes: GQA at 8K and the ragged batch ----------------
     others = {}
     iso_quality = {}
@@ -387,6 +409,8 @@ def main():
         "append_alone_ms": t_append * 1e3,
         "single_layer_decode": single,
         "other_decode_shapes": others,
+        "multi_token_decode": {"workload": "long32k x48 layers, the last Q positions as Q query tokens "
+                                           "(causal), per layer 32 query / 4 KV heads", "by_tokens": multi},
         "prefill_quantize": prefill,
         "isotropy": None if args.no_isotropy else {
             "timing": {"workload": "K of prefill 48x4x32768 bf16 Student-t(3), stats per (layer, head)",

@@ -143,13 +143,15 @@ extern "C" int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, i
   return iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap).workspace_bytes;
 }
 
-extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t* k_codes, const float* k_scales,
-                                   const uint8_t* v_codes, const float* v_scales, const float* rot,
-                                   int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch,
-                                   int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap, float sm_scale,
-                                   float* out, void* workspace, int64_t workspace_bytes, int32_t head_dim,
-                                   int32_t bits, void* stream) {
-  static const char* fn = "iq_decode_attention";
+namespace {
+
+// iq_decode_attention (q_tokens = 1) and iq_decode_attention_multi: the batch's q_tokens query
+// tokens per sequence run as batch * q_tokens sequences of the kernels that share their cache.
+int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens, const uint8_t* k_codes,
+                const float* k_scales, const uint8_t* v_codes, const float* v_scales, const float* rot,
+                int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out, void* workspace,
+                int64_t workspace_bytes, int32_t head_dim, int32_t bits, void* stream) {
   iq::clear_error();
   int rc = check_dims(fn, head_dim, bits);
   if (rc) return rc;
@@ -157,7 +159,11 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
     iq::set_error("%s: unknown q_dtype %d", fn, q_dtype);
     return IQ_EUNSUPPORTED;
   }
-  rc = check_decode_sizes(fn, batch, n_q_heads, n_kv_heads, cache_cap);
+  if (q_tokens < 1 || q_tokens > 65535 || (int64_t)batch * q_tokens > 65535) {
+    iq::set_error("%s: need 1 <= n_q_tokens and batch * n_q_tokens <= 65535", fn);
+    return IQ_EINVAL;
+  }
+  rc = check_decode_sizes(fn, batch * q_tokens, n_q_heads, n_kv_heads, cache_cap);
   if (rc) return rc;
   if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !rot || !out) {
     iq::set_error("%s: a required pointer is NULL", fn);
@@ -173,7 +179,7 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
     iq::set_error("%s: misaligned pointer", fn);
     return IQ_EINVAL;
   }
-  const iq::DecodeGeometry geo = iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap);
+  const iq::DecodeGeometry geo = iq::decode_geometry(batch * q_tokens, n_q_heads, n_kv_heads, cache_cap);
   if (!workspace || workspace_bytes < geo.workspace_bytes || !aligned(workspace, 256)) {
     iq::set_error("%s: workspace must be 256-byte aligned and hold %lld bytes (got %lld)", fn,
                   (long long)geo.workspace_bytes, (long long)workspace_bytes);
@@ -190,6 +196,7 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
   a.rot_stride_batch = rot_stride_batch;
   a.seq_lens = seq_lens;
   a.batch = batch;
+  a.q_tokens = q_tokens;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
   a.cache_cap = cache_cap;
@@ -202,6 +209,31 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
     return IQ_EHIP;
   }
   return IQ_OK;
+}
+
+}  // namespace
+
+extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t* k_codes, const float* k_scales,
+                                   const uint8_t* v_codes, const float* v_scales, const float* rot,
+                                   int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch,
+                                   int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap, float sm_scale,
+                                   float* out, void* workspace, int64_t workspace_bytes, int32_t head_dim,
+                                   int32_t bits, void* stream) {
+  return decode_impl("iq_decode_attention", q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot,
+                     rot_stride_batch, seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace,
+                     workspace_bytes, head_dim, bits, stream);
+}
+
+extern "C" int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t n_q_tokens,
+                                         const uint8_t* k_codes, const float* k_scales, const uint8_t* v_codes,
+                                         const float* v_scales, const float* rot, int64_t rot_stride_batch,
+                                         const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out,
+                                         void* workspace, int64_t workspace_bytes, int32_t head_dim, int32_t bits,
+                                         void* stream) {
+  return decode_impl("iq_decode_attention_multi", q, q_dtype, n_q_tokens, k_codes, k_scales, v_codes, v_scales, rot,
+                     rot_stride_batch, seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace,
+                     workspace_bytes, head_dim, bits, stream);
 }
 
 extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,
@@ -257,6 +289,7 @@ extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const 
   a.rot_stride_batch = rot_stride_batch;
   a.seq_lens = nullptr;
   a.batch = batch;
+  a.q_tokens = 1;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
   a.cache_cap = cache_cap;

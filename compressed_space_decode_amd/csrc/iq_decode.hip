@@ -123,7 +123,8 @@ struct DecodeKArgs {
   const float* rot;
   int64_t rot_stride_b;
   const int32_t* seq_lens;
-  int batch, Hq, Hkv, G, head_groups;
+  int batch, Hq, Hkv, G, head_groups;   // batch: sequences times query tokens (work-item sequences)
+  int q_tokens;           // query tokens per cached sequence; sequence b reads cache b / q_tokens
   int64_t cap;
   int target;             // most (sequence, chunk) pairs per (KV head, head group) column
   float sm_log2;          // softmax scale times log2(e)
@@ -148,18 +149,25 @@ struct LenSource {
   const int32_t* positions;   // fused append: length = position + 1 (0 outside the cache)
   const int32_t* seq_lens;    // else the given lengths clamped to [0, cap]; NULL: every length cap
   int cap, batch;
+  int q_tokens;               // several query tokens per cached sequence: sequence i is token
+                              // i % q_tokens of cache i / q_tokens and sees len - q_tokens + i % q_tokens + 1
 };
 
 // The stored value for sequence i (a position or a length; 0 when there is none), then its length.
 __device__ __forceinline__ int len_raw(const LenSource& s, int i) {
   const int32_t* src = s.positions ? s.positions : s.seq_lens;
-  return (src != nullptr && i < s.batch) ? src[i] : 0;
+  if (src == nullptr || i >= s.batch) return 0;
+  return src[s.q_tokens > 1 ? i / s.q_tokens : i];
 }
 __device__ __forceinline__ int len_of(const LenSource& s, int i, int raw) {
   if (i >= s.batch) return 0;
   if (s.positions) return (raw >= 0 && raw < s.cap) ? raw + 1 : 0;
-  if (s.seq_lens) return raw < 0 ? 0 : (raw > s.cap ? s.cap : raw);
-  return s.cap;
+  int l = s.seq_lens ? (raw < 0 ? 0 : (raw > s.cap ? s.cap : raw)) : s.cap;
+  if (s.q_tokens > 1) {
+    l -= s.q_tokens - 1 - i % s.q_tokens;       // causal: the last q_tokens positions are the queries
+    if (l < 0) l = 0;
+  }
+  return l;
 }
 __device__ __forceinline__ int len_at(const LenSource& s, int i) { return len_of(s, i, len_raw(s, i)); }
 
@@ -604,6 +612,7 @@ struct SetupLoads {
 __device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, int g, int h0, int nh, int lane) {
   SetupLoads v;
   const int qi = lane >> 3, qe = lane & 7;
+  const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;          // the cache (and rotation) of sequence b
   const int64_t off = ((int64_t)b * a.Hq + h0 + (qi < nh ? qi : 0)) * 128 + 16 * qe;
   if (a.q_bf16) {
     const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
@@ -617,7 +626,7 @@ __device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, in
     v.q2 = qp[2];
     v.q3 = qp[3];
   }
-  const float* rq = a.rot + b * a.rot_stride_b + (int64_t)g * 256 + (lane & 31) * 8;
+  const float* rq = a.rot + bc * a.rot_stride_b + (int64_t)g * 256 + (lane & 31) * 8;
   v.r0 = make_float4(rq[0], rq[1], rq[2], rq[3]);
   v.r1 = make_float4(rq[4], rq[5], rq[6], rq[7]);
   return v;
@@ -646,7 +655,7 @@ void decode_split_kernel(DecodeKArgs a) {
   // says otherwise: the query and rotation loads then overlap the plan.
   // (the lengths are loaded first: memory loads complete in order, so the plan then waits for
   // them alone)
-  const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch};
+  const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch, a.q_tokens};
   const int raw0 = len_raw(src, lane);                       // sequences 0..63
   int b_guess = x / a.guess_per_seq;
   if (b_guess > a.batch - 1) b_guess = a.batch - 1;
@@ -669,8 +678,9 @@ void decode_split_kernel(DecodeKArgs a) {
   const int tok0 = plan.j * plan.chunk;
   if (tok0 >= len) return;                                   // uniform; never taken
   const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
-  const int64_t kv = (int64_t)b * a.Hkv + g;
-  const float* rot = a.rot + b * a.rot_stride_b + (int64_t)g * 256;
+  const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;        // cache of sequence b (uniform)
+  const int64_t kv = (int64_t)bc * a.Hkv + g;
+  const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
 
   CacheBuffers cb;
   cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
@@ -925,6 +935,7 @@ struct CombineArgs {
   const int32_t* seq_lens;
   const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
   int Hq, G;
+  int q_tokens;                 // as in the split kernel
   int64_t cap;
   int x_max;                    // partial rows per query head
   float* out;
@@ -944,7 +955,8 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   // used only when the sequence has tokens, and then the split kernel wrote them)
   const int chunk = a.plan[0];
   const int x0 = a.plan[64 + b];
-  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq}, b);
+  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, a.q_tokens}, b);
+  const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;
   float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
   if (len == 0) {                       // an empty sequence attends to nothing
     outp[tid] = 0.f;
@@ -969,7 +981,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     for (int m = 1; m < 64; m <<= 1) L += wave_xor(L, m);
     if (lane == 0) inv_l = 1.f / L;
   } else if (lane < 32) {               // the SO(4) blocks of this head's KV head
-    build_block(a.rot + b * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
+    build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
   }
   __syncthreads();
   {
@@ -1093,8 +1105,10 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.vs = a.v_scales;
   k.rot = a.rot;
   k.rot_stride_b = a.rot_stride_batch;
+  const int vb = a.batch * a.q_tokens;           // work-item sequences
   k.seq_lens = a.seq_lens;
-  k.batch = a.batch;
+  k.batch = vb;
+  k.q_tokens = a.q_tokens;
   k.Hq = a.n_q_heads;
   k.Hkv = a.n_kv_heads;
   k.G = G;
@@ -1131,10 +1145,11 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.positions = a.positions;
   c.Hq = a.n_q_heads;
   c.G = G;
+  c.q_tokens = a.q_tokens;
   c.cap = a.cache_cap;
   c.x_max = geo.x_max;
   c.out = a.out;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(a.batch * a.n_q_heads)), dim3(128), 0, stream, c);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(vb * a.n_q_heads)), dim3(128), 0, stream, c);
   return hipGetLastError();
 }
 

@@ -61,6 +61,7 @@ struct DecodeLaunch {
   int64_t rot_stride_batch;
   const int32_t* seq_lens;
   int batch, n_q_heads, n_kv_heads;
+  int q_tokens;          // query tokens per sequence (q, out: [batch][q_tokens][n_q_heads][128])
   int64_t cache_cap;
   float sm_scale;
   float* out;

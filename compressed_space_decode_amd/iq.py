@@ -33,6 +33,8 @@ SIGNATURES = {
     "iq_decode_attention_append": (ctypes.c_int, [_P, _I32, _P, _P, _I32, _I64, _I64, _P, _P, _P, _P, _P, _P,
                                                   _I64, _I32, _I32, _I32, _I64, _F, _P, _P, _I64, _I32, _I32,
                                                   _P]),
+    "iq_decode_attention_multi": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                                 _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
     "iq_isotropy_workspace_bytes": (_I64, [_I64, _I32, _I64]),
     "iq_isotropy_stats": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64,
                                          _P, _P, _I64, _P]),
@@ -174,6 +176,41 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         HEAD_DIM, BITS, _stream(q))
+    _check(rc)
+    return out
+
+
+def decode_attention_multi(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None, sm_scale=0.0,
+                           out=None, workspace=None, shared_rot=False):
+    """Attention of Q new query tokens per sequence: q [B][Q][Hq][128] (cuda f32/bf16,
+    contiguous); the new tokens are the last Q of each sequence's seq_lens cached positions and
+    token i attends causally up to its own position.  Other arguments as decode_attention; the
+    workspace size is decode_workspace_bytes(B * Q, ...).  Returns out float32 [B][Q][Hq][128]."""
+    import torch
+    B, Q, Hq, d = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    if d != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B][Q][Hq][128]")
+    for t in (k_codes, k_scales, v_codes, v_scales, rot):
+        if not t.is_contiguous():
+            raise ValueError("cache and rotation tensors must be contiguous")
+    for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
+        if tuple(c.shape) != (B, Hkv, cap, RECORD_BYTES) or tuple(sc.shape) != (B, Hkv, cap):
+            raise ValueError("caches must be [B][Hkv][cap][48] codes and [B][Hkv][cap] scales")
+    if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
+        raise ValueError("rot has the wrong number of values")
+    if seq_lens is not None and (seq_lens.numel() != B or seq_lens.dtype != torch.int32
+                                 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be a contiguous int32 tensor with one length per sequence")
+    if out is None:
+        out = torch.empty((B, Q, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(decode_workspace_bytes(B * Q, Hq, Hkv, cap), dtype=torch.uint8, device=q.device)
+    rc = lib().iq_decode_attention_multi(
+        q.data_ptr(), _dtype_code(q), Q, k_codes.data_ptr(), k_scales.data_ptr(),
+        v_codes.data_ptr(), v_scales.data_ptr(), rot.data_ptr(), 0 if shared_rot else Hkv * ROT_PARAMS,
+        seq_lens.data_ptr() if seq_lens is not None else None, B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), HEAD_DIM, BITS, _stream(q))
     _check(rc)
     return out
 

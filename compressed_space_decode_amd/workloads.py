@@ -70,6 +70,13 @@ def dense_rotations(seed, n):
     return (q * np.sign(np.diagonal(r, axis1=-2, axis2=-1))[:, None, :]).astype(np.float32)
 
 
+def multi_token_queries(n_seq, n_tokens, n_q_heads):
+    """bf16 bits [n_seq][n_tokens][n_q_heads][128]: N(0,1) queries of several new tokens per
+    sequence, drawn from SeedSequence([7, n_tokens])."""
+    rng = np.random.default_rng(np.random.SeedSequence([7, int(n_tokens)]))
+    return f32_to_bf16_bits(rng.standard_normal((n_seq, n_tokens, n_q_heads, D), dtype=np.float32))
+
+
 def _as_dtype(x, dtype):
     if dtype == "bf16":
         return f32_to_bf16_bits(x)

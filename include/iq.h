@@ -168,6 +168,37 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
                         int32_t head_dim, int32_t bits, void* stream);
 
 /*
+ * iq_decode_attention_multi -- attention of n_q_tokens new query tokens per
+ * sequence on the packed cache (chunked prefill, or checking several drafted
+ * tokens at once).  Source: Abstract (attention computed on the packed 3-bit
+ * tensors); several query tokens per step is this library's extension.
+ *   q, out       [batch][n_q_tokens][n_q_heads][128] (q as in
+ *                iq_decode_attention; out float).
+ *   seq_lens     as in iq_decode_attention: the cached tokens of sequence b,
+ *                including its n_q_tokens new ones, which are the last
+ *                n_q_tokens positions (written to the cache beforehand, e.g.
+ *                by iq_quantize_kv).  NULL means cache_cap.
+ *   Query token i of sequence b sits at position L - n_q_tokens + i
+ *   (L = seq_lens[b]) and attends to positions 0 .. L - n_q_tokens + i
+ *   (causal); a token whose position is below 0 gets zeros.
+ *   workspace    at least iq_decode_workspace_bytes(batch * n_q_tokens,
+ *                n_q_heads, n_kv_heads, cache_cap) bytes, 256-byte aligned.
+ *   Other arguments as in iq_decode_attention; n_q_tokens = 1 is exactly
+ *   iq_decode_attention.
+ * Errors: as iq_decode_attention; IQ_EINVAL also for n_q_tokens < 1 or
+ * batch * n_q_tokens > 65535.
+ */
+int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t n_q_tokens,
+                              const uint8_t* k_codes, const float* k_scales,
+                              const uint8_t* v_codes, const float* v_scales,
+                              const float* rot, int64_t rot_stride_batch,
+                              const int32_t* seq_lens,
+                              int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                              int64_t cache_cap, float sm_scale, float* out,
+                              void* workspace, int64_t workspace_bytes,
+                              int32_t head_dim, int32_t bits, void* stream);
+
+/*
  * iq_decode_attention_append -- one decode step with the step's new token
  * appended in the same launch.  Source: Abstract (quantised KV written as
  * packed 3-bit tensors, attention computed on them).  For every sequence b

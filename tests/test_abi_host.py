@@ -26,7 +26,8 @@ def _declared():
 def test_header_declares_the_boundary():
     assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
                                   "iq_decode_workspace_bytes", "iq_decode_attention",
-                                  "iq_decode_attention_append", "iq_isotropy_workspace_bytes",
+                                  "iq_decode_attention_append", "iq_decode_attention_multi",
+                                  "iq_isotropy_workspace_bytes",
                                   "iq_isotropy_stats"])
 
 
@@ -205,3 +206,33 @@ def test_isotropy_workspace_bytes():
     assert n == 2 * 3 * (128 + 4 * (4 * 128 + 8)) * 4 + 256
     assert iq.isotropy_workspace_bytes(1, 1, 0) == 128 * 4 + 256
     assert iq.lib().iq_isotropy_workspace_bytes(0, 1, 10) == binding.IQ_EINVAL
+
+
+def _multi(**kw):
+    args = dict(q=FAKE, qd=1, Q=4, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, rot=FAKE, rs=0, lens=None, B=2, Hq=8, Hkv=2,
+                cap=1000, sm=0.0, out=FAKE, ws=FAKE, wsb=16, hd=128, bits=3)
+    args.update(kw)
+    return iq.lib().iq_decode_attention_multi(
+        args["q"], args["qd"], args["Q"], args["kc"], args["ks"], args["vc"], args["vs"], args["rot"], args["rs"],
+        args["lens"], args["B"], args["Hq"], args["Hkv"], args["cap"], args["sm"], args["out"], args["ws"],
+        args["wsb"], args["hd"], args["bits"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(), binding.IQ_EWORKSPACE),             # everything valid but the 16-byte workspace
+    (dict(Q=0), binding.IQ_EINVAL),
+    (dict(B=20000, Q=4), binding.IQ_EINVAL),      # batch * n_q_tokens > 65535
+    (dict(qd=5), binding.IQ_EUNSUPPORTED),
+    (dict(hd=64), binding.IQ_EUNSUPPORTED),
+    (dict(q=None), binding.IQ_EINVAL),
+    (dict(Hq=6, Hkv=4), binding.IQ_EINVAL),
+    (dict(q=FAKE + 4), binding.IQ_EINVAL),
+])
+def test_decode_multi_validation(kw, code):
+    assert _multi(**kw) == code
+    assert binding.last_error().startswith("iq_decode_attention_multi")
+
+
+def test_decode_multi_workspace_is_that_of_batch_times_tokens():
+    need = iq.decode_workspace_bytes(2 * 4, 8, 2, 1000)
+    assert _multi(wsb=need - 1) == binding.IQ_EWORKSPACE
