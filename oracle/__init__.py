@@ -18,6 +18,9 @@ docstring).  Parity status of each function:
     make_rotation: pinned by
     tests/test_oracle_*.py (closed forms, textbook identities, brute force,
     hand-derived golden bytes, published generator test vectors).
+  * formats (2- and 4-bit uniform and Lloyd-Max 3-bit quantizers, generic
+    packing, attention on them): pinned by tests/test_oracle_formats.py
+    (hand-derived records, brute force, Max's published tables).
   * diagnostics.isotropy_stats (the isotropy measures of the rotation and
     its variants): pinned by tests/test_oracle_diagnostics.py (closed-form
     kurtosis values, a hand-worked quantization error, independent
@@ -32,5 +35,5 @@ from .isoquant import (  # noqa: F401
     block_matrix, rotation_matrix, rotate, quantize, dequantize_rotated,
     pack, unpack, decode_attention, multi_token_attention, dense_attention_on_dequantized,
 )
-from . import diagnostics  # noqa: F401
+from . import diagnostics, formats  # noqa: F401
 from .rotation_gen import splitmix64, make_rotation  # noqa: F401
