@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-other-shapes", action="store_true", help="skip the gqa8k and ragged decode timings")
     ap.add_argument("--no-isotropy", action="store_true", help="skip the isotropy diagnostics")
+    ap.add_argument("--no-formats", action="store_true", help="skip the 2/4-bit and Lloyd-Max record formats")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
@@ -241,6 +242,64 @@ def main():
               "eager_ms": t_eager1 * 1e3}
     log("single-layer decode %.1f us from graph replays (%.1f us eager)" % (t_decode1 * 1e6, t_eager1 * 1e6))
 
+    # ---------------- record formats: quantize + decode time and attention error per format ----------------
+    formats = {}
+    if not args.no_formats:
+        def exact_attention(qx, kx, vx):
+            """fp32 attention of qx [Hq][128] on unquantized kx, vx [Hkv][T][128] (the accuracy reference)."""
+            Gx = qx.shape[0] // kx.shape[0]
+            r = torch.empty_like(qx)
+            for g in range(kx.shape[0]):
+                s_ = (qx[g * Gx:(g + 1) * Gx] @ kx[g].t().contiguous()) / np.sqrt(D)
+                r[g * Gx:(g + 1) * Gx] = torch.softmax(s_, dim=-1) @ vx[g]
+            return r
+
+        def rel_err(a, b):
+            return float(torch.linalg.vector_norm(a - b) / torch.linalg.vector_norm(b))
+
+        ref = exact_attention(q[0].float(), k_all[0].float(), v_all[0].float())
+        # a Gaussian workload (Q, K, V ~ N(0,1), 4 heads, 512 tokens, fp32): attention spread over many tokens
+        wt = W.decode_workload("tiny")
+        kt, vt, qt = (torch.from_numpy(wt[n]).to(dev) for n in ("k", "v", "q"))
+        rott = torch.from_numpy(wt["params"]).to(dev)
+        Tt = kt.shape[2]
+        ref_t = exact_attention(qt[0], kt[0], vt[0])
+        for fmt in ("u2", "u3", "u4", "lm3"):
+            rb = 16 * iq.FORMAT_BITS[fmt]
+            kcf = torch.empty((L, HKV, T, rb), dtype=torch.uint8, device=dev)
+            vcf = torch.empty_like(kcf)
+            ksf = torch.empty((L, HKV, T), dtype=torch.float32, device=dev)
+            vsf = torch.empty_like(ksf)
+
+            def quant_f(fmt=fmt):
+                iq.quantize_kv(k_all, v_all, rot, kcf, ksf, vcf, vsf, fmt=fmt)
+
+            def dec_f(fmt=fmt):
+                iq.decode_attention(q, kcf, ksf, vcf, vsf, rot, seq_lens=lens, out=out, workspace=ws, fmt=fmt)
+
+            quant_f()
+            dec_f()
+            torch.cuda.synchronize()
+            err = rel_err(out[0], ref)
+            kct = torch.empty((1, kt.shape[1], Tt, rb), dtype=torch.uint8, device=dev)
+            vct = torch.empty_like(kct)
+            kst = torch.empty((1, kt.shape[1], Tt), dtype=torch.float32, device=dev)
+            vst = torch.empty_like(kst)
+            iq.quantize_kv(kt, vt, rott, kct, kst, vct, vst, fmt=fmt)
+            err_t = rel_err(iq.decode_attention(qt, kct, kst, vct, vst, rott, fmt=fmt)[0], ref_t)
+            del kct, vct, kst, vst
+            t_qf = time_calls(quant_f, 5, stream)
+            t_df = time_calls(dec_f, 20, stream)
+            cache_b = L * HKV * T * 2 * (rb + 4)
+            formats[fmt] = {"bits": iq.FORMAT_BITS[fmt], "record_bytes": rb,
+                            "attention_rel_error_long32k_layer0": err, "attention_rel_error_gaussian": err_t,
+                            "quantize_ms": t_qf * 1e3, "decode_ms": t_df * 1e3,
+                            "decode_GBs": cache_b / t_df / 1e9, "cache_bytes": cache_b}
+            log("format %s: attention error %.4f (long32k layer 0), %.4f (Gaussian), quantize %.2f ms, "
+                "decode %.1f us (%.0f GB/s)" % (fmt, err, err_t, t_qf * 1e3, t_df * 1e6, cache_b / t_df / 1e9))
+            del kcf, vcf, ksf, vsf
+        del ref, ref_t, kt, vt, qt
+
     # ---------------- several query tokens per sequence on the same 48-layer cache ----------------
     multi = {}
     if not args.no_other_shapes:
@@ -409,6 +468,10 @@ def main():
         "append_alone_ms": t_append * 1e3,
         "single_layer_decode": single,
         "other_decode_shapes": others,
+        "record_formats": {"workload": "long32k x48 layers: K+V quantize and decode time; relative error of the "
+                                       "attention output against fp32 attention on the unquantized K/V, for long32k "
+                                       "layer 0 (peaked scores) and for the Gaussian tiny workload",
+                           "by_format": formats},
         "multi_token_decode": {"workload": "long32k x48 layers, the last Q positions as Q query tokens "
                                            "(causal), per layer 32 query / 4 KV heads", "by_tokens": multi},
         "prefill_quantize": prefill,

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libiq.so")
-SOURCES = ["iq_api.hip", "iq_quantize.hip", "iq_decode.hip", "iq_diag.hip", "iq_rotation.cpp"]
+SOURCES = ["iq_api.hip", "iq_quantize.hip", "iq_decode.hip", "iq_diag.hip", "iq_formats.hip", "iq_rotation.cpp"]
 ARCH = "gfx950"
 
 

@@ -41,6 +41,27 @@ int check_dims(const char* fn, int32_t head_dim, int32_t bits) {
 
 extern "C" const char* iq_last_error(void) { return iq::g_err; }
 
+namespace {
+
+int check_format(const char* fn, int32_t head_dim, int32_t format) {
+  if (head_dim != IQ_HEAD_DIM) {
+    iq::set_error("%s: head_dim must be 128 (got %d)", fn, head_dim);
+    return IQ_EUNSUPPORTED;
+  }
+  if (format < IQ_FMT_U3 || format > IQ_FMT_LM3) {
+    iq::set_error("%s: unknown record format %d", fn, format);
+    return IQ_EUNSUPPORTED;
+  }
+  return IQ_OK;
+}
+
+int quantize_impl(const char* fn, const void* k, const void* v, int32_t dtype, int64_t n_seq, int32_t n_heads,
+                  int64_t n_tokens, int64_t stride_seq, int64_t stride_head, int64_t stride_tok, const float* rot,
+                  int64_t rot_stride_seq, uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                  int64_t cache_cap, int64_t tok_offset, int32_t format, void* stream);
+
+}  // namespace
+
 extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64_t n_seq, int32_t n_heads,
                               int64_t n_tokens, int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
                               const float* rot, int64_t rot_stride_seq, uint8_t* k_codes, float* k_scales,
@@ -48,8 +69,31 @@ extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64
                               int32_t head_dim, int32_t bits, void* stream) {
   static const char* fn = "iq_quantize_kv";
   iq::clear_error();
-  int rc = check_dims(fn, head_dim, bits);
+  const int rc = check_dims(fn, head_dim, bits);
   if (rc) return rc;
+  return quantize_impl(fn, k, v, dtype, n_seq, n_heads, n_tokens, stride_seq, stride_head, stride_tok, rot,
+                       rot_stride_seq, k_codes, k_scales, v_codes, v_scales, cache_cap, tok_offset, IQ_FMT_U3, stream);
+}
+
+extern "C" int iq_quantize_kv_format(const void* k, const void* v, int32_t dtype, int64_t n_seq, int32_t n_heads,
+                                     int64_t n_tokens, int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
+                                     const float* rot, int64_t rot_stride_seq, uint8_t* k_codes, float* k_scales,
+                                     uint8_t* v_codes, float* v_scales, int64_t cache_cap, int64_t tok_offset,
+                                     int32_t head_dim, int32_t format, void* stream) {
+  static const char* fn = "iq_quantize_kv_format";
+  iq::clear_error();
+  const int rc = check_format(fn, head_dim, format);
+  if (rc) return rc;
+  return quantize_impl(fn, k, v, dtype, n_seq, n_heads, n_tokens, stride_seq, stride_head, stride_tok, rot,
+                       rot_stride_seq, k_codes, k_scales, v_codes, v_scales, cache_cap, tok_offset, format, stream);
+}
+
+namespace {
+
+int quantize_impl(const char* fn, const void* k, const void* v, int32_t dtype, int64_t n_seq, int32_t n_heads,
+                  int64_t n_tokens, int64_t stride_seq, int64_t stride_head, int64_t stride_tok, const float* rot,
+                  int64_t rot_stride_seq, uint8_t* k_codes, float* k_scales, uint8_t* v_codes, float* v_scales,
+                  int64_t cache_cap, int64_t tok_offset, int32_t format, void* stream) {
   if (dtype != IQ_F32 && dtype != IQ_BF16) {
     iq::set_error("%s: unknown dtype %d", fn, dtype);
     return IQ_EUNSUPPORTED;
@@ -59,6 +103,10 @@ extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64
     return IQ_EINVAL;
   }
   if (n_tokens == 0) return IQ_OK;   // nothing to do (empty inputs may have NULL data pointers)
+  if (format == IQ_FMT_U4 && ((k && !aligned(k_codes, 8)) || (v && !aligned(v_codes, 8)))) {
+    iq::set_error("%s: 4-bit records need 8-byte aligned codes", fn);
+    return IQ_EINVAL;
+  }
   if (k == nullptr && v == nullptr) {
     iq::set_error("%s: k and v are both NULL", fn);
     return IQ_EINVAL;
@@ -100,13 +148,15 @@ extern "C" int iq_quantize_kv(const void* k, const void* v, int32_t dtype, int64
   a.rot_stride_seq = rot_stride_seq;
   a.cache_cap = cache_cap;
   a.tok_offset = tok_offset;
-  const hipError_t err = iq::launch_quantize(a, static_cast<hipStream_t>(stream));
+  const hipError_t err = iq::launch_quantize_format(a, format, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
     return IQ_EHIP;
   }
   return IQ_OK;
 }
+
+}  // namespace
 
 namespace {
 
@@ -151,10 +201,8 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
                 const float* k_scales, const uint8_t* v_codes, const float* v_scales, const float* rot,
                 int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
                 int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out, void* workspace,
-                int64_t workspace_bytes, int32_t head_dim, int32_t bits, void* stream) {
-  iq::clear_error();
-  int rc = check_dims(fn, head_dim, bits);
-  if (rc) return rc;
+                int64_t workspace_bytes, int32_t format, void* stream) {
+  int rc = IQ_OK;
   if (q_dtype != IQ_F32 && q_dtype != IQ_BF16) {
     iq::set_error("%s: unknown q_dtype %d", fn, q_dtype);
     return IQ_EUNSUPPORTED;
@@ -167,6 +215,10 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   if (rc) return rc;
   if (!q || !k_codes || !k_scales || !v_codes || !v_scales || !rot || !out) {
     iq::set_error("%s: a required pointer is NULL", fn);
+    return IQ_EINVAL;
+  }
+  if (format == IQ_FMT_U4 && (!aligned(k_codes, 8) || !aligned(v_codes, 8))) {
+    iq::set_error("%s: 4-bit records need 8-byte aligned codes", fn);
     return IQ_EINVAL;
   }
   if (rot_stride_batch < 0) {
@@ -197,6 +249,7 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   a.seq_lens = seq_lens;
   a.batch = batch;
   a.q_tokens = q_tokens;
+  a.format = format;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = n_kv_heads;
   a.cache_cap = cache_cap;
@@ -219,9 +272,26 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
                                    int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap, float sm_scale,
                                    float* out, void* workspace, int64_t workspace_bytes, int32_t head_dim,
                                    int32_t bits, void* stream) {
-  return decode_impl("iq_decode_attention", q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot,
-                     rot_stride_batch, seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace,
-                     workspace_bytes, head_dim, bits, stream);
+  static const char* fn = "iq_decode_attention";
+  iq::clear_error();
+  const int rc = check_dims(fn, head_dim, bits);
+  if (rc) return rc;
+  return decode_impl(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens, batch,
+                     n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, IQ_FMT_U3, stream);
+}
+
+extern "C" int iq_decode_attention_format(const void* q, int32_t q_dtype, const uint8_t* k_codes,
+                                          const float* k_scales, const uint8_t* v_codes, const float* v_scales,
+                                          const float* rot, int64_t rot_stride_batch, const int32_t* seq_lens,
+                                          int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap,
+                                          float sm_scale, float* out, void* workspace, int64_t workspace_bytes,
+                                          int32_t head_dim, int32_t format, void* stream) {
+  static const char* fn = "iq_decode_attention_format";
+  iq::clear_error();
+  const int rc = check_format(fn, head_dim, format);
+  if (rc) return rc;
+  return decode_impl(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens, batch,
+                     n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, format, stream);
 }
 
 extern "C" int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t n_q_tokens,
@@ -231,9 +301,13 @@ extern "C" int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t
                                          int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out,
                                          void* workspace, int64_t workspace_bytes, int32_t head_dim, int32_t bits,
                                          void* stream) {
-  return decode_impl("iq_decode_attention_multi", q, q_dtype, n_q_tokens, k_codes, k_scales, v_codes, v_scales, rot,
-                     rot_stride_batch, seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace,
-                     workspace_bytes, head_dim, bits, stream);
+  static const char* fn = "iq_decode_attention_multi";
+  iq::clear_error();
+  const int rc = check_dims(fn, head_dim, bits);
+  if (rc) return rc;
+  return decode_impl(fn, q, q_dtype, n_q_tokens, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch,
+                     seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes,
+                     IQ_FMT_U3, stream);
 }
 
 extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,

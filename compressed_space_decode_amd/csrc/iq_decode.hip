@@ -45,6 +45,7 @@
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
 // blocks followed by the Hadamard transform).
+#include "iq.h"
 #include "iq_internal.h"
 #include "iq_vector.h"
 
@@ -926,6 +927,193 @@ void decode_split_kernel(DecodeKArgs a) {
   }
 }
 
+// ---------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit) ----------------
+// The same split of the context and the same partials as decode_split_kernel, computed on the
+// vector units: lanes are (token slot = lane / 8, coordinates 16e..16e+15 with e = lane % 8), every
+// wave walks all tokens of the chunk eight at a time and owns query heads 2*wave and 2*wave + 1 of
+// the group.  The rotated queries (times the softmax scale and log2 e) sit in LDS; each token
+// slot keeps its own online softmax, and the eight slots merge at the end.
+// The record bytes of this lane's 16 coordinates (2b bytes at 2b*e): 2 bits in .x; 3 bits in the
+// aligned words around bytes 6e..6e+5; 4 bits in .x (coordinates 16e..16e+7) and .y.
+template <int kFmt>
+__device__ __forceinline__ uint2 format_raw(const uint8_t* rec, int e) {
+  if constexpr (kFmt == IQ_FMT_U2) {
+    return make_uint2(reinterpret_cast<const unsigned*>(rec)[e], 0u);
+  } else if constexpr (kFmt == IQ_FMT_U4) {
+    return reinterpret_cast<const uint2*>(rec)[e];
+  } else {
+    const unsigned* wp = reinterpret_cast<const unsigned*>(rec + ((6 * e) & ~3));
+    return make_uint2(wp[0], wp[1]);
+  }
+}
+
+// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform) or the
+// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]).
+template <int kFmt>
+__device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
+  if constexpr (kFmt == IQ_FMT_U2) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = (float)((raw.x >> (2 * i)) & 3u) - 1.5f;
+  } else if constexpr (kFmt == IQ_FMT_U4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[i] = (float)((raw.x >> (4 * i)) & 15u) - 7.5f;
+      v[8 + i] = (float)((raw.y >> (4 * i)) & 15u) - 7.5f;
+    }
+  } else {
+    const unsigned sh = 8 * ((6 * e) & 3);                 // 0 or 16
+    const unsigned lo = sh ? __builtin_amdgcn_alignbit(raw.y, raw.x, 16) : raw.x;   // bits 0..31 of the 48
+    const unsigned hi = sh ? (raw.y >> 16) : raw.y;                                   // bits 32..47
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
+                       : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
+                       : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
+      const unsigned mi = c >= 4u ? c - 4u : 3u - c;
+      const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
+      v[i] = c >= 4u ? mag : -mag;
+    }
+  }
+}
+
+template <int kFmt>
+__global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) {
+  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);
+  __shared__ float fold[32][16];
+  __shared__ __attribute__((aligned(16))) float qs[8][128];
+  const int x = blockIdx.y;
+  const int g = blockIdx.x / a.head_groups;
+  const int hg = blockIdx.x % a.head_groups;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = lane & 7, slot = lane >> 3;
+  const int cap = (int)a.cap;
+  const int h0 = g * a.G + hg * 8;
+  const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
+  const LenSource src{nullptr, a.seq_lens, cap, a.batch, a.q_tokens};
+  const ChunkPlan plan = plan_chunks(src, len_at(src, lane), a.target, x, lane);
+  if (plan.b < 0) return;                                    // uniform
+  const int b = plan.b, len = plan.len;
+  if (tid == 0 && blockIdx.x == 0) {
+    if (x == 0) a.plan[0] = plan.chunk;
+    if (plan.j == 0) a.plan[64 + b] = x;
+  }
+  const int tok0 = plan.j * plan.chunk;
+  if (tok0 >= len) return;
+  const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
+  const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;
+  const int64_t kv = (int64_t)bc * a.Hkv + g;
+  const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
+
+  // set-up: the group's queries rotated by the same lane-parallel transform as the quantizer
+  if (tid < 32) vec::build_folded_block(rot + tid * 8, fold[tid]);
+  __syncthreads();
+  if (wave == 0) {
+    float F[4][16];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) F[j][i] = fold[4 * e + j][i];
+    const int qi = slot;
+    const bool have = qi < nh;
+    const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * e;
+    float xq[16], y[16];
+    if (a.q_bf16)
+      vec::load16<true>(a.q, off, true, xq);
+    else
+      vec::load16<false>(a.q, off, true, xq);
+    vec::rotate8(xq, F, e, y);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qs[qi][16 * e + i] = have ? y[i] * a.sm_log2 : 0.f;
+  }
+  __syncthreads();
+
+  const uint8_t* kc = a.kc + kv * a.cap * kRec;
+  const uint8_t* vc = a.vc + kv * a.cap * kRec;
+  const float* ksc = a.ks + kv * a.cap;
+  const float* vsc = a.vs + kv * a.cap;
+  const int nj = min(2, max(0, nh - 2 * wave));          // heads of this wave (uniform)
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][16];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
+  if (nj > 0) {
+    // the next token's record words and scales are loaded one iteration ahead
+    int t = tok0 + slot;
+    const int tl = t < tok_end ? t : tok0;                 // an in-range token for idle slots
+    uint2 rk = format_raw<kFmt>(kc + (int64_t)tl * kRec, e), rv = format_raw<kFmt>(vc + (int64_t)tl * kRec, e);
+    float sk = ksc[tl], sv = vsc[tl];
+    for (; t < tok_end; t += 8) {
+      const int tn = t + 8 < tok_end ? t + 8 : t;
+      const uint2 nk = format_raw<kFmt>(kc + (int64_t)tn * kRec, e), nv = format_raw<kFmt>(vc + (int64_t)tn * kRec, e);
+      const float nsk = ksc[tn], nsv = vsc[tn];
+      float kvv[16], vvv[16];
+      format_values<kFmt>(rk, e, kvv);
+      format_values<kFmt>(rv, e, vvv);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (j < nj) {
+          const float4* qp = reinterpret_cast<const float4*>(&qs[2 * wave + j][16 * e]);
+          float dot = 0.f;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 qv = qp[q4];
+            dot = fmaf(qv.x, kvv[4 * q4], dot);
+            dot = fmaf(qv.y, kvv[4 * q4 + 1], dot);
+            dot = fmaf(qv.z, kvv[4 * q4 + 2], dot);
+            dot = fmaf(qv.w, kvv[4 * q4 + 3], dot);
+          }
+          dot += dpp_xor1(dot);
+          dot += dpp_xor2(dot);
+          dot += swz_xor4(dot);
+          const float z = dot * sk;                       // score in log2 units
+          const float mn = fmaxf(m[j], z);
+          const float f = __builtin_amdgcn_exp2f(m[j] - mn);
+          const float p = __builtin_amdgcn_exp2f(z - mn);
+          l[j] = fmaf(l[j], f, p);
+          const float pv = p * sv;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[j][i] = fmaf(o[j][i], f, pv * vvv[i]);
+          m[j] = mn;
+        }
+      }
+      rk = nk;
+      rv = nv;
+      sk = nsk;
+      sv = nsv;
+    }
+  }
+  // merge the eight token slots (lanes e, e+8, ..., e+56), write this wave's heads
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j >= nj) continue;                                 // uniform
+    float M = m[j];
+#pragma unroll
+    for (int d = 8; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
+    const float f = m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
+    float L = l[j] * f;
+#pragma unroll
+    for (int d = 8; d < 64; d <<= 1) L += __shfl_xor(L, d, 64);
+    float ov[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ov[i] = o[j][i] * f;
+#pragma unroll
+      for (int d = 8; d < 64; d <<= 1) ov[i] += __shfl_xor(ov[i], d, 64);
+    }
+    if (slot == 0) {
+      const int64_t pidx = (int64_t)(h0 + 2 * wave + j) * a.x_max + x;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) a.part_o[pidx * 128 + 16 * e + i] = ov[i];
+      if (e == 0) {
+        a.part_ml[pidx * 2] = M;
+        a.part_ml[pidx * 2 + 1] = L;
+      }
+    }
+  }
+}
+
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
@@ -1128,7 +1316,13 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_stride_seq = a.new_stride_seq;
   k.new_stride_head = a.new_stride_head;
   const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)geo.x_max, 1u);
-  if (a.positions)
+  if (a.format == IQ_FMT_U2)
+    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_U2>, grid1, dim3(kThreads), 0, stream, k);
+  else if (a.format == IQ_FMT_U4)
+    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_U4>, grid1, dim3(kThreads), 0, stream, k);
+  else if (a.format == IQ_FMT_LM3)
+    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_LM3>, grid1, dim3(kThreads), 0, stream, k);
+  else if (a.positions)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
   else
     hipLaunchKernelGGL(decode_split_kernel<false>, grid1, dim3(kThreads), 0, stream, k);

@@ -1,0 +1,168 @@
+// Quantizer variants with the same rotation: 2- and 4-bit uniform codes and
+// the 8-level Lloyd-Max codebook with an RMS scale.
+//
+// Method: "RotaryQuant: Fitting 120B MoE Models on Consumer Hardware via Fused
+// Compressed-Space Attention" (arXiv 2608.08081), Abstract: Walsh-Hadamard
+// transform and block-diagonal SO(4) rotation, then scalar quantization of
+// every coordinate with one scale per vector, stored packed.  The pages use
+// 3 bits; these formats change only the scalar quantizer:
+//   IQ_FMT_U2, IQ_FMT_U4  uniform mid-rise, 2^b levels, s = max|x'| / (2^(b-1) - 1/2),
+//                         code = clamp(floor(x'/s + 2^(b-1)), 0, 2^b - 1);
+//   IQ_FMT_LM3            the Lloyd-Max levels of a unit Gaussian as J. Max printed them
+//                         (+-0.2451, +-0.7560, +-1.344, +-2.152), scaled by the RMS
+//                         sigma = |x'| / sqrt(128); the code of the nearest level (ties up).
+// Records: one little-endian bit stream of b bits per code, 16 b bytes.
+//
+// Work split as in the 3-bit quantize kernel: 8 lanes per vector, lane e holds
+// coordinates 16e..16e+15, i.e. the 2b bytes 2b*e .. 2b*e + 2b - 1 of the record.
+#include "iq.h"
+#include "iq_internal.h"
+#include "iq_vector.h"
+
+namespace iq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerStep = kThreads / 8;
+constexpr int kTokPerGroup = 256;
+
+// Max's 8 levels, ascending, and the midpoints between consecutive levels.
+constexpr float kLM[8] = {-2.152f, -1.344f, -0.7560f, -0.2451f, 0.2451f, 0.7560f, 1.344f, 2.152f};
+
+__device__ __forceinline__ float max8(float v) {
+  v = fmaxf(v, vec::dpp_xor1(v));
+  v = fmaxf(v, vec::dpp_xor2(v));
+  return fmaxf(v, vec::swz_xor4(v));
+}
+__device__ __forceinline__ float sum8(float v) {
+  v += vec::dpp_xor1(v);
+  v += vec::dpp_xor2(v);
+  return v + vec::swz_xor4(v);
+}
+
+// Codes of the lane's 16 rotated values; returns the vector's scale (s or sigma).
+template <int kFmt>
+__device__ __forceinline__ float codes16(const float y[16], unsigned c[16]) {
+  if constexpr (kFmt == IQ_FMT_LM3) {
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) ss = fmaf(y[i], y[i], ss);
+    const float sigma = sqrtf(sum8(ss) * (1.f / 128.f));
+    const float r = sigma > 0.f ? 1.f / sigma : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float u = y[i] * r;
+      unsigned k = 0;
+#pragma unroll
+      for (int t = 0; t < 7; ++t) k += u >= 0.5f * (kLM[t] + kLM[t + 1]) ? 1u : 0u;
+      c[i] = sigma > 0.f ? k : 4u;
+    }
+    return sigma;
+  } else {
+    constexpr int b = kFmt == IQ_FMT_U2 ? 2 : 4;
+    constexpr float half = (float)(1 << (b - 1));
+    constexpr float top = (float)((1 << b) - 1);
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(y[i]));
+    amax = max8(amax);
+    const float rcp = amax > 0.f ? (half - 0.5f) / amax : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = (unsigned)fminf(fmaxf(floorf(fmaf(y[i], rcp, half)), 0.f), top);
+    return amax / (half - 0.5f);
+  }
+}
+
+template <bool kBF16, int kFmt>
+__global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunch a) {
+  constexpr int kBits = kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3;
+  constexpr int kRec = 16 * kBits;
+  __shared__ float mats[32][16];
+  const int s = blockIdx.z;
+  const int h = blockIdx.y;
+  const int64_t t_begin = (int64_t)blockIdx.x * kTokPerGroup;
+  const int tid = threadIdx.x;
+  if (tid < 32) vec::build_folded_block(a.rot + (int64_t)s * a.rot_stride_seq + (int64_t)h * 256 + tid * 8, mats[tid]);
+  __syncthreads();
+  const int lane = tid & 63;
+  const int e = lane & 7;
+  const int vsub = (tid >> 6) * 8 + (lane >> 3);
+  float F[4][16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) F[j][i] = mats[4 * e + j][i];
+
+  for (int step = 0; step < kTokPerGroup / kVecPerStep; ++step) {
+    const int64_t t0 = t_begin + (int64_t)step * kVecPerStep;
+    if (t0 >= a.n_tokens) break;                  // uniform over the work-group
+    const int64_t t = t0 + vsub;
+    const bool valid = t < a.n_tokens;
+#pragma unroll
+    for (int sd = 0; sd < 2; ++sd) {
+      const QuantSide side = a.side[sd];
+      if (side.src == nullptr) continue;          // uniform
+      float x[16], y[16];
+      vec::load16<kBF16>(side.src, (int64_t)s * a.stride_seq + (int64_t)h * a.stride_head + t * a.stride_tok + 16 * e,
+                         valid, x);
+      vec::rotate8(x, F, e, y);
+      unsigned c[16];
+      const float scale = codes16<kFmt>(y, c);
+      const int64_t rec = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset + t;
+      uint8_t* dst = side.codes + rec * kRec;
+      if constexpr (kBits == 2) {
+        unsigned w = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w |= c[i] << (2 * i);
+        if (valid) reinterpret_cast<unsigned*>(dst)[e] = w;
+      } else if constexpr (kBits == 4) {
+        unsigned w0 = 0, w1 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          w0 |= c[i] << (4 * i);
+          w1 |= c[8 + i] << (4 * i);
+        }
+        if (valid) reinterpret_cast<uint2*>(dst)[e] = make_uint2(w0, w1);
+      } else {
+        unsigned g0 = 0, g1 = 0, w[3];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          g0 |= c[k] << (3 * k);
+          g1 |= c[8 + k] << (3 * k);
+        }
+        vec::quarter_words(g0, g1, w);          // every lane runs it (cross-lane move)
+        if (valid && (e & 1) == 0) {
+          unsigned* q = reinterpret_cast<unsigned*>(dst + 12 * (e >> 1));
+          q[0] = w[0];
+          q[1] = w[1];
+          q[2] = w[2];
+        }
+      }
+      if (valid && e == 0) side.scales[rec] = scale;
+    }
+  }
+}
+
+template <bool kBF16>
+void launch_format(int fmt, dim3 grid, hipStream_t stream, const QuantizeLaunch& a) {
+  if (fmt == IQ_FMT_U2)
+    hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_U2>), grid, dim3(kThreads), 0, stream, a);
+  else if (fmt == IQ_FMT_U4)
+    hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_U4>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_LM3>), grid, dim3(kThreads), 0, stream, a);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_format(const QuantizeLaunch& a, int format, hipStream_t stream) {
+  if (format == IQ_FMT_U3) return launch_quantize(a, stream);
+  const dim3 grid((unsigned)((a.n_tokens + kTokPerGroup - 1) / kTokPerGroup), (unsigned)a.n_heads, (unsigned)a.n_seq);
+  if (a.bf16)
+    launch_format<true>(format, grid, stream, a);
+  else
+    launch_format<false>(format, grid, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace iq

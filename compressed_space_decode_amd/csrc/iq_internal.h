@@ -29,6 +29,8 @@ struct QuantizeLaunch {
 };
 
 hipError_t launch_quantize(const QuantizeLaunch& a, hipStream_t stream);
+// Record format IQ_FMT_* (IQ_FMT_U3 is launch_quantize).
+hipError_t launch_quantize_format(const QuantizeLaunch& a, int format, hipStream_t stream);
 
 // Isotropy statistics of one set of vectors after a transform (iq_isotropy_stats).
 struct DiagLaunch {
@@ -62,6 +64,7 @@ struct DecodeLaunch {
   const int32_t* seq_lens;
   int batch, n_q_heads, n_kv_heads;
   int q_tokens;          // query tokens per sequence (q, out: [batch][q_tokens][n_q_heads][128])
+  int format;            // record format IQ_FMT_* of the cache (IQ_FMT_U3: the fast kernels)
   int64_t cache_cap;
   float sm_scale;
   float* out;

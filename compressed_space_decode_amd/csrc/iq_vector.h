@@ -112,12 +112,10 @@ __device__ __forceinline__ void load16(const void* base, int64_t elem_off, bool 
   }
 }
 
-// Quantises one 128-vector held by 8 consecutive lanes (lane e = lane & 7 holds coordinates
-// 16e..16e+15 in x, and F holds its folded blocks 4e..4e+3).  Every lane of the wave must run
-// it (cross-lane moves).  Returns the vector's scale and this lane's two 24-bit code groups:
-// codes of coordinates 16e..16e+7 and 16e+8..16e+15, code j of a group at bits 3j..3j+2, i.e.
-// bytes 6e..6e+5 of the record (one little-endian bit stream, code i at bits 3i..3i+2).
-__device__ __forceinline__ float quantize8(float x[16], const float (&F)[4][16], int e, unsigned& g0, unsigned& g1) {
+// The rotation y = R x of one 128-vector held by 8 consecutive lanes (lane e = lane & 7 holds
+// coordinates 16e..16e+15 in x; F holds its folded blocks 4e..4e+3).  Every lane of the wave must
+// run it (cross-lane moves); x is overwritten.
+__device__ __forceinline__ void rotate8(float x[16], const float (&F)[4][16], int e, float y[16]) {
   // Cross-lane butterfly: new = partner + sg * mine gives (lower + upper) on the lower lane and
   // (lower - upper) on the upper lane.  Hadamard stages of stride 16, 32, 64 (partners e^1, ^2, ^4).
   const float sg1 = (e & 1) ? -1.f : 1.f;
@@ -145,7 +143,6 @@ __device__ __forceinline__ float quantize8(float x[16], const float (&F)[4][16],
       x[blk + i + 4] = u - v;
     }
   // Folded 4x4 blocks (stride-2/1 stages, SO(4) rotation, 1/sqrt(128)).
-  float y[16];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -156,6 +153,16 @@ __device__ __forceinline__ float quantize8(float x[16], const float (&F)[4][16],
       acc = fmaf(F[j][4 * r + 3], x[4 * j + 3], acc);
       y[4 * j + r] = acc;
     }
+}
+
+// Quantises one 128-vector held by 8 consecutive lanes (lane e = lane & 7 holds coordinates
+// 16e..16e+15 in x, and F holds its folded blocks 4e..4e+3).  Every lane of the wave must run
+// it (cross-lane moves).  Returns the vector's scale and this lane's two 24-bit code groups:
+// codes of coordinates 16e..16e+7 and 16e+8..16e+15, code j of a group at bits 3j..3j+2, i.e.
+// bytes 6e..6e+5 of the record (one little-endian bit stream, code i at bits 3i..3i+2).
+__device__ __forceinline__ float quantize8(float x[16], const float (&F)[4][16], int e, unsigned& g0, unsigned& g1) {
+  float y[16];
+  rotate8(x, F, e, y);
   // Per-vector scale: absmax over the 8 lanes of the vector.
   float amax = 0.f;
 #pragma unroll

@@ -17,6 +17,8 @@ IQ_OK, IQ_EINVAL, IQ_EUNSUPPORTED, IQ_EWORKSPACE, IQ_EHIP = 0, -1, -2, -3, -4
 IQ_F32, IQ_BF16 = 0, 1
 HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS = 128, 3, 48, 256
 TRANSFORMS = {"none": 0, "wht": 1, "so4": 2, "wht_so4": 3, "dense": 4}   # IQ_T_*
+FORMATS = {"u3": 0, "u2": 1, "u4": 2, "lm3": 3}                          # IQ_FMT_*
+FORMAT_BITS = {"u3": 3, "u2": 2, "u4": 4, "lm3": 3}
 N_STATS = 260
 
 # (name, restype, argtypes) of every entry point declared in include/iq.h
@@ -35,6 +37,10 @@ SIGNATURES = {
                                                   _P]),
     "iq_decode_attention_multi": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                                  _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
+    "iq_quantize_kv_format": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64,
+                                             _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
+    "iq_decode_attention_format": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                                  _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
     "iq_isotropy_workspace_bytes": (_I64, [_I64, _I32, _I64]),
     "iq_isotropy_stats": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _I32, _P, _I64, _P, _I64,
                                          _P, _P, _I64, _P]),
@@ -96,11 +102,12 @@ def _dtype_code(t):
     raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype)
 
 
-def quantize_kv(k, v, rot, k_codes, k_scales, v_codes, v_scales, tok_offset=0, shared_rot=False):
+def quantize_kv(k, v, rot, k_codes, k_scales, v_codes, v_scales, tok_offset=0, shared_rot=False, fmt="u3"):
     """Quantize K and/or V [n_seq][n_heads][n_tokens][128] (cuda, f32/bf16, last dim
-    contiguous) into the cache (codes uint8 [n_seq][n_heads][cap][48], scales float32
+    contiguous) into the cache (codes uint8 [n_seq][n_heads][cap][16 * bits], scales float32
     [n_seq][n_heads][cap]).  ``rot`` is float32 [n_seq][n_heads][32][8] on the device
-    (or [n_heads][32][8] with shared_rot=True).  Either k or v may be None."""
+    (or [n_heads][32][8] with shared_rot=True).  Either k or v may be None.  ``fmt`` is a
+    record format of FORMATS ("u3": the pages' 3-bit codes, iq_quantize_kv)."""
     ref = k if k is not None else v
     n_seq, n_heads, n_tokens, d = ref.shape
     if d != HEAD_DIM:
@@ -115,21 +122,25 @@ def quantize_kv(k, v, rot, k_codes, k_scales, v_codes, v_scales, tok_offset=0, s
     for c, sc, t in ((k_codes, k_scales, k), (v_codes, v_scales, v)):
         if t is None:
             continue
-        if (tuple(c.shape) != (n_seq, n_heads, cap, RECORD_BYTES) or tuple(sc.shape) != (n_seq, n_heads, cap)
+        if (tuple(c.shape) != (n_seq, n_heads, cap, 16 * FORMAT_BITS[fmt]) or tuple(sc.shape) != (n_seq, n_heads, cap)
                 or not c.is_contiguous() or not sc.is_contiguous()):
-            raise ValueError("cache must be contiguous codes [n_seq][n_heads][cap][48] and scales [n_seq][n_heads][cap]")
+            raise ValueError("cache must be contiguous codes [n_seq][n_heads][cap][%d] and scales [n_seq][n_heads][cap]"
+                             % (16 * FORMAT_BITS[fmt]))
     want_rot = (n_heads if shared_rot else n_seq * n_heads) * ROT_PARAMS
     if rot.numel() != want_rot or not rot.is_contiguous():
         raise ValueError("rot must be a contiguous float32 tensor of %d values" % want_rot)
     rot_stride = 0 if shared_rot else n_heads * ROT_PARAMS
-    rc = lib().iq_quantize_kv(
-        k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
-        _dtype_code(ref), n_seq, n_heads, n_tokens,
-        ref.stride(0), ref.stride(1), ref.stride(2),
-        rot.data_ptr(), rot_stride,
-        k_codes.data_ptr() if k is not None else None, k_scales.data_ptr() if k is not None else None,
-        v_codes.data_ptr() if v is not None else None, v_scales.data_ptr() if v is not None else None,
-        cap, int(tok_offset), HEAD_DIM, BITS, _stream(ref))
+    args = (k.data_ptr() if k is not None else None, v.data_ptr() if v is not None else None,
+            _dtype_code(ref), n_seq, n_heads, n_tokens,
+            ref.stride(0), ref.stride(1), ref.stride(2),
+            rot.data_ptr(), rot_stride,
+            k_codes.data_ptr() if k is not None else None, k_scales.data_ptr() if k is not None else None,
+            v_codes.data_ptr() if v is not None else None, v_scales.data_ptr() if v is not None else None,
+            cap, int(tok_offset), HEAD_DIM)
+    if fmt == "u3":
+        rc = lib().iq_quantize_kv(*args, BITS, _stream(ref))
+    else:
+        rc = lib().iq_quantize_kv_format(*args, FORMATS[fmt], _stream(ref))
     _check(rc)
 
 
@@ -141,7 +152,7 @@ def decode_workspace_bytes(batch, n_q_heads, n_kv_heads, cache_cap):
 
 
 def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None, sm_scale=0.0,
-                     out=None, workspace=None, shared_rot=False):
+                     out=None, workspace=None, shared_rot=False, fmt="u3"):
     """One decode step on the packed cache.  q [B][Hq][128] (cuda f32/bf16, contiguous);
     caches [B][Hkv][cap][48] / [B][Hkv][cap]; rot float32 [B][Hkv][32][8] (or [Hkv][32][8]
     with shared_rot=True); seq_lens int32 [B] on the device or None.  Returns out
@@ -155,8 +166,8 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         if not t.is_contiguous():
             raise ValueError("cache and rotation tensors must be contiguous")
     for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
-        if tuple(c.shape) != (B, Hkv, cap, RECORD_BYTES) or tuple(sc.shape) != (B, Hkv, cap):
-            raise ValueError("caches must be [B][Hkv][cap][48] codes and [B][Hkv][cap] scales")
+        if tuple(c.shape) != (B, Hkv, cap, 16 * FORMAT_BITS[fmt]) or tuple(sc.shape) != (B, Hkv, cap):
+            raise ValueError("caches must be [B][Hkv][cap][%d] codes and [B][Hkv][cap] scales" % (16 * FORMAT_BITS[fmt]))
     if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
         raise ValueError("rot has the wrong number of values")
     if seq_lens is not None and seq_lens.numel() != B:
@@ -168,14 +179,16 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if seq_lens is not None and (seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous()):
         raise ValueError("seq_lens must be a contiguous int32 tensor")
-    rc = lib().iq_decode_attention(
-        q.data_ptr(), _dtype_code(q), k_codes.data_ptr(), k_scales.data_ptr(),
-        v_codes.data_ptr(), v_scales.data_ptr(), rot.data_ptr(),
-        0 if shared_rot else Hkv * ROT_PARAMS,
-        seq_lens.data_ptr() if seq_lens is not None else None,
-        B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
-        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-        HEAD_DIM, BITS, _stream(q))
+    args = (q.data_ptr(), _dtype_code(q), k_codes.data_ptr(), k_scales.data_ptr(),
+            v_codes.data_ptr(), v_scales.data_ptr(), rot.data_ptr(),
+            0 if shared_rot else Hkv * ROT_PARAMS,
+            seq_lens.data_ptr() if seq_lens is not None else None,
+            B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), HEAD_DIM)
+    if fmt == "u3":
+        rc = lib().iq_decode_attention(*args, BITS, _stream(q))
+    else:
+        rc = lib().iq_decode_attention_format(*args, FORMATS[fmt], _stream(q))
     _check(rc)
     return out
 

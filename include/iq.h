@@ -59,6 +59,15 @@ enum {
 
 enum { IQ_F32 = 0, IQ_BF16 = 1 };
 
+/* Record formats: the pages' 3-bit uniform codes and variants with the same rotation (see
+ * iq_quantize_kv_format).  Record size 16 * bits bytes. */
+enum {
+  IQ_FMT_U3 = 0,    /* 3-bit uniform mid-rise, s = max|x'| / 3.5 (the default), 48 bytes */
+  IQ_FMT_U2 = 1,    /* 2-bit uniform mid-rise, s = max|x'| / 1.5, 32 bytes */
+  IQ_FMT_U4 = 2,    /* 4-bit uniform mid-rise, s = max|x'| / 7.5, 64 bytes */
+  IQ_FMT_LM3 = 3    /* 3-bit Lloyd-Max levels of a unit Gaussian scaled by the RMS, 48 bytes */
+};
+
 #define IQ_HEAD_DIM 128
 #define IQ_BITS 3
 #define IQ_RECORD_BYTES 48
@@ -116,6 +125,34 @@ int iq_quantize_kv(const void* k, const void* v, int32_t dtype,
                    int32_t head_dim, int32_t bits, void* stream);
 
 /*
+ * iq_quantize_kv_format -- iq_quantize_kv for any record format IQ_FMT_*.
+ * Source: Abstract (rotation, then scalar quantization with one scale per
+ * vector, packed); the 2- and 4-bit and Lloyd-Max variants are readings that
+ * keep the rotation and change the scalar quantizer:
+ *   IQ_FMT_U2 / IQ_FMT_U4  s = max|x'| / (2^(b-1) - 1/2),
+ *                          code = clamp(floor(x'/s + 2^(b-1)), 0, 2^b - 1),
+ *                          level s * (code - (2^b - 1)/2);
+ *   IQ_FMT_LM3             sigma = |x'| / sqrt(128) (stored as the scale), the
+ *                          code of the nearest of the levels +-0.2451,
+ *                          +-0.7560, +-1.344, +-2.152 (J. Max's Lloyd-Max
+ *                          quantizer of a unit Gaussian) to x'/sigma, ties up;
+ *                          level sigma * L[code]; sigma = 0 gives code 4.
+ * Records are one little-endian bit stream of b bits per code (bit j of the
+ * code of coordinate i is stream bit b*i + j): codes uint8[n_seq][n_heads]
+ * [cache_cap][16*b].  IQ_FMT_U3 is exactly iq_quantize_kv.  4-bit codes must
+ * be 8-byte aligned.  Other arguments and errors as iq_quantize_kv, with
+ * format in place of bits (IQ_EUNSUPPORTED for an unknown format).
+ */
+int iq_quantize_kv_format(const void* k, const void* v, int32_t dtype,
+                          int64_t n_seq, int32_t n_heads, int64_t n_tokens,
+                          int64_t stride_seq, int64_t stride_head, int64_t stride_tok,
+                          const float* rot, int64_t rot_stride_seq,
+                          uint8_t* k_codes, float* k_scales,
+                          uint8_t* v_codes, float* v_scales,
+                          int64_t cache_cap, int64_t tok_offset,
+                          int32_t head_dim, int32_t format, void* stream);
+
+/*
  * iq_decode_workspace_bytes -- device workspace that iq_decode_attention
  * (and iq_decode_attention_append) needs with these sizes on the current
  * device: the split plan (chunk size and each sequence's first chunk) and
@@ -166,6 +203,25 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
                         int64_t cache_cap, float sm_scale, float* out,
                         void* workspace, int64_t workspace_bytes,
                         int32_t head_dim, int32_t bits, void* stream);
+
+/*
+ * iq_decode_attention_format -- iq_decode_attention on a cache written by
+ * iq_quantize_kv_format with the same format (codes [batch][n_kv_heads]
+ * [cache_cap][16*b]).  Source: Abstract (attention on the packed tensors).
+ * IQ_FMT_U3 runs the same kernels as iq_decode_attention; the other formats
+ * run a vector-unit kernel with the same split of the context and the same
+ * combine.  Other arguments and errors as iq_decode_attention, with format
+ * in place of bits.
+ */
+int iq_decode_attention_format(const void* q, int32_t q_dtype,
+                               const uint8_t* k_codes, const float* k_scales,
+                               const uint8_t* v_codes, const float* v_scales,
+                               const float* rot, int64_t rot_stride_batch,
+                               const int32_t* seq_lens,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                               int64_t cache_cap, float sm_scale, float* out,
+                               void* workspace, int64_t workspace_bytes,
+                               int32_t head_dim, int32_t format, void* stream);
 
 /*
  * iq_decode_attention_multi -- attention of n_q_tokens new query tokens per

@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
                                   "iq_decode_workspace_bytes", "iq_decode_attention",
                                   "iq_decode_attention_append", "iq_decode_attention_multi",
+                                  "iq_quantize_kv_format", "iq_decode_attention_format",
                                   "iq_isotropy_workspace_bytes",
                                   "iq_isotropy_stats"])
 
@@ -236,3 +237,33 @@ def test_decode_multi_validation(kw, code):
 def test_decode_multi_workspace_is_that_of_batch_times_tokens():
     need = iq.decode_workspace_bytes(2 * 4, 8, 2, 1000)
     assert _multi(wsb=need - 1) == binding.IQ_EWORKSPACE
+
+
+def _qfmt(fmt, **kw):
+    args = dict(k=FAKE, v=FAKE, dtype=1, n_seq=1, n_heads=1, n_tokens=4, ss=512, sh=512, st=128,
+                rot=FAKE, rs=256, kc=FAKE, ks=FAKE, vc=FAKE, vs=FAKE, cap=4, off=0, hd=128)
+    args.update(kw)
+    return iq.lib().iq_quantize_kv_format(args["k"], args["v"], args["dtype"], args["n_seq"], args["n_heads"],
+                                          args["n_tokens"], args["ss"], args["sh"], args["st"], args["rot"],
+                                          args["rs"], args["kc"], args["ks"], args["vc"], args["vs"], args["cap"],
+                                          args["off"], args["hd"], fmt, None)
+
+
+def test_format_entry_points_validate():
+    assert _qfmt(7) == binding.IQ_EUNSUPPORTED and "format" in binding.last_error()
+    assert _qfmt(-1) == binding.IQ_EUNSUPPORTED
+    assert _qfmt(1, hd=64) == binding.IQ_EUNSUPPORTED
+    assert _qfmt(2, kc=FAKE + 4) == binding.IQ_EINVAL            # 4-bit records: 8-byte aligned codes
+    assert "8-byte" in binding.last_error()
+    assert _qfmt(3, n_tokens=0) == binding.IQ_OK                  # nothing to do
+    assert _qfmt(1, off=1) == binding.IQ_EINVAL
+    lib = iq.lib()
+    rc = lib.iq_decode_attention_format(FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 1, 8, 2, 1000, 0.0, FAKE,
+                                        FAKE, 16, 128, 9, None)
+    assert rc == binding.IQ_EUNSUPPORTED and binding.last_error().startswith("iq_decode_attention_format")
+    rc = lib.iq_decode_attention_format(FAKE, 1, FAKE + 4, FAKE, FAKE, FAKE, FAKE, 0, None, 1, 8, 2, 1000, 0.0, FAKE,
+                                        FAKE, 1 << 30, 128, 2, None)
+    assert rc == binding.IQ_EINVAL
+    rc = lib.iq_decode_attention_format(FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 1, 8, 2, 1000, 0.0, FAKE,
+                                        FAKE, 16, 128, 1, None)
+    assert rc == binding.IQ_EWORKSPACE
