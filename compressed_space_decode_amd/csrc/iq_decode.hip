@@ -68,6 +68,7 @@ constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running
 constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 constexpr int kMaxChunks = 1024;    // most chunks of one sequence (the combine's LDS weights)
+constexpr int kFewChunks = 16;      // rows with at most this many chunks merge in registers
 
 // Field j (0..7) of a 24-bit group is taken from byte window j / 3 (bytes 0-1, 1-2 or 2-3 of the
 // group) at bit position field_pos(j) <= 7 of each 16-bit half.
@@ -1154,7 +1155,30 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   nvalid = min(nvalid, min(kMaxChunks, a.x_max - x0));   // plan; the bound keeps every read in range
   const int64_t first = (int64_t)h * a.x_max + x0;   // partial row of chunk 0; chunks are adjacent
   const float* ml = a.part_ml + first * 2;
-  if (wave == 0) {                      // weights 2^(m_c - M) and 1/L
+  if (nvalid <= kFewChunks) {           // uniform: every thread loads all (max, sum) pairs and its partials at once
+    const float* po = a.part_o + first * 128 + tid;
+    float mv[kFewChunks], lv[kFewChunks], ov[kFewChunks];
+#pragma unroll
+    for (int c = 0; c < kFewChunks; ++c) {
+      const int cc = c < nvalid ? c : nvalid - 1;      // in range; weight 0 below
+      mv[c] = ml[2 * cc];
+      lv[c] = ml[2 * cc + 1];
+      ov[c] = po[(int64_t)cc * 128];
+    }
+    if (wave == 1 && lane < 32)         // the SO(4) blocks of this head's KV head
+      build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < kFewChunks; ++c) M = c < nvalid ? fmaxf(M, mv[c]) : M;
+    float L = 0.f, acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < kFewChunks; ++c) {
+      const float w = c < nvalid ? __builtin_amdgcn_exp2f(mv[c] - M) : 0.f;
+      L = fmaf(w, lv[c], L);
+      acc = fmaf(w, ov[c], acc);
+    }
+    y[tid] = acc / L;
+  } else if (wave == 0) {               // weights 2^(m_c - M) and 1/L
     float M = -INFINITY;
     for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c]);
 #pragma unroll
@@ -1171,8 +1195,8 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   } else if (lane < 32) {               // the SO(4) blocks of this head's KV head
     build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
   }
-  __syncthreads();
-  {
+  if (nvalid > kFewChunks) {
+    __syncthreads();
     const float* po = a.part_o + first * 128 + tid;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int c = 0;
