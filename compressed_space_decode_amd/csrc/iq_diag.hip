@@ -22,7 +22,8 @@
 // moments are taken about the vector's own mean (two passes over registers).
 // Each work-group writes fp32 sums for its 256 tokens.
 // Kernel 2 (diag_finalize_kernel): one work-group per (sequence, head) adds
-// the partial sums in fp64 and forms the statistics.
+// the partial sums in fp64 (two threads per coordinate, independent
+// accumulators) and forms the statistics.
 #include "iq_internal.h"
 #include "iq_vector.h"
 
@@ -299,42 +300,66 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
   }
 }
 
-// One work-group (128 threads, one per coordinate) per (sequence, head).
-__global__ __launch_bounds__(128) void diag_finalize_kernel(DiagArgs a) {
-  const int s = blockIdx.y, h = blockIdx.x, i = threadIdx.x;
+// One work-group (256 threads: two per coordinate, each adding half of the partials with four
+// independent accumulators) per (sequence, head).
+__global__ __launch_bounds__(256) void diag_finalize_kernel(DiagArgs a) {
+  __shared__ double half_sums[4][128];
+  __shared__ double scal[2][5];
+  const int s = blockIdx.y, h = blockIdx.x, tid = threadIdx.x, i = tid & 127, part = tid >> 7;
   const int64_t head = (int64_t)s * a.n_heads + h;
   double* st = a.stats + head * 260;
   const double n = (double)a.n_tokens;
   if (a.n_tokens == 0) {
-    st[i] = 0.0;
-    st[128 + i] = 0.0;
-    if (i < 4) st[256 + i] = 0.0;
+    if (part == 0) {
+      st[i] = 0.0;
+      st[128 + i] = 0.0;
+      if (i < 4) st[256 + i] = 0.0;
+    }
     return;
   }
   const float* p = a.part + head * (128 + (int64_t)a.n_chunks * kPartFloats);
-  double S1 = 0.0, S2 = 0.0, S3 = 0.0, S4 = 0.0;
-  for (int c = 0; c < a.n_chunks; ++c) {
-    const float* q = p + 128 + (int64_t)c * kPartFloats;
-    S1 += q[i];
-    S2 += q[128 + i];
-    S3 += q[256 + i];
-    S4 += q[384 + i];
+  const int c_begin = part * ((a.n_chunks + 1) / 2), c_end = part ? a.n_chunks : (a.n_chunks + 1) / 2;
+  double S[4][4] = {};                                // [accumulator][moment]
+  int c = c_begin;
+  for (; c + 4 <= c_end; c += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float* q = p + 128 + (int64_t)(c + u) * kPartFloats;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) S[u][m] += q[128 * m + i];
+    }
   }
-  const double mu = S1 / n;                           // mean of d = y - y_ref
-  double m2 = S2 / n - mu * mu;
-  const double m4 = S4 / n - 4.0 * mu * (S3 / n) + 6.0 * mu * mu * (S2 / n) - 3.0 * mu * mu * mu * mu;
+  for (; c < c_end; ++c) {
+    const float* q = p + 128 + (int64_t)c * kPartFloats;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) S[0][m] += q[128 * m + i];
+  }
+  if (i < 5) {                                        // the scalars: kurtosis sum, error, energy, PAPR sum, nonzero
+    double v = 0.0;
+    for (int cc = c_begin; cc < c_end; ++cc) v += p[128 + (int64_t)cc * kPartFloats + 4 * 128 + i];
+    scal[part][i] = v;
+  }
+  if (part == 1) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) half_sums[m][i] = (S[0][m] + S[1][m]) + (S[2][m] + S[3][m]);
+  }
+  __syncthreads();
+  if (part == 1) return;
+  double M[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) M[m] = ((S[0][m] + S[1][m]) + (S[2][m] + S[3][m])) + half_sums[m][i];
+  const double mu = M[0] / n;                         // mean of d = y - y_ref
+  double m2 = M[1] / n - mu * mu;
+  const double m4 = M[3] / n - 4.0 * mu * (M[2] / n) + 6.0 * mu * mu * (M[1] / n) - 3.0 * mu * mu * mu * mu;
   if (m2 < 0.0) m2 = 0.0;
   const double ym = mu + (double)p[i];                // mean of y
   const double mean_sq = m2 + ym * ym;
   st[i] = m2 > kZeroVar * mean_sq ? m4 / (m2 * m2) : 0.0;
   st[128 + i] = m2;
   if (i == 0) {
-    double sc[5] = {0.0, 0.0, 0.0, 0.0, 0.0};   // kurtosis sum, error, energy, PAPR sum, nonzero vectors
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const float* q = p + 128 + (int64_t)c * kPartFloats + 4 * 128;
+    double sc[5];
 #pragma unroll
-      for (int k = 0; k < 5; ++k) sc[k] += q[k];
-    }
+    for (int k = 0; k < 5; ++k) sc[k] = scal[0][k] + scal[1][k];
     st[256] = sc[0] / n;
     st[257] = sc[2] > 0.0 ? sc[1] / sc[2] : 0.0;
     st[258] = sc[4] > 0.0 ? sc[3] / sc[4] : 0.0;
@@ -384,7 +409,7 @@ hipError_t launch_diag(const DiagLaunch& a, hipStream_t stream) {
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(diag_finalize_kernel, dim3((unsigned)a.n_heads, (unsigned)a.n_seq), dim3(128), 0, stream, k);
+  hipLaunchKernelGGL(diag_finalize_kernel, dim3((unsigned)a.n_heads, (unsigned)a.n_seq), dim3(256), 0, stream, k);
   return hipGetLastError();
 }
 
