@@ -68,7 +68,8 @@ __device__ __forceinline__ float codes16(const float y[16], unsigned c[16]) {
     amax = max8(amax);
     const float rcp = amax > 0.f ? (half - 0.5f) / amax : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = (unsigned)fminf(fmaxf(floorf(fmaf(y[i], rcp, half)), 0.f), top);
+    for (int i = 0; i < 16; ++i)   // u in [0.5, 2^b - 0.5]: truncation is the floor, clamp the top only
+      c[i] = min(__float2uint_rz(fmaf(y[i], rcp, half)), (unsigned)top);
     return amax / (half - 0.5f);
   }
 }

@@ -171,12 +171,11 @@ __device__ __forceinline__ float quantize8(float x[16], const float (&F)[4][16],
   amax = fmaxf(amax, dpp_xor2(amax));
   amax = fmaxf(amax, swz_xor4(amax));
   const float rcp = amax > 0.f ? 3.5f / amax : 0.f;
+  // u = y / s + 4 lies in [0.5, 7.5] (up to rounding), so the conversion's truncation is the
+  // floor and only the top needs clamping (a negative u would convert to 0)
   unsigned c[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float u = floorf(fmaf(y[i], rcp, 4.0f));
-    c[i] = (unsigned)fminf(fmaxf(u, 0.f), 7.f);
-  }
+  for (int i = 0; i < 16; ++i) c[i] = min(__float2uint_rz(fmaf(y[i], rcp, 4.0f)), 7u);
   g0 = 0;
   g1 = 0;
 #pragma unroll
