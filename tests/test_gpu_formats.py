@@ -122,3 +122,27 @@ def test_three_bit_format_through_the_format_entry_points_is_the_dedicated_path(
     assert rc == 0
     torch.cuda.synchronize()
     assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
+
+
+@pytest.mark.parametrize("fmt,Hq,Hkv", [("u4", 4, 4), ("lm3", 24, 2), ("u2", 3, 1)])
+def test_decode_format_head_groupings(fmt, Hq, Hkv):
+    # G = 1 (three of the four waves hold no head), G = 12 (two head groups, the second with four
+    # heads) and G = 3
+    rng = np.random.default_rng(240 + Hq)
+    B, cap = 2, 700
+    lens = [700, 333]
+    k = rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)
+    v = rng.standard_normal((B, Hkv, cap, 128)).astype(np.float32)
+    q = (rng.standard_normal((B, Hq, 128)) * 2.0).astype(np.float32)
+    params = _params(rng, B, Hkv)
+    rot = torch.from_numpy(params).cuda()
+    kc, ks = _cache(B, Hkv, cap, fmt)
+    vc, vs = _cache(B, Hkv, cap, fmt)
+    iq.quantize_kv(torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda(), rot, kc, ks, vc, vs, fmt=fmt)
+    out = iq.decode_attention(torch.from_numpy(q).cuda(), kc, ks, vc, vs, rot,
+                              seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"), fmt=fmt)
+    torch.cuda.synchronize()
+    b = F.bits(fmt)
+    ref = F.decode_attention_format(q.astype(np.float64), F.unpack_bits(kc.cpu().numpy(), b), ks.cpu().numpy(),
+                                    F.unpack_bits(vc.cpu().numpy(), b), vs.cpu().numpy(), params, np.array(lens), fmt)
+    P.check_output(out.cpu().numpy(), ref, what="decode %s Hq=%d Hkv=%d" % (fmt, Hq, Hkv))

@@ -70,3 +70,9 @@ def test_one_token_is_decode_attention():
     lens = torch.tensor([2000, 777], dtype=torch.int32, device="cuda")
     dec = iq.decode_attention(P.torch_input(qin[:, 0], "bf16"), *cache, rot, seq_lens=lens)
     assert torch.equal(out[:, 0], dec)
+
+
+def test_multi_token_two_head_groups():
+    # 16 query heads per KV head: each token's rows span two head groups
+    rng = np.random.default_rng(65)
+    _check(rng, 2, 2, 32, 2, 1200, [1200, 517], what="Q=2 G=16")
