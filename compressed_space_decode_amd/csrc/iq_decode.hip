@@ -476,6 +476,23 @@ __device__ __forceinline__ void quad_transpose(unsigned g[4], int lane) {
 }
 
 
+// Sets the wave's issue priority from its progress through its chunk: 3 below 70% of the chunk,
+// 2 below 90%, 1 below 97.5%, 0 after.  At equal priority a SIMD's arbiter prefers older waves,
+// so the first work-group resident on a compute unit would run ahead and the last one would
+// stream alone at the end with one wave per SIMD; dropping the priority of the waves that are
+// further along keeps the work-groups of a compute unit in step.  (done, span: tokens, uniform.)
+__device__ __forceinline__ void progress_priority(int done, int span) {
+  const long long d = done, s = span;
+  if (10 * d < 7 * s)
+    __builtin_amdgcn_s_setprio(3);
+  else if (10 * d < 9 * s)
+    __builtin_amdgcn_s_setprio(2);
+  else if (40 * d < 39 * s)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
 // t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
 // past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
@@ -699,6 +716,13 @@ void decode_split_kernel(DecodeKArgs a) {
 
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
+  // The first two blocks of every wave are loaded now, so that they stream while wave 0 rotates
+  // the queries.  In the work-group that appends a token to one of those blocks these loads read
+  // zeros without a memory access (an end of 0), and the blocks are loaded after the append.
+  const bool reload = kAppend && pos >= tok0 && pos < tok0 + 2 * step;   // uniform
+  BlockData buf, buf2, buf3;
+  load_block(buf, cb, t0, reload ? 0 : tok_end, lo);
+  load_block(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   SetupSmem& ss = sm.u.setup;
@@ -853,15 +877,15 @@ void decode_split_kernel(DecodeKArgs a) {
   st.vlim = 0.f;                     // the first block always rescales
   st.pmul = 0.f;
 
-  // The first three blocks' loads are issued after the set-up: the set-up's own loads and waits
-  // sit in a branch, and issuing these behind it keeps the count of loads in flight exact.
-  BlockData buf, buf2, buf3;
-  load_block(buf, cb, t0, tok_end, lo);
-  load_block(buf2, cb, t0 + step, tok_end, lo);
+  if (reload) {                      // uniform; the barriers above ordered it after the append
+    load_block(buf, cb, t0, tok_end, lo);
+    load_block(buf2, cb, t0 + step, tok_end, lo);
+  }
   // Three buffers: the first two are refilled three blocks ahead once their codes are unpacked;
   // the third is loaded at the top of each round of three blocks.  So the buffers carried around
   // the loop were refilled one or two blocks before its back-edge, never just before it.
   while (t0 < tok_end) {            // uniform
+    progress_priority(t0 - tok0, tok_end - tok0);
     load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
     process_block<true>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);

@@ -63,18 +63,18 @@ def _two_call(s, positions, cap):
     return out, (kc, ks, vc, vs)
 
 
-def _fused(s, positions):
+def _fused(s, positions, workspace=None):
     kc, ks, vc, vs = [t.clone() for t in s["cache"]]
     pos = torch.tensor(positions, dtype=torch.int32, device="cuda")
     out = iq.decode_attention_append(P.torch_input(s["q"], s["dtype"]), P.torch_input(s["k_new"], s["dtype"]),
                                      P.torch_input(s["v_new"], s["dtype"]), pos, kc, ks, vc, vs, s["rot"],
-                                     shared_rot=s["shared"])
+                                     workspace=workspace, shared_rot=s["shared"])
     torch.cuda.synchronize()
     return out, (kc, ks, vc, vs)
 
 
-def _check(s, positions, cap, what):
-    out_f, cache_f = _fused(s, positions)
+def _check(s, positions, cap, what, workspace=None):
+    out_f, cache_f = _fused(s, positions, workspace)
     out_r, cache_r = _two_call(s, positions, cap)
     for a, b, name in zip(cache_f, cache_r, ("k codes", "k scales", "v codes", "v scales")):
         assert torch.equal(a, b), "%s: fused append left different %s" % (what, name)
@@ -128,3 +128,21 @@ def test_append_f32_inputs_and_shared_rotation():
     cap = 2000
     s = _setup(rng, 2, 12, 3, cap, dtype="f32", shared=True)
     _check(s, [1999, 640], cap, "f32, shared rotation")
+
+
+def test_append_inside_and_after_the_first_blocks_of_a_chunk():
+    # Each wave loads its chunk's first two 32-token blocks before the query set-up; the
+    # work-group whose first 256 tokens hold the new token loads them only after the append.
+    # With these lengths the kernels pick 640-token chunks (on 256 compute units): position
+    # 3850 is token 10 of chunk 6 (loaded after the append), 5520 is token 400 of chunk 8 (past
+    # the early blocks), 300 is in the first chunk, 8191 is the last slot.
+    rng = np.random.default_rng(45)
+    cap = 8192
+    s = _setup(rng, 8, 8, 8, cap)
+    positions = [3850, 5520, 300, 8000, 8000, 8000, 8000, cap - 1]
+    ws = torch.zeros(iq.decode_workspace_bytes(8, 8, 8, cap), dtype=torch.uint8, device="cuda")
+    _check(s, positions, cap, "append in and past the early blocks", workspace=ws)
+    chunk = int(ws[:4].view(torch.int32)[0])          # the plan at the start of the workspace
+    offsets = [p % chunk for p in positions]
+    assert any(p >= chunk and o < 256 for p, o in zip(positions, offsets)), (chunk, offsets)
+    assert any(o >= 256 for o in offsets), (chunk, offsets)
