@@ -20,6 +20,13 @@ Readings (the pages fix only "3-bit scalar"):
     sigma = |x'| / sqrt(128): the code is the number of midpoints between consecutive levels that are at or below
     x'/sigma (the nearest level, ties upward) and the value is sigma L[c].
     A zero vector gives sigma = 0 and code 4.  The stored scale is sigma.
+  * "a3": the asymmetric (min/max) alternative to the symmetric 3-bit quantizer,
+    as in the KIVI-style schemes the pages cite: the 8 levels are equally spaced
+    from the vector's minimum m to its maximum M, s = (M - m) / 7,
+    code = clamp(floor((x' - m)/s + 1/2), 0, 7) (the nearest level, ties upward),
+    value m + s c.  A constant vector gives s = 0 and code 0 (value m, exact).
+    Two numbers are stored per vector, (s, m): its scales array has a trailing
+    dimension of 2.  Its records are the 3-bit records of "u3".
   * Records: one little-endian bit stream of b bits per code (bit j of code i
     is stream bit b*i + j, byte k holds stream bits 8k..8k+7): 16 b bytes.
 """
@@ -29,12 +36,17 @@ import numpy as np
 
 from .isoquant import D, rotate, rotation_matrix
 
-FORMATS = ("u2", "u3", "u4", "lm3")
+FORMATS = ("u2", "u3", "u4", "lm3", "a3")
 LLOYD_MAX_8 = (-2.152, -1.344, -0.7560, -0.2451, 0.2451, 0.7560, 1.344, 2.152)   # as Max printed them
 
 
 def bits(fmt):
-    return {"u2": 2, "u3": 3, "u4": 4, "lm3": 3}[fmt]
+    return {"u2": 2, "u3": 3, "u4": 4, "lm3": 3, "a3": 3}[fmt]
+
+
+def scale_words(fmt):
+    """fp32 numbers stored per vector: (s, m) for "a3", one scale otherwise."""
+    return 2 if fmt == "a3" else 1
 
 
 def record_bytes(fmt):
@@ -76,9 +88,18 @@ def unpack_bits(records, b):
 def quantize_rotated(y, fmt):
     """Quantize rows y [..., 128] that are already rotated.  Returns (codes uint8,
     scales float32, s_exact float64, u float64): u is the value compared with the
-    decision thresholds (x'/s + 2^(b-1) for the uniform formats, x'/sigma for lm3),
-    so that tests can measure how close a decision was."""
+    decision thresholds (x'/s + 2^(b-1) for the uniform formats, x'/sigma for lm3,
+    (x' - m)/s + 1/2 for a3), so that tests can measure how close a decision was.
+    For a3 the scales have a trailing dimension of 2: (s, m)."""
     y = np.asarray(y, dtype=np.float64)
+    if fmt == "a3":
+        m = np.min(y, axis=-1)
+        s = (np.max(y, axis=-1) - m) / 7.0
+        safe = np.where(s > 0, s, 1.0)
+        u = (y - m[..., None]) / safe[..., None] + 0.5
+        codes = np.clip(np.floor(u), 0, 7)
+        codes = np.where((s > 0)[..., None], codes, 0)
+        return codes.astype(np.uint8), np.stack([s, m], axis=-1).astype(np.float32), s, u
     if fmt == "lm3":
         sigma = np.sqrt(np.sum(y * y, axis=-1) / D)
         safe = np.where(sigma > 0, sigma, 1.0)
@@ -108,6 +129,9 @@ def quantize_format(x, params, fmt):
 def levels(codes, scales, fmt):
     """Values in rotated space of codes [..., 128] with their per-vector scales, fp64."""
     c = np.asarray(codes, dtype=np.int64)
+    if fmt == "a3":
+        sm = np.asarray(scales, dtype=np.float64)
+        return sm[..., 1:2] + sm[..., 0:1] * c
     sc = np.asarray(scales, dtype=np.float64)[..., None]
     if fmt == "lm3":
         return sc * np.array(LLOYD_MAX_8)[c]

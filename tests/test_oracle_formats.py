@@ -150,3 +150,50 @@ def test_u3_attention_is_the_pinned_decode_attention():
                                oracle.decode_attention(q, kc, ks, vc, vs, p, lens), rtol=1e-12, atol=1e-14)
     c_old, s_old, _, _ = oracle.quantize(k[0, 0], p[0, 0])
     np.testing.assert_array_equal(kc[0, 0], c_old)
+
+
+def test_asymmetric_format_nearest_level_extremes_and_shift():
+    rng = np.random.default_rng(78)
+    y = rng.standard_normal((40, 128)) * np.exp(rng.uniform(-1, 1, size=(40, 1))) + rng.uniform(-3, 3, size=(40, 1))
+    codes, sm, s, u = F.quantize_rotated(y, "a3")
+    assert sm.shape == (40, 2) and F.scale_words("a3") == 2
+    m, M = y.min(axis=1), y.max(axis=1)
+    np.testing.assert_allclose(s, (M - m) / 7, rtol=1e-15)
+    np.testing.assert_array_equal(sm[:, 1], m.astype(np.float32))
+    # brute force: the nearest of the 8 levels m + s j, ties upward
+    for r in range(40):
+        lv = m[r] + s[r] * np.arange(8)
+        d = np.abs(y[r][:, None] - lv[None, :])
+        np.testing.assert_array_equal(codes[r], np.argmin(d + 1e-12 * np.arange(8)[None, ::-1], axis=1))
+    # the minimum and maximum coordinates take codes 0 and 7 and are reconstructed exactly
+    rows = np.arange(40)
+    assert np.all(codes[rows, np.argmin(y, axis=1)] == 0) and np.all(codes[rows, np.argmax(y, axis=1)] == 7)
+    x = F.levels(codes, np.stack([s, m], axis=-1), "a3")
+    np.testing.assert_allclose(x[rows, np.argmin(y, axis=1)], m, rtol=0, atol=0)
+    np.testing.assert_allclose(x[rows, np.argmax(y, axis=1)], M, rtol=1e-14)
+    assert np.all(np.abs(y - x) <= s[:, None] / 2 * (1 + 1e-12))
+    # a constant shift moves m and leaves the codes and the step unchanged (an absmax scale would not)
+    c2, sm2, s2, _ = F.quantize_rotated(y + 10.0, "a3")
+    np.testing.assert_array_equal(c2, codes)
+    np.testing.assert_allclose(s2, s, rtol=1e-12)
+    # hand-computed: the ramp 0..7 repeated is its own code with s = 1, m = 0; a constant vector
+    # has s = 0, codes 0 and is reconstructed exactly
+    ramp = (np.arange(128) % 8).astype(np.float64)
+    c3, sm3, _, _ = F.quantize_rotated(ramp[None] * 0.5 - 1.0, "a3")
+    np.testing.assert_array_equal(c3[0], np.arange(128) % 8)
+    np.testing.assert_array_equal(sm3[0], np.float32([0.5, -1.0]))
+    c4, sm4, _, _ = F.quantize_rotated(np.full((1, 128), -2.25), "a3")
+    assert np.all(c4 == 0) and sm4[0, 0] == 0 and sm4[0, 1] == -2.25
+    np.testing.assert_array_equal(F.levels(c4, sm4, "a3"), np.full((1, 128), -2.25))
+
+
+def test_asymmetric_beats_symmetric_on_offset_data():
+    # on zero-mean Gaussians the min/max range is at most twice the absmax, so the asymmetric step
+    # is no larger; on data with an offset the symmetric absmax scale wastes its levels
+    y = np.random.default_rng(79).standard_normal((2000, 128))
+    for off, factor in ((0.0, 1.0), (3.0, 4.0)):
+        mse = {}
+        for fmt in ("u3", "a3"):
+            codes, scales, _, _ = F.quantize_rotated(y + off, fmt)
+            mse[fmt] = np.mean((y + off - F.levels(codes, scales, fmt)) ** 2)
+        assert mse["a3"] * factor < mse["u3"], (off, mse)
