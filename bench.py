@@ -63,7 +63,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-other-shapes", action="store_true", help="skip the gqa8k and ragged decode timings")
     ap.add_argument("--no-isotropy", action="store_true", help="skip the isotropy diagnostics")
-    ap.add_argument("--no-formats", action="store_true", help="skip the 2/4-bit and Lloyd-Max record formats")
+    ap.add_argument("--no-formats", action="store_true",
+                    help="skip the 2/4-bit, Lloyd-Max and asymmetric record formats")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
@@ -264,11 +265,12 @@ def main():
         rott = torch.from_numpy(wt["params"]).to(dev)
         Tt = kt.shape[2]
         ref_t = exact_attention(qt[0], kt[0], vt[0])
-        for fmt in ("u2", "u3", "u4", "lm3"):
+        for fmt in ("u2", "u3", "u4", "lm3", "a3"):
             rb = 16 * iq.FORMAT_BITS[fmt]
+            sw = 2 if fmt == "a3" else 1                 # fp32 per vector: (s, m) for the asymmetric format
             kcf = torch.empty((L, HKV, T, rb), dtype=torch.uint8, device=dev)
             vcf = torch.empty_like(kcf)
-            ksf = torch.empty((L, HKV, T), dtype=torch.float32, device=dev)
+            ksf = torch.empty(iq.scale_shape((L, HKV, T), fmt), dtype=torch.float32, device=dev)
             vsf = torch.empty_like(ksf)
 
             def quant_f(fmt=fmt):
@@ -283,14 +285,14 @@ def main():
             err = rel_err(out[0], ref)
             kct = torch.empty((1, kt.shape[1], Tt, rb), dtype=torch.uint8, device=dev)
             vct = torch.empty_like(kct)
-            kst = torch.empty((1, kt.shape[1], Tt), dtype=torch.float32, device=dev)
+            kst = torch.empty(iq.scale_shape((1, kt.shape[1], Tt), fmt), dtype=torch.float32, device=dev)
             vst = torch.empty_like(kst)
             iq.quantize_kv(kt, vt, rott, kct, kst, vct, vst, fmt=fmt)
             err_t = rel_err(iq.decode_attention(qt, kct, kst, vct, vst, rott, fmt=fmt)[0], ref_t)
             del kct, vct, kst, vst
             t_qf = time_calls(quant_f, 5, stream)
             t_df = time_calls(dec_f, 20, stream)
-            cache_b = L * HKV * T * 2 * (rb + 4)
+            cache_b = L * HKV * T * 2 * (rb + 4 * sw)
             formats[fmt] = {"bits": iq.FORMAT_BITS[fmt], "record_bytes": rb,
                             "attention_rel_error_long32k_layer0": err, "attention_rel_error_gaussian": err_t,
                             "quantize_ms": t_qf * 1e3, "decode_ms": t_df * 1e3,

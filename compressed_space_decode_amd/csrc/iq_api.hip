@@ -48,7 +48,7 @@ int check_format(const char* fn, int32_t head_dim, int32_t format) {
     iq::set_error("%s: head_dim must be 128 (got %d)", fn, head_dim);
     return IQ_EUNSUPPORTED;
   }
-  if (format < IQ_FMT_U3 || format > IQ_FMT_LM3) {
+  if (format < IQ_FMT_U3 || format > IQ_FMT_A3) {
     iq::set_error("%s: unknown record format %d", fn, format);
     return IQ_EUNSUPPORTED;
   }
@@ -105,6 +105,10 @@ int quantize_impl(const char* fn, const void* k, const void* v, int32_t dtype, i
   if (n_tokens == 0) return IQ_OK;   // nothing to do (empty inputs may have NULL data pointers)
   if (format == IQ_FMT_U4 && ((k && !aligned(k_codes, 8)) || (v && !aligned(v_codes, 8)))) {
     iq::set_error("%s: 4-bit records need 8-byte aligned codes", fn);
+    return IQ_EINVAL;
+  }
+  if (format == IQ_FMT_A3 && ((k && !aligned(k_scales, 8)) || (v && !aligned(v_scales, 8)))) {
+    iq::set_error("%s: asymmetric (s, m) scale pairs need 8-byte alignment", fn);
     return IQ_EINVAL;
   }
   if (k == nullptr && v == nullptr) {
@@ -219,6 +223,10 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   }
   if (format == IQ_FMT_U4 && (!aligned(k_codes, 8) || !aligned(v_codes, 8))) {
     iq::set_error("%s: 4-bit records need 8-byte aligned codes", fn);
+    return IQ_EINVAL;
+  }
+  if (format == IQ_FMT_A3 && (!aligned(k_scales, 8) || !aligned(v_scales, 8))) {
+    iq::set_error("%s: asymmetric (s, m) scale pairs need 8-byte alignment", fn);
     return IQ_EINVAL;
   }
   if (rot_stride_batch < 0) {

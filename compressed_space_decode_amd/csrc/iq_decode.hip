@@ -952,7 +952,7 @@ void decode_split_kernel(DecodeKArgs a) {
   }
 }
 
-// ---------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit) ----------------
+// ------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit, asymmetric 3-bit) -------------
 // The same split of the context and the same partials as decode_split_kernel, computed on the
 // vector units: lanes are (token slot = lane / 8, coordinates 16e..16e+15 with e = lane % 8), every
 // wave walks all tokens of the chunk eight at a time and owns query heads 2*wave and 2*wave + 1 of
@@ -972,8 +972,9 @@ __device__ __forceinline__ uint2 format_raw(const uint8_t* rec, int e) {
   }
 }
 
-// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform) or the
-// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]).
+// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform), the
+// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]), or c itself
+// (asymmetric: the level is m + s c, the m part is added separately).
 template <int kFmt>
 __device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
   if constexpr (kFmt == IQ_FMT_U2) {
@@ -994,18 +995,23 @@ __device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
       const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
                        : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
                        : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
-      const unsigned mi = c >= 4u ? c - 4u : 3u - c;
-      const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
-      v[i] = c >= 4u ? mag : -mag;
+      if constexpr (kFmt == IQ_FMT_A3) {
+        v[i] = (float)c;
+      } else {
+        const unsigned mi = c >= 4u ? c - 4u : 3u - c;
+        const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
+        v[i] = c >= 4u ? mag : -mag;
+      }
     }
   }
 }
 
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) {
-  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);
+  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);   // LM3, A3: 48
   __shared__ float fold[32][16];
   __shared__ __attribute__((aligned(16))) float qs[8][128];
+  __shared__ float qsum[8];          // asymmetric format: sum of each head's row of qs
   const int x = blockIdx.y;
   const int g = blockIdx.x / a.head_groups;
   const int hg = blockIdx.x % a.head_groups;
@@ -1050,15 +1056,27 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     vec::rotate8(xq, F, e, y);
 #pragma unroll
     for (int i = 0; i < 16; ++i) qs[qi][16 * e + i] = have ? y[i] * a.sm_log2 : 0.f;
+    if constexpr (kFmt == IQ_FMT_A3) {
+      float t = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) t += y[i];
+      t += dpp_xor1(t);
+      t += dpp_xor2(t);
+      t += swz_xor4(t);
+      if (e == 0) qsum[qi] = have ? t * a.sm_log2 : 0.f;
+    }
   }
   __syncthreads();
 
   const uint8_t* kc = a.kc + kv * a.cap * kRec;
   const uint8_t* vc = a.vc + kv * a.cap * kRec;
-  const float* ksc = a.ks + kv * a.cap;
-  const float* vsc = a.vs + kv * a.cap;
+  // scales: one float per token, or the (s, m) pair of the asymmetric format
+  constexpr int kSW = kFmt == IQ_FMT_A3 ? 2 : 1;
+  const float* ksc = a.ks + kv * a.cap * kSW;
+  const float* vsc = a.vs + kv * a.cap * kSW;
   const int nj = min(2, max(0, nh - 2 * wave));          // heads of this wave (uniform)
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][16];
+  float lm[2] = {0.f, 0.f};          // asymmetric format: sum of p m_V (added to every coordinate)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1068,11 +1086,13 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     int t = tok0 + slot;
     const int tl = t < tok_end ? t : tok0;                 // an in-range token for idle slots
     uint2 rk = format_raw<kFmt>(kc + (int64_t)tl * kRec, e), rv = format_raw<kFmt>(vc + (int64_t)tl * kRec, e);
-    float sk = ksc[tl], sv = vsc[tl];
+    float sk = ksc[kSW * tl], sv = vsc[kSW * tl];
+    float mk = kSW == 2 ? ksc[kSW * tl + 1] : 0.f, mv = kSW == 2 ? vsc[kSW * tl + 1] : 0.f;
     for (; t < tok_end; t += 8) {
       const int tn = t + 8 < tok_end ? t + 8 : t;
       const uint2 nk = format_raw<kFmt>(kc + (int64_t)tn * kRec, e), nv = format_raw<kFmt>(vc + (int64_t)tn * kRec, e);
-      const float nsk = ksc[tn], nsv = vsc[tn];
+      const float nsk = ksc[kSW * tn], nsv = vsc[kSW * tn];
+      const float nmk = kSW == 2 ? ksc[kSW * tn + 1] : 0.f, nmv = kSW == 2 ? vsc[kSW * tn + 1] : 0.f;
       float kvv[16], vvv[16];
       format_values<kFmt>(rk, e, kvv);
       format_values<kFmt>(rv, e, vvv);
@@ -1092,7 +1112,8 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
           dot += dpp_xor1(dot);
           dot += dpp_xor2(dot);
           dot += swz_xor4(dot);
-          const float z = dot * sk;                       // score in log2 units
+          // score in log2 units; asymmetric: q.(m + s c) = s (q.c) + m sum(q)
+          const float z = kSW == 2 ? fmaf(dot, sk, mk * qsum[2 * wave + j]) : dot * sk;
           const float mn = fmaxf(m[j], z);
           const float f = __builtin_amdgcn_exp2f(m[j] - mn);
           const float p = __builtin_amdgcn_exp2f(z - mn);
@@ -1100,6 +1121,7 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
           const float pv = p * sv;
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[j][i] = fmaf(o[j][i], f, pv * vvv[i]);
+          if constexpr (kSW == 2) lm[j] = fmaf(lm[j], f, p * mv);
           m[j] = mn;
         }
       }
@@ -1107,6 +1129,8 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
       rv = nv;
       sk = nsk;
       sv = nsv;
+      mk = nmk;
+      mv = nmv;
     }
   }
   // merge the eight token slots (lanes e, e+8, ..., e+56), write this wave's heads
@@ -1123,7 +1147,7 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     float ov[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      ov[i] = o[j][i] * f;
+      ov[i] = (o[j][i] + lm[j]) * f;
 #pragma unroll
       for (int d = 8; d < 64; d <<= 1) ov[i] += __shfl_xor(ov[i], d, 64);
     }
@@ -1370,6 +1394,8 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
     hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_U4>, grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_LM3)
     hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_LM3>, grid1, dim3(kThreads), 0, stream, k);
+  else if (a.format == IQ_FMT_A3)
+    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_A3>, grid1, dim3(kThreads), 0, stream, k);
   else if (a.positions)
     hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
   else

@@ -10,7 +10,10 @@
 //                         code = clamp(floor(x'/s + 2^(b-1)), 0, 2^b - 1);
 //   IQ_FMT_LM3            the Lloyd-Max levels of a unit Gaussian as J. Max printed them
 //                         (+-0.2451, +-0.7560, +-1.344, +-2.152), scaled by the RMS
-//                         sigma = |x'| / sqrt(128); the code of the nearest level (ties up).
+//                         sigma = |x'| / sqrt(128); the code of the nearest level (ties up);
+//   IQ_FMT_A3             asymmetric (min/max, as in the KIVI-style schemes the pages cite):
+//                         m = min x', s = (max x' - m) / 7, code = clamp(floor((x' - m)/s
+//                         + 1/2), 0, 7), level m + s code; (s, m) stored per vector.
 // Records: one little-endian bit stream of b bits per code, 16 b bytes.
 //
 // Work split as in the 3-bit quantize kernel: 8 lanes per vector, lane e holds
@@ -34,16 +37,37 @@ __device__ __forceinline__ float max8(float v) {
   v = fmaxf(v, vec::dpp_xor2(v));
   return fmaxf(v, vec::swz_xor4(v));
 }
+__device__ __forceinline__ float min8(float v) {
+  v = fminf(v, vec::dpp_xor1(v));
+  v = fminf(v, vec::dpp_xor2(v));
+  return fminf(v, vec::swz_xor4(v));
+}
 __device__ __forceinline__ float sum8(float v) {
   v += vec::dpp_xor1(v);
   v += vec::dpp_xor2(v);
   return v + vec::swz_xor4(v);
 }
 
-// Codes of the lane's 16 rotated values; returns the vector's scale (s or sigma).
+// Codes of the lane's 16 rotated values; returns the vector's scale (s or sigma) and, for the
+// asymmetric format, its minimum m.
 template <int kFmt>
-__device__ __forceinline__ float codes16(const float y[16], unsigned c[16]) {
-  if constexpr (kFmt == IQ_FMT_LM3) {
+__device__ __forceinline__ float2 codes16(const float y[16], unsigned c[16]) {
+  if constexpr (kFmt == IQ_FMT_A3) {
+    float mn = y[0], mx = y[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      mn = fminf(mn, y[i]);
+      mx = fmaxf(mx, y[i]);
+    }
+    mn = min8(mn);
+    mx = max8(mx);
+    const float range = mx - mn;
+    const float rcp = range > 0.f ? 7.f / range : 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)   // the argument lies in [0.5, 7.5]: truncation is the floor
+      c[i] = min(__float2uint_rz(fmaf(y[i] - mn, rcp, 0.5f)), 7u);
+    return make_float2(range / 7.f, mn);
+  } else if constexpr (kFmt == IQ_FMT_LM3) {
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) ss = fmaf(y[i], y[i], ss);
@@ -57,7 +81,7 @@ __device__ __forceinline__ float codes16(const float y[16], unsigned c[16]) {
       for (int t = 0; t < 7; ++t) k += u >= 0.5f * (kLM[t] + kLM[t + 1]) ? 1u : 0u;
       c[i] = sigma > 0.f ? k : 4u;
     }
-    return sigma;
+    return make_float2(sigma, 0.f);
   } else {
     constexpr int b = kFmt == IQ_FMT_U2 ? 2 : 4;
     constexpr float half = (float)(1 << (b - 1));
@@ -70,13 +94,13 @@ __device__ __forceinline__ float codes16(const float y[16], unsigned c[16]) {
 #pragma unroll
     for (int i = 0; i < 16; ++i)   // u in [0.5, 2^b - 0.5]: truncation is the floor, clamp the top only
       c[i] = min(__float2uint_rz(fmaf(y[i], rcp, half)), (unsigned)top);
-    return amax / (half - 0.5f);
+    return make_float2(amax / (half - 0.5f), 0.f);
   }
 }
 
 template <bool kBF16, int kFmt>
 __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunch a) {
-  constexpr int kBits = kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3;
+  constexpr int kBits = kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3;   // LM3, A3: 3
   constexpr int kRec = 16 * kBits;
   __shared__ float mats[32][16];
   const int s = blockIdx.z;
@@ -108,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunc
                          valid, x);
       vec::rotate8(x, F, e, y);
       unsigned c[16];
-      const float scale = codes16<kFmt>(y, c);
+      const float2 scale = codes16<kFmt>(y, c);
       const int64_t rec = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset + t;
       uint8_t* dst = side.codes + rec * kRec;
       if constexpr (kBits == 2) {
@@ -139,7 +163,12 @@ __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunc
           q[2] = w[2];
         }
       }
-      if (valid && e == 0) side.scales[rec] = scale;
+      if (valid && e == 0) {
+        if constexpr (kFmt == IQ_FMT_A3)
+          reinterpret_cast<float2*>(side.scales)[rec] = scale;
+        else
+          side.scales[rec] = scale.x;
+      }
     }
   }
 }
@@ -150,8 +179,10 @@ void launch_format(int fmt, dim3 grid, hipStream_t stream, const QuantizeLaunch&
     hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_U2>), grid, dim3(kThreads), 0, stream, a);
   else if (fmt == IQ_FMT_U4)
     hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_U4>), grid, dim3(kThreads), 0, stream, a);
-  else
+  else if (fmt == IQ_FMT_LM3)
     hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_LM3>), grid, dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((quantize_format_kernel<kBF16, IQ_FMT_A3>), grid, dim3(kThreads), 0, stream, a);
 }
 
 }  // namespace

@@ -17,8 +17,13 @@ IQ_OK, IQ_EINVAL, IQ_EUNSUPPORTED, IQ_EWORKSPACE, IQ_EHIP = 0, -1, -2, -3, -4
 IQ_F32, IQ_BF16 = 0, 1
 HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS = 128, 3, 48, 256
 TRANSFORMS = {"none": 0, "wht": 1, "so4": 2, "wht_so4": 3, "dense": 4}   # IQ_T_*
-FORMATS = {"u3": 0, "u2": 1, "u4": 2, "lm3": 3}                          # IQ_FMT_*
-FORMAT_BITS = {"u3": 3, "u2": 2, "u4": 4, "lm3": 3}
+FORMATS = {"u3": 0, "u2": 1, "u4": 2, "lm3": 3, "a3": 4}                 # IQ_FMT_*
+FORMAT_BITS = {"u3": 3, "u2": 2, "u4": 4, "lm3": 3, "a3": 3}
+
+
+def scale_shape(lead, fmt):
+    """Shape of a scales array: one fp32 per vector, or the (s, m) pair of the asymmetric format."""
+    return tuple(lead) + ((2,) if fmt == "a3" else ())
 N_STATS = 260
 
 # (name, restype, argtypes) of every entry point declared in include/iq.h
@@ -122,10 +127,11 @@ def quantize_kv(k, v, rot, k_codes, k_scales, v_codes, v_scales, tok_offset=0, s
     for c, sc, t in ((k_codes, k_scales, k), (v_codes, v_scales, v)):
         if t is None:
             continue
-        if (tuple(c.shape) != (n_seq, n_heads, cap, 16 * FORMAT_BITS[fmt]) or tuple(sc.shape) != (n_seq, n_heads, cap)
+        if (tuple(c.shape) != (n_seq, n_heads, cap, 16 * FORMAT_BITS[fmt])
+                or tuple(sc.shape) != scale_shape((n_seq, n_heads, cap), fmt)
                 or not c.is_contiguous() or not sc.is_contiguous()):
-            raise ValueError("cache must be contiguous codes [n_seq][n_heads][cap][%d] and scales [n_seq][n_heads][cap]"
-                             % (16 * FORMAT_BITS[fmt]))
+            raise ValueError("cache must be contiguous codes [n_seq][n_heads][cap][%d] and scales %s"
+                             % (16 * FORMAT_BITS[fmt], "[n_seq][n_heads][cap]" + ("[2]" if fmt == "a3" else "")))
     want_rot = (n_heads if shared_rot else n_seq * n_heads) * ROT_PARAMS
     if rot.numel() != want_rot or not rot.is_contiguous():
         raise ValueError("rot must be a contiguous float32 tensor of %d values" % want_rot)
@@ -166,8 +172,9 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         if not t.is_contiguous():
             raise ValueError("cache and rotation tensors must be contiguous")
     for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
-        if tuple(c.shape) != (B, Hkv, cap, 16 * FORMAT_BITS[fmt]) or tuple(sc.shape) != (B, Hkv, cap):
-            raise ValueError("caches must be [B][Hkv][cap][%d] codes and [B][Hkv][cap] scales" % (16 * FORMAT_BITS[fmt]))
+        if tuple(c.shape) != (B, Hkv, cap, 16 * FORMAT_BITS[fmt]) or tuple(sc.shape) != scale_shape((B, Hkv, cap), fmt):
+            raise ValueError("caches must be [B][Hkv][cap][%d] codes and %s scales"
+                             % (16 * FORMAT_BITS[fmt], "[B][Hkv][cap]" + ("[2]" if fmt == "a3" else "")))
     if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
         raise ValueError("rot has the wrong number of values")
     if seq_lens is not None and seq_lens.numel() != B:

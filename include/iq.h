@@ -65,7 +65,9 @@ enum {
   IQ_FMT_U3 = 0,    /* 3-bit uniform mid-rise, s = max|x'| / 3.5 (the default), 48 bytes */
   IQ_FMT_U2 = 1,    /* 2-bit uniform mid-rise, s = max|x'| / 1.5, 32 bytes */
   IQ_FMT_U4 = 2,    /* 4-bit uniform mid-rise, s = max|x'| / 7.5, 64 bytes */
-  IQ_FMT_LM3 = 3    /* 3-bit Lloyd-Max levels of a unit Gaussian scaled by the RMS, 48 bytes */
+  IQ_FMT_LM3 = 3,   /* 3-bit Lloyd-Max levels of a unit Gaussian scaled by the RMS, 48 bytes */
+  IQ_FMT_A3 = 4     /* 3-bit asymmetric: 8 levels from the vector's min to its max, 48 bytes,
+                       and two fp32 per vector (step, min) in the scales arrays */
 };
 
 #define IQ_HEAD_DIM 128
@@ -136,7 +138,13 @@ int iq_quantize_kv(const void* k, const void* v, int32_t dtype,
  *                          code of the nearest of the levels +-0.2451,
  *                          +-0.7560, +-1.344, +-2.152 (J. Max's Lloyd-Max
  *                          quantizer of a unit Gaussian) to x'/sigma, ties up;
- *                          level sigma * L[code]; sigma = 0 gives code 4.
+ *                          level sigma * L[code]; sigma = 0 gives code 4;
+ *   IQ_FMT_A3              the asymmetric alternative: m = min x', M = max x',
+ *                          s = (M - m) / 7, code = clamp(floor((x' - m)/s + 1/2),
+ *                          0, 7), level m + s * code; M = m gives s = 0 and
+ *                          code 0.  (s, m) are stored as two floats per vector:
+ *                          scales float[n_seq][n_heads][cache_cap][2], 8-byte
+ *                          aligned.
  * Records are one little-endian bit stream of b bits per code (bit j of the
  * code of coordinate i is stream bit b*i + j): codes uint8[n_seq][n_heads]
  * [cache_cap][16*b].  IQ_FMT_U3 is exactly iq_quantize_kv.  4-bit codes must
@@ -210,8 +218,9 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
  * [cache_cap][16*b]).  Source: Abstract (attention on the packed tensors).
  * IQ_FMT_U3 runs the same kernels as iq_decode_attention; the other formats
  * run a vector-unit kernel with the same split of the context and the same
- * combine.  Other arguments and errors as iq_decode_attention, with format
- * in place of bits.
+ * combine.  IQ_FMT_A3 scales are (s, m) pairs, float[batch][n_kv_heads]
+ * [cache_cap][2], 8-byte aligned.  Other arguments and errors as
+ * iq_decode_attention, with format in place of bits.
  */
 int iq_decode_attention_format(const void* q, int32_t q_dtype,
                                const uint8_t* k_codes, const float* k_scales,

@@ -267,3 +267,9 @@ def test_format_entry_points_validate():
     rc = lib.iq_decode_attention_format(FAKE, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, 1, 8, 2, 1000, 0.0, FAKE,
                                         FAKE, 16, 128, 1, None)
     assert rc == binding.IQ_EWORKSPACE
+    # the asymmetric format's (s, m) scale pairs must be 8-byte aligned, in both entry points
+    assert _qfmt(4, ks=FAKE + 4) == binding.IQ_EINVAL and "(s, m)" in binding.last_error()
+    rc = lib.iq_decode_attention_format(FAKE, 1, FAKE, FAKE, FAKE, FAKE + 4, FAKE, 0, None, 1, 8, 2, 1000, 0.0, FAKE,
+                                        FAKE, 1 << 30, 128, 4, None)
+    assert rc == binding.IQ_EINVAL and "(s, m)" in binding.last_error()
+    assert _qfmt(5) == binding.IQ_EUNSUPPORTED                    # past the last format

@@ -28,7 +28,7 @@ def _params(rng, *lead):
 
 def _cache(n_seq, H, cap, fmt):
     codes = torch.zeros((n_seq, H, cap, F.record_bytes(fmt)), dtype=torch.uint8, device="cuda")
-    scales = torch.zeros((n_seq, H, cap), dtype=torch.float32, device="cuda")
+    scales = torch.zeros(iq.scale_shape((n_seq, H, cap), fmt), dtype=torch.float32, device="cuda")
     return codes, scales
 
 
@@ -42,7 +42,10 @@ def _check_codes(x64, params, rec, sc, fmt, what):
     if n:
         rows, cols = np.nonzero(mism)
         assert np.all(np.abs(codes_g[mism].astype(int) - codes_o[mism].astype(int)) == 1), what
-        amax = np.max(np.abs(u - (2 ** (b - 1) if fmt != "lm3" else 0.0)), axis=1)   # max|x'| in units of the step
+        if fmt == "a3":
+            amax = np.full(u.shape[0], 7.0)                   # the range max x' - min x' in units of the step
+        else:
+            amax = np.max(np.abs(u - (2 ** (b - 1) if fmt != "lm3" else 0.0)), axis=1)   # max|x'| in step units
         if fmt == "lm3":
             L = np.array(F.LLOYD_MAX_8)
             th = (L[:-1] + L[1:]) / 2
@@ -50,11 +53,16 @@ def _check_codes(x64, params, rec, sc, fmt, what):
         else:
             dist = np.abs(u[rows, cols] - np.rint(u[rows, cols]))
         assert np.all(dist <= 1e-6 * amax[rows] + 1e-12), "%s: a code differs away from a threshold" % what
-    np.testing.assert_allclose(sc, scales_o.astype(np.float64), rtol=1e-6, atol=0, err_msg=what)
+    if fmt == "a3":      # (s, m): the step within 1e-6 relative, the minimum within 1e-6 of the range
+        np.testing.assert_allclose(sc[:, 0], scales_o[:, 0].astype(np.float64), rtol=1e-6, atol=0, err_msg=what)
+        rng_ = 7.0 * scales_o[:, 0].astype(np.float64)
+        assert np.all(np.abs(sc[:, 1] - scales_o[:, 1].astype(np.float64)) <= 1e-6 * rng_ + 1e-30), what
+    else:
+        np.testing.assert_allclose(sc, scales_o.astype(np.float64), rtol=1e-6, atol=0, err_msg=what)
     return n
 
 
-@pytest.mark.parametrize("fmt", ["u2", "u4", "lm3"])
+@pytest.mark.parametrize("fmt", ["u2", "u4", "lm3", "a3"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_format_matches_oracle(fmt, dtype):
     rng = np.random.default_rng(200 + F.FORMATS.index(fmt) + (10 if dtype == "bf16" else 0))
@@ -80,7 +88,7 @@ def test_quantize_format_matches_oracle(fmt, dtype):
     print("%s %s: %d threshold flips of %d codes" % (fmt, dtype, flips, x.size), flush=True)
 
 
-@pytest.mark.parametrize("fmt", ["u2", "u4", "lm3"])
+@pytest.mark.parametrize("fmt", ["u2", "u4", "lm3", "a3"])
 def test_decode_format_matches_oracle(fmt):
     rng = np.random.default_rng(220 + F.FORMATS.index(fmt))
     B, Hq, Hkv, cap = 3, 16, 2, 2100
@@ -124,7 +132,7 @@ def test_three_bit_format_through_the_format_entry_points_is_the_dedicated_path(
     assert torch.equal(a[0], c[0]) and torch.equal(a[1], c[1])
 
 
-@pytest.mark.parametrize("fmt,Hq,Hkv", [("u4", 4, 4), ("lm3", 24, 2), ("u2", 3, 1)])
+@pytest.mark.parametrize("fmt,Hq,Hkv", [("u4", 4, 4), ("lm3", 24, 2), ("u2", 3, 1), ("a3", 12, 1)])
 def test_decode_format_head_groupings(fmt, Hq, Hkv):
     # G = 1 (three of the four waves hold no head), G = 12 (two head groups, the second with four
     # heads) and G = 3
