@@ -317,7 +317,8 @@ struct MergeSmem {
 constexpr int kPRow = 32;
 struct WaveLoopSmem {
   char p[kBlock * kPRow];
-  float sc[64];
+  float sc[64];           // the block's K scales (lanes 0-31) and V scales (lanes 32-63)
+  float mn[64];           // asymmetric format: the matching minima m
 };
 // Computed once per work-group by wave 0: sum of q' per head and the operand exponent E, with
 // wave 0's scratch.  Shares storage with the loop staging (a barrier separates them).
@@ -366,7 +367,8 @@ __device__ __forceinline__ constexpr int pv_token(int g4, int e) { return e < 4 
 struct BlockData {
   unsigned kw[2][3];      // K quarter g4 of tokens n and 16 + n
   unsigned vw[2][3];      // V quarter (lane >> 2) & 3 of tokens 16t + 4 g4 + (lane & 3), t = 0, 1
-  unsigned ksc, vsc;      // K and V scale bits of token n (row groups 0, 2) or 16 + n (1, 3)
+  unsigned ksc, vsc;      // K and V scale bits of token n (row groups 0, 2) or 16 + n (1, 3);
+                          // asymmetric format: this lane's (s, m) pair, of K (lanes 0-31) or V
 };
 
 // Per-lane constant byte offsets within a 32-token block.
@@ -374,6 +376,7 @@ struct LaneOffsets {
   unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is +768)
   unsigned vcode;         // byte offset of this lane's V quarter (token 4 g4 + (lane & 3); +768 for t = 1)
   unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
+  bool vside;             // lanes 32-63: the V scale (asymmetric format: the V (s, m) pair)
 };
 
 // Raw buffer resources over one (sequence, KV head)'s codes and scales.  Every access puts its
@@ -400,6 +403,7 @@ __device__ __forceinline__ unsigned opaque(unsigned v) {
 // Issues the loads of the block at token t0, or, if t0 is not below tok_end, loads that read
 // zeros without a memory access.  The whole offset is in the range-checked part of the buffer
 // address (vector offset plus immediate), so tokens past the end of the slice read as zeros too.
+template <bool kAsym>
 __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb, int t0, int tok_end,
                                            const LaneOffsets& lo) {
   typedef unsigned u3v __attribute__((ext_vector_type(3)));
@@ -416,11 +420,24 @@ __device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb,
     const u3v vq = __builtin_amdgcn_raw_buffer_load_b96(cb.vc, vo + 768 * tt, 0, 0);
     d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
   }
-  // Both scale loads run in every lane (keeps the resources uniform); the block's consumer picks
-  // one, so nothing here waits for the loads.
-  const unsigned so = lo.scale + (in ? (unsigned)t0 * 4u : kNoBlock);
-  d.ksc = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, so, 0, 0);
-  d.vsc = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, so, 0, 0);
+  if constexpr (kAsym) {
+    // each lane loads the (s, m) pair it stages, under an exec mask: K in lanes 0-31, V in 32-63
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    const unsigned so = 2 * lo.scale + (in ? (unsigned)t0 * 8u : kNoBlock);
+    u2v sm;
+    if (lo.vside)
+      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.vs, so, 0, 0);
+    else
+      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.ks, so, 0, 0);
+    d.ksc = sm.x;
+    d.vsc = sm.y;
+  } else {
+    // Both scale loads run in every lane (keeps the resources uniform); the block's consumer picks
+    // one, so nothing here waits for the loads.
+    const unsigned so = lo.scale + (in ? (unsigned)t0 * 4u : kNoBlock);
+    d.ksc = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, so, 0, 0);
+    d.vsc = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, so, 0, 0);
+  }
 }
 
 // Running state of one wave's online softmax.  Lane (n, g4) owns heads 2*g4 and 2*g4+1.
@@ -429,7 +446,7 @@ struct WaveState {
   float m_run[2];         // running max (log2 units), uniform over the 16 lanes of a row group
   float thr[2];           // m_run + kHeadroom: a score above it moves the running max
   float l_run[2];         // sum of p over this lane's tokens
-  float ls_run[2];        // sum of P'' over this lane's tokens
+  float ls_run[2];        // sum of P'' over this lane's tokens (asymmetric format: sum of p m_V)
   int vexp;               // vlim = 2^vexp is above every V scale seen; -200: none yet
   float vlim;             // 2^vexp (0 before the first block)
   float pmul;             // kPScale / vlim
@@ -496,13 +513,18 @@ __device__ __forceinline__ void progress_priority(int done, int span) {
 // Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
 // t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
 // past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
-template <bool kRefill>
+template <bool kRefill, bool kAsym>
 __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], float c1,
                                               const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
                                               unsigned pwr, unsigned prd) {
-  ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
+  if constexpr (kAsym) {
+    ws.sc[lane] = __uint_as_float(cur.ksc);
+    ws.mn[lane] = __uint_as_float(cur.vsc);
+  } else {
+    ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
+  }
   // ---- QK: S[(head, part)][token] = q' x codes, tile tt = tokens 16*tt + column ----
   floatx4 S[2];
 #pragma unroll
@@ -542,16 +564,29 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   //      (no copies, and no waits for them, at the loop back-edge). ----
   if (kRefill) {
     __builtin_amdgcn_sched_barrier(0);
-    load_block(cur, cb, t_refill, tok_end, lo);
+    load_block<kAsym>(cur, cb, t_refill, tok_end, lo);
   }
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
   float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
   float z[2][2];
+  float mv[2] = {0.f, 0.f};                                   // asymmetric format: V minima
+  if constexpr (kAsym) {
+    // q'.(m + s c) = s (q'.c) + m sum(q'): c2[j] is log2(e) sm sum(q') of head 2*g4 + j
+    const float mk0 = ws.mn[n], mk1 = ws.mn[16 + n];
+    mv[0] = ws.mn[32 + n];
+    mv[1] = ws.mn[48 + n];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    z[j][0] = sk0 * fmaf(S[0][2 * j] + S[0][2 * j + 1], c1, -c2[j]);
-    z[j][1] = sk1 * fmaf(S[1][2 * j] + S[1][2 * j + 1], c1, -c2[j]);
+    for (int j = 0; j < 2; ++j) {
+      z[j][0] = fmaf(sk0 * c1, S[0][2 * j] + S[0][2 * j + 1], mk0 * c2[j]);
+      z[j][1] = fmaf(sk1 * c1, S[1][2 * j] + S[1][2 * j + 1], mk1 * c2[j]);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      z[j][0] = sk0 * fmaf(S[0][2 * j] + S[0][2 * j + 1], c1, -c2[j]);
+      z[j][1] = sk1 * fmaf(S[1][2 * j] + S[1][2 * j + 1], c1, -c2[j]);
+    }
   }
   if (rem < kBlock) {                                         // last, partial block only
     if (n >= rem) { z[0][0] = z[1][0] = -INFINITY; sv0 = 0.f; }
@@ -579,7 +614,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
       const float m_new = fmaxf(st.m_run[j], row_max(fmaxf(z[j][0], z[j][1])));
       const float alpha = __builtin_amdgcn_exp2f(st.m_run[j] - m_new);   // 0 when m_run = -inf
       st.l_run[j] *= alpha;
-      st.ls_run[j] *= alpha * ratio;
+      st.ls_run[j] *= kAsym ? alpha : alpha * ratio;
       st.m_run[j] = m_new;
       st.thr[j] = m_new + kHeadroom;
       const float f = alpha * ratio;
@@ -600,7 +635,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
       const float p = __builtin_amdgcn_exp2f(z[j][tt] - st.m_run[j]);
       st.l_run[j] += p;
       const float pp = p * svm[tt];
-      st.ls_run[j] += pp;
+      st.ls_run[j] = kAsym ? fmaf(p, mv[tt], st.ls_run[j]) : st.ls_run[j] + pp;
       const _Float16 hi = (_Float16)pp;
       h4[2 * j] = hi;
       h4[2 * j + 1] = (_Float16)(pp - (float)hi);
@@ -651,7 +686,8 @@ __device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, in
   return v;
 }
 
-template <bool kAppend>
+// kAsym: the asymmetric 3-bit format (same records, an (s, m) pair per token; no append).
+template <bool kAppend, bool kAsym>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
 void decode_split_kernel(DecodeKArgs a) {
   __shared__ DecodeSmem sm;
@@ -704,8 +740,9 @@ void decode_split_kernel(DecodeKArgs a) {
   CacheBuffers cb;
   cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
   cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
-  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, cap * 4, kBufferConfig);
-  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, cap * 4, kBufferConfig);
+  constexpr int kSW = kAsym ? 2 : 1;                         // fp32 per token in the scale arrays
+  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
+  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
   const int n = lane & 15;          // MFMA column: token within a 16-token tile / V group
   const int g4 = lane >> 4;         // row group: quarter of the K record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
@@ -713,6 +750,7 @@ void decode_split_kernel(DecodeKArgs a) {
   lo.vcode = (unsigned)(48 * (4 * g4 + (lane & 3)) + 12 * ((lane >> 2) & 3));
   lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
   const bool vscale = g4 >= 2;
+  lo.vside = vscale;
 
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
@@ -721,8 +759,8 @@ void decode_split_kernel(DecodeKArgs a) {
   // zeros without a memory access (an end of 0), and the blocks are loaded after the append.
   const bool reload = kAppend && pos >= tok0 && pos < tok0 + 2 * step;   // uniform
   BlockData buf, buf2, buf3;
-  load_block(buf, cb, t0, reload ? 0 : tok_end, lo);
-  load_block(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
+  load_block<kAsym>(buf, cb, t0, reload ? 0 : tok_end, lo);
+  load_block<kAsym>(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   SetupSmem& ss = sm.u.setup;
@@ -860,7 +898,8 @@ void decode_split_kernel(DecodeKArgs a) {
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
-  const float c2[2] = {a.sm_log2 * 3.5f * qsum0, a.sm_log2 * 3.5f * qsum1};
+  // (asymmetric format: c2 = log2(e) sm sum q', the coefficient of the minimum m_K)
+  const float c2[2] = {a.sm_log2 * (kAsym ? 1.f : 3.5f) * qsum0, a.sm_log2 * (kAsym ? 1.f : 3.5f) * qsum1};
   // LDS addresses: this lane's P'' writes (token n of each tile, rows 4*g4..4*g4+3) and its
   // transposed P'' reads (token row 4*g4 + n/4, piece n%4; tile 1 is 16 rows further).
   const unsigned pwr = (unsigned)(n * kPRow + 8 * g4);
@@ -878,24 +917,24 @@ void decode_split_kernel(DecodeKArgs a) {
   st.pmul = 0.f;
 
   if (reload) {                      // uniform; the barriers above ordered it after the append
-    load_block(buf, cb, t0, tok_end, lo);
-    load_block(buf2, cb, t0 + step, tok_end, lo);
+    load_block<kAsym>(buf, cb, t0, tok_end, lo);
+    load_block<kAsym>(buf2, cb, t0 + step, tok_end, lo);
   }
   // Three buffers: the first two are refilled three blocks ahead once their codes are unpacked;
   // the third is loaded at the top of each round of three blocks.  So the buffers carried around
   // the loop were refilled one or two blocks before its back-edge, never just before it.
   while (t0 < tok_end) {            // uniform
     progress_priority(t0 - tok0, tok_end - tok0);
-    load_block(buf3, cb, t0 + 2 * step, tok_end, lo);
-    process_block<true>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+    load_block<kAsym>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    process_block<true, kAsym>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block<true>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+    process_block<true, kAsym>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block<false>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
+    process_block<false, kAsym>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
                          n, g4, pwr, prd);
     t0 += step;
   }
@@ -925,7 +964,9 @@ void decode_split_kernel(DecodeKArgs a) {
       const float up = (float)(1 << (24 - field_pos(j8)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        sm.u.merge.o[wave][2 * g4 + j][coord] = back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
+        sm.u.merge.o[wave][2 * g4 + j][coord] =
+            kAsym ? fmaf(back * up, st.O[j8][2 * j] + st.O[j8][2 * j + 1], ls_tot[j])
+                  : back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
     }
   }
   __syncthreads();
@@ -952,7 +993,8 @@ void decode_split_kernel(DecodeKArgs a) {
   }
 }
 
-// ------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit, asymmetric 3-bit) -------------
+// ---------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit) ----------------
+// (the asymmetric 3-bit format has the 3-bit records and runs decode_split_kernel<false, true>)
 // The same split of the context and the same partials as decode_split_kernel, computed on the
 // vector units: lanes are (token slot = lane / 8, coordinates 16e..16e+15 with e = lane % 8), every
 // wave walks all tokens of the chunk eight at a time and owns query heads 2*wave and 2*wave + 1 of
@@ -972,9 +1014,8 @@ __device__ __forceinline__ uint2 format_raw(const uint8_t* rec, int e) {
   }
 }
 
-// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform), the
-// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]), or c itself
-// (asymmetric: the level is m + s c, the m part is added separately).
+// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform) or the
+// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]).
 template <int kFmt>
 __device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
   if constexpr (kFmt == IQ_FMT_U2) {
@@ -995,23 +1036,18 @@ __device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
       const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
                        : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
                        : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
-      if constexpr (kFmt == IQ_FMT_A3) {
-        v[i] = (float)c;
-      } else {
-        const unsigned mi = c >= 4u ? c - 4u : 3u - c;
-        const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
-        v[i] = c >= 4u ? mag : -mag;
-      }
+      const unsigned mi = c >= 4u ? c - 4u : 3u - c;
+      const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
+      v[i] = c >= 4u ? mag : -mag;
     }
   }
 }
 
 template <int kFmt>
 __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) {
-  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);   // LM3, A3: 48
+  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);
   __shared__ float fold[32][16];
   __shared__ __attribute__((aligned(16))) float qs[8][128];
-  __shared__ float qsum[8];          // asymmetric format: sum of each head's row of qs
   const int x = blockIdx.y;
   const int g = blockIdx.x / a.head_groups;
   const int hg = blockIdx.x % a.head_groups;
@@ -1056,27 +1092,15 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     vec::rotate8(xq, F, e, y);
 #pragma unroll
     for (int i = 0; i < 16; ++i) qs[qi][16 * e + i] = have ? y[i] * a.sm_log2 : 0.f;
-    if constexpr (kFmt == IQ_FMT_A3) {
-      float t = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) t += y[i];
-      t += dpp_xor1(t);
-      t += dpp_xor2(t);
-      t += swz_xor4(t);
-      if (e == 0) qsum[qi] = have ? t * a.sm_log2 : 0.f;
-    }
   }
   __syncthreads();
 
   const uint8_t* kc = a.kc + kv * a.cap * kRec;
   const uint8_t* vc = a.vc + kv * a.cap * kRec;
-  // scales: one float per token, or the (s, m) pair of the asymmetric format
-  constexpr int kSW = kFmt == IQ_FMT_A3 ? 2 : 1;
-  const float* ksc = a.ks + kv * a.cap * kSW;
-  const float* vsc = a.vs + kv * a.cap * kSW;
+  const float* ksc = a.ks + kv * a.cap;
+  const float* vsc = a.vs + kv * a.cap;
   const int nj = min(2, max(0, nh - 2 * wave));          // heads of this wave (uniform)
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][16];
-  float lm[2] = {0.f, 0.f};          // asymmetric format: sum of p m_V (added to every coordinate)
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1086,13 +1110,11 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     int t = tok0 + slot;
     const int tl = t < tok_end ? t : tok0;                 // an in-range token for idle slots
     uint2 rk = format_raw<kFmt>(kc + (int64_t)tl * kRec, e), rv = format_raw<kFmt>(vc + (int64_t)tl * kRec, e);
-    float sk = ksc[kSW * tl], sv = vsc[kSW * tl];
-    float mk = kSW == 2 ? ksc[kSW * tl + 1] : 0.f, mv = kSW == 2 ? vsc[kSW * tl + 1] : 0.f;
+    float sk = ksc[tl], sv = vsc[tl];
     for (; t < tok_end; t += 8) {
       const int tn = t + 8 < tok_end ? t + 8 : t;
       const uint2 nk = format_raw<kFmt>(kc + (int64_t)tn * kRec, e), nv = format_raw<kFmt>(vc + (int64_t)tn * kRec, e);
-      const float nsk = ksc[kSW * tn], nsv = vsc[kSW * tn];
-      const float nmk = kSW == 2 ? ksc[kSW * tn + 1] : 0.f, nmv = kSW == 2 ? vsc[kSW * tn + 1] : 0.f;
+      const float nsk = ksc[tn], nsv = vsc[tn];
       float kvv[16], vvv[16];
       format_values<kFmt>(rk, e, kvv);
       format_values<kFmt>(rv, e, vvv);
@@ -1112,8 +1134,7 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
           dot += dpp_xor1(dot);
           dot += dpp_xor2(dot);
           dot += swz_xor4(dot);
-          // score in log2 units; asymmetric: q.(m + s c) = s (q.c) + m sum(q)
-          const float z = kSW == 2 ? fmaf(dot, sk, mk * qsum[2 * wave + j]) : dot * sk;
+          const float z = dot * sk;                       // score in log2 units
           const float mn = fmaxf(m[j], z);
           const float f = __builtin_amdgcn_exp2f(m[j] - mn);
           const float p = __builtin_amdgcn_exp2f(z - mn);
@@ -1121,7 +1142,6 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
           const float pv = p * sv;
 #pragma unroll
           for (int i = 0; i < 16; ++i) o[j][i] = fmaf(o[j][i], f, pv * vvv[i]);
-          if constexpr (kSW == 2) lm[j] = fmaf(lm[j], f, p * mv);
           m[j] = mn;
         }
       }
@@ -1129,8 +1149,6 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
       rv = nv;
       sk = nsk;
       sv = nsv;
-      mk = nmk;
-      mv = nmv;
     }
   }
   // merge the eight token slots (lanes e, e+8, ..., e+56), write this wave's heads
@@ -1147,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     float ov[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      ov[i] = (o[j][i] + lm[j]) * f;
+      ov[i] = o[j][i] * f;
 #pragma unroll
       for (int d = 8; d < 64; d <<= 1) ov[i] += __shfl_xor(ov[i], d, 64);
     }
@@ -1395,11 +1413,11 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   else if (a.format == IQ_FMT_LM3)
     hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_LM3>, grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_A3)
-    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_A3>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.positions)
-    hipLaunchKernelGGL(decode_split_kernel<true>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<true, false>), grid1, dim3(kThreads), 0, stream, k);
   else
-    hipLaunchKernelGGL(decode_split_kernel<false>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, false>), grid1, dim3(kThreads), 0, stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 

@@ -216,8 +216,9 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
  * iq_decode_attention_format -- iq_decode_attention on a cache written by
  * iq_quantize_kv_format with the same format (codes [batch][n_kv_heads]
  * [cache_cap][16*b]).  Source: Abstract (attention on the packed tensors).
- * IQ_FMT_U3 runs the same kernels as iq_decode_attention; the other formats
- * run a vector-unit kernel with the same split of the context and the same
+ * IQ_FMT_U3 runs the same kernels as iq_decode_attention and IQ_FMT_A3 (the
+ * same records) a variant of its matrix-core kernel; the other formats run a
+ * vector-unit kernel with the same split of the context and the same
  * combine.  IQ_FMT_A3 scales are (s, m) pairs, float[batch][n_kv_heads]
  * [cache_cap][2], 8-byte aligned.  Other arguments and errors as
  * iq_decode_attention, with format in place of bits.
