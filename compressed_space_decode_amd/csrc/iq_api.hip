@@ -169,6 +169,7 @@ namespace {
 // to lie past every slice: cache_cap * 48 stays below it with a 64-token margin (83,886,016
 // tokens).
 constexpr int64_t kMaxCacheCap = 0xF0000000ll / 48 - 64;
+constexpr int64_t kMaxCacheCapU4 = 0xF0000000ll / 64 - 64;   // 62,914,432 tokens
 
 int check_decode_sizes(const char* fn, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int64_t cache_cap) {
   if (batch < 1 || batch > 65535 || n_q_heads < 1 || n_kv_heads < 1 || cache_cap < 1) {
@@ -227,6 +228,11 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   }
   if (format == IQ_FMT_A3 && (!aligned(k_scales, 8) || !aligned(v_scales, 8))) {
     iq::set_error("%s: asymmetric (s, m) scale pairs need 8-byte alignment", fn);
+    return IQ_EINVAL;
+  }
+  // 64-byte records: the kernel's buffer offsets reach cache_cap * 64 (same 64-token margin)
+  if (format == IQ_FMT_U4 && cache_cap > kMaxCacheCapU4) {
+    iq::set_error("%s: 4-bit records allow cache_cap <= %lld", fn, (long long)kMaxCacheCapU4);
     return IQ_EINVAL;
   }
   if (rot_stride_batch < 0) {

@@ -42,6 +42,12 @@
 //     tokens: exactly the B operand column n of O[head, part][coordinate 8n + j]
 //     += P'' x V for the 8 tiles j.  V never passes through LDS;
 //   * the 4 waves merge in LDS and write one (max, sum, o') partial.
+// The same kernel reads the record variants (template parameter kFmt): 4-bit and 2-bit uniform
+// codes (fields at bits <= 6 and <= 8 of a half are exact fp16 subnormals too; other unpack
+// masks, byte windows and slot maps) and the asymmetric 3-bit format (the same records, an
+// (s, m) pair per token: q'.(m + s c) = s (q'.c) + m sum(q'), and sum p m_V is added to every
+// output coordinate).  Lloyd-Max 3-bit levels are not uniform, so that format runs a vector-unit
+// kernel (decode_lm3_kernel) on the same split and partials.
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
 // blocks followed by the Hadamard transform).
@@ -98,6 +104,79 @@ __device__ __forceinline__ void unpack_quarter(unsigned w0, unsigned w1, unsigne
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[8 * P + j] = win[P][j / 3] & field_mask(j);
 }
+
+// Record geometry of the formats the matrix-core kernel reads: 3-bit (U3, and A3 with the same
+// records), 4-bit and 2-bit uniform.  A quarter is the 32 coordinates 32 g4 .. 32 g4 + 31 of a
+// record, kQW dwords; a group is 8 coordinates.
+template <int kFmt>
+struct Fmt {
+  static constexpr int kBits = kFmt == IQ_FMT_U4 ? 4 : kFmt == IQ_FMT_U2 ? 2 : 3;
+  static constexpr int kRec = 16 * kBits;             // record bytes
+  static constexpr int kQW = kBits;                   // dwords of a quarter (4 kBits bytes)
+  static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : 3.5f;
+  static constexpr bool kAsym = kFmt == IQ_FMT_A3;
+};
+
+// K slot s (0..31) of a quarter: the coordinate it holds and the bit position of its field.
+//  3-bit: as slot_coord / slot_pow.
+//  4-bit: word w = s/2 holds (dword w/4 = group w/4) & 0x000F000F or & 0x00F000F0, unshifted (w%4 <
+//         2) or shifted right 8 bits: coordinates t and t + 4 of the group (t = w%4) at bit 4 (t%2).
+//  2-bit: word w holds dword w/8 (16 coordinates) & (0x00030003 << 2t) for t = w%8 <= 4, else the
+//         dword shifted right 8 bits & (0x00030003 << 2(t-4)): coordinates t and t + 8.
+template <int kFmt>
+__device__ __forceinline__ int slot_coord_f(int s) {
+  const int w = s >> 1;
+  if constexpr (Fmt<kFmt>::kBits == 3) return slot_coord(s);
+  else if constexpr (Fmt<kFmt>::kBits == 4) return 8 * (w >> 2) + (w & 3) + 4 * (s & 1);
+  else return 16 * (w >> 3) + (w & 7) + 8 * (s & 1);
+}
+template <int kFmt>
+__device__ __forceinline__ int slot_pow_f(int s) {
+  const int t = (s >> 1) & 7;
+  if constexpr (Fmt<kFmt>::kBits == 3) return slot_pow(s);
+  else if constexpr (Fmt<kFmt>::kBits == 4) return 4 * (t & 1);
+  else return t <= 4 ? 2 * t : 2 * (t - 4);
+}
+
+// Unpacks one K quarter into the 16 fp16-pair words of the 4 QK products (words 4kb..4kb+3).
+template <int kFmt>
+__device__ __forceinline__ void unpack_k(const unsigned (&w)[Fmt<kFmt>::kQW], unsigned o[16]) {
+  if constexpr (Fmt<kFmt>::kBits == 3) {
+    unpack_quarter(w[0], w[1], w[2], o);
+  } else if constexpr (Fmt<kFmt>::kBits == 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned h = w[k] >> 8;
+      o[4 * k] = w[k] & 0x000F000Fu;
+      o[4 * k + 1] = w[k] & 0x00F000F0u;
+      o[4 * k + 2] = h & 0x000F000Fu;
+      o[4 * k + 3] = h & 0x00F000F0u;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const unsigned h = w[k] >> 8;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) o[8 * k + t] = t <= 4 ? w[k] & (0x00030003u << (2 * t)) : h & (0x00030003u << (2 * (t - 4)));
+    }
+  }
+}
+
+// V operand of the PV product for output field j (coordinate 8n + j): which byte window of a token
+// pair holds it, at which bit position, under which mask.
+template <int kFmt>
+struct VField {
+  static constexpr int kWin = Fmt<kFmt>::kBits == 3 ? 3 : Fmt<kFmt>::kBits == 4 ? 4 : 2;   // windows per pair
+  __device__ __forceinline__ static constexpr int win(int j) {
+    return Fmt<kFmt>::kBits == 3 ? j / 3 : Fmt<kFmt>::kBits == 4 ? j / 2 : (j <= 4 ? 0 : 1);
+  }
+  __device__ __forceinline__ static constexpr int pos(int j) {
+    return Fmt<kFmt>::kBits == 3 ? field_pos(j) : Fmt<kFmt>::kBits == 4 ? 4 * (j & 1) : (j <= 4 ? 2 * j : 2 * (j - 4));
+  }
+  __device__ __forceinline__ static constexpr unsigned mask(int j) {
+    return Fmt<kFmt>::kBits == 3 ? field_mask(j) : Fmt<kFmt>::kBits == 4 ? 0x000F000Fu << pos(j) : 0x00030003u << pos(j);
+  }
+};
 
 __device__ __forceinline__ half8 as_half8(unsigned a, unsigned b, unsigned c, unsigned d) {
   uint4v v = {a, b, c, d};
@@ -364,17 +443,18 @@ __device__ __forceinline__ void build_block(const float* p, float* out16) {
 // 16 + 4*g4 + e - 4 (e >= 4) of the block, for both operands.
 __device__ __forceinline__ constexpr int pv_token(int g4, int e) { return e < 4 ? 4 * g4 + e : 12 + 4 * g4 + e; }
 
+template <int kQW>
 struct BlockData {
-  unsigned kw[2][3];      // K quarter g4 of tokens n and 16 + n
-  unsigned vw[2][3];      // V quarter (lane >> 2) & 3 of tokens 16t + 4 g4 + (lane & 3), t = 0, 1
+  unsigned kw[2][kQW];    // K quarter g4 of tokens n and 16 + n
+  unsigned vw[2][kQW];    // V quarter (lane >> 2) & 3 of tokens 16t + 4 g4 + (lane & 3), t = 0, 1
   unsigned ksc, vsc;      // K and V scale bits of token n (row groups 0, 2) or 16 + n (1, 3);
                           // asymmetric format: this lane's (s, m) pair, of K (lanes 0-31) or V
 };
 
 // Per-lane constant byte offsets within a 32-token block.
 struct LaneOffsets {
-  unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is +768)
-  unsigned vcode;         // byte offset of this lane's V quarter (token 4 g4 + (lane & 3); +768 for t = 1)
+  unsigned kcode;         // byte offset of this lane's K quarter (token n; token 16 + n is 16 records on)
+  unsigned vcode;         // byte offset of this lane's V quarter (token 4 g4 + (lane & 3); t = 1: 16 records on)
   unsigned scale;         // byte offset of this lane's scale (token n or 16 + n)
   bool vside;             // lanes 32-63: the V scale (asymmetric format: the V (s, m) pair)
 };
@@ -389,8 +469,8 @@ struct CacheBuffers {
 
 constexpr int kBufferConfig = 0x00020000;   // raw (untyped) buffer, 32-bit data format
 
-// Block base for a block that is not to be read: beyond every slice (capacity * 48 is validated
-// to stay below it), so its loads return zeros without reaching memory.
+// Block base for a block that is not to be read: beyond every slice (capacity times the record
+// size is validated to stay below it), so its loads return zeros without reaching memory.
 constexpr unsigned kNoBlock = 0xF0000000u;
 
 // Keeps v in a register as an opaque value, so per-load constants added to it stay immediate
@@ -403,23 +483,36 @@ __device__ __forceinline__ unsigned opaque(unsigned v) {
 // Issues the loads of the block at token t0, or, if t0 is not below tok_end, loads that read
 // zeros without a memory access.  The whole offset is in the range-checked part of the buffer
 // address (vector offset plus immediate), so tokens past the end of the slice read as zeros too.
-template <bool kAsym>
-__device__ __forceinline__ void load_block(BlockData& d, const CacheBuffers& cb, int t0, int tok_end,
+// Loads one quarter (kQW dwords) at byte offset off of buffer r.
+template <int kQW>
+__device__ __forceinline__ void load_quarter(unsigned (&w)[kQW], __amdgpu_buffer_rsrc_t r, unsigned off) {
+  if constexpr (kQW == 3) {
+    typedef unsigned u3v __attribute__((ext_vector_type(3)));
+    const u3v q = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    w[0] = q.x; w[1] = q.y; w[2] = q.z;
+  } else if constexpr (kQW == 4) {
+    typedef unsigned u4v __attribute__((ext_vector_type(4)));
+    const u4v q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+  } else {
+    typedef unsigned u2v __attribute__((ext_vector_type(2)));
+    const u2v q = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    w[0] = q.x; w[1] = q.y;
+  }
+}
+
+template <int kFmt>
+__device__ __forceinline__ void load_block(BlockData<Fmt<kFmt>::kQW>& d, const CacheBuffers& cb, int t0, int tok_end,
                                            const LaneOffsets& lo) {
-  typedef unsigned u3v __attribute__((ext_vector_type(3)));
+  constexpr bool kAsym = Fmt<kFmt>::kAsym;
+  constexpr unsigned kRec = Fmt<kFmt>::kRec;
   const bool in = t0 < tok_end;                                      // uniform
-  const unsigned base = in ? (unsigned)t0 * 48u : kNoBlock;
+  const unsigned base = in ? (unsigned)t0 * kRec : kNoBlock;
   const unsigned ko = opaque(lo.kcode + base), vo = opaque(lo.vcode + base);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const u3v kq = __builtin_amdgcn_raw_buffer_load_b96(cb.kc, ko + 768 * tt, 0, 0);
-    d.kw[tt][0] = kq.x; d.kw[tt][1] = kq.y; d.kw[tt][2] = kq.z;
-  }
+  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW>(d.kw[tt], cb.kc, ko + 16 * kRec * tt);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const u3v vq = __builtin_amdgcn_raw_buffer_load_b96(cb.vc, vo + 768 * tt, 0, 0);
-    d.vw[tt][0] = vq.x; d.vw[tt][1] = vq.y; d.vw[tt][2] = vq.z;
-  }
+  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW>(d.vw[tt], cb.vc, vo + 16 * kRec * tt);
   if constexpr (kAsym) {
     // each lane loads the (s, m) pair it stages, under an exec mask: K in lanes 0-31, V in 32-63
     typedef unsigned u2v __attribute__((ext_vector_type(2)));
@@ -513,12 +606,13 @@ __device__ __forceinline__ void progress_priority(int done, int span) {
 // Processes the block in `cur` (`rem` valid tokens), then refills `cur` with the block at
 // t_refill as soon as the current codes are unpacked; the refill loads are unconditional (zeros
 // past the chunk), so the wait for a buffer at the top of a block leaves newer loads in flight.
-template <bool kRefill, bool kAsym>
-__device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_refill, int tok_end,
+template <bool kRefill, int kFmt>
+__device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], float c1,
                                               const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
                                               unsigned pwr, unsigned prd) {
+  constexpr bool kAsym = Fmt<kFmt>::kAsym;
   if constexpr (kAsym) {
     ws.sc[lane] = __uint_as_float(cur.ksc);
     ws.mn[lane] = __uint_as_float(cur.vsc);
@@ -530,7 +624,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     unsigned u[16];
-    unpack_quarter(cur.kw[tt][0], cur.kw[tt][1], cur.kw[tt][2], u);
+    unpack_k<kFmt>(cur.kw[tt], u);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -542,21 +636,44 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   // ---- V: each lane holds quarter y = (lane >> 2) & 3 (groups 4y..4y+3) of the tokens
   //      16t + 4 g4 + x, x = lane & 3; a 4x4 transpose inside each quad of lanes leaves lane x with
   //      group 4y + x = n of the quad's four tokens, in token order: B operand column n in the
-  //      token order of the PV product.  Then the three byte windows of each token pair. ----
-  unsigned vwin[4][3];
+  //      token order of the PV product.  Then the byte windows of each token pair (3-bit: bytes
+  //      0-1, 1-2, 2-3 of the group; 4-bit: byte b of each token's group in bytes 0 and 2; 2-bit:
+  //      the two groups side by side, and that shifted right 8 bits). ----
+  constexpr int kWin = VField<kFmt>::kWin;
+  unsigned vwin[4][kWin];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    unsigned gq[4];                                                  // group k in bytes 0..2
-    gq[0] = cur.vw[tt][0];
-    gq[1] = __builtin_amdgcn_alignbyte(cur.vw[tt][1], cur.vw[tt][0], 3);
-    gq[2] = __builtin_amdgcn_alignbyte(cur.vw[tt][2], cur.vw[tt][1], 2);
-    gq[3] = cur.vw[tt][2] >> 8;
+    unsigned gq[4];                                                  // group k from byte 0
+    if constexpr (Fmt<kFmt>::kBits == 3) {
+      gq[0] = cur.vw[tt][0];
+      gq[1] = __builtin_amdgcn_alignbyte(cur.vw[tt][1], cur.vw[tt][0], 3);
+      gq[2] = __builtin_amdgcn_alignbyte(cur.vw[tt][2], cur.vw[tt][1], 2);
+      gq[3] = cur.vw[tt][2] >> 8;
+    } else if constexpr (Fmt<kFmt>::kBits == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) gq[k] = cur.vw[tt][k];
+    } else {                                                         // upper halves unused
+      gq[0] = cur.vw[tt][0];
+      gq[1] = cur.vw[tt][0] >> 16;
+      gq[2] = cur.vw[tt][1];
+      gq[3] = cur.vw[tt][1] >> 16;
+    }
     quad_transpose(gq, lane);
 #pragma unroll
     for (int p = 0; p < 2; ++p) {                                    // tokens 2p and 2p + 1 of the quad
-      vwin[2 * tt + p][0] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x05040100u);   // bytes 0-1
-      vwin[2 * tt + p][1] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x06050201u);   // bytes 1-2
-      vwin[2 * tt + p][2] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x07060302u);   // bytes 2-3
+      unsigned* vw = vwin[2 * tt + p];
+      if constexpr (Fmt<kFmt>::kBits == 3) {
+        vw[0] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x05040100u);   // bytes 0-1
+        vw[1] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x06050201u);   // bytes 1-2
+        vw[2] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x07060302u);   // bytes 2-3
+      } else if constexpr (Fmt<kFmt>::kBits == 4) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)                                   // byte b of each, upper bytes zero
+          vw[b] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x0C000C00u | ((4u + b) << 16) | (unsigned)b);
+      } else {
+        vw[0] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x05040100u);
+        vw[1] = vw[0] >> 8;
+      }
     }
   }
   // ---- the codes are in registers now: refill the buffer.  The scheduling barrier keeps the
@@ -564,7 +681,7 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   //      (no copies, and no waits for them, at the loop back-edge). ----
   if (kRefill) {
     __builtin_amdgcn_sched_barrier(0);
-    load_block<kAsym>(cur, cb, t_refill, tok_end, lo);
+    load_block<kFmt>(cur, cb, t_refill, tok_end, lo);
   }
   // ---- scores: heads 2*g4 + j, tokens n (tile 0) and 16 + n (tile 1) ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
@@ -649,8 +766,9 @@ __device__ __forceinline__ void process_block(BlockData& cur, int rem, int t_ref
   const half8 pop = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const unsigned m = field_mask(j);
-    const half8 vb = as_half8(vwin[0][j / 3] & m, vwin[1][j / 3] & m, vwin[2][j / 3] & m, vwin[3][j / 3] & m);
+    const unsigned m = VField<kFmt>::mask(j);
+    const int wj = VField<kFmt>::win(j);
+    const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
     st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vb, st.O[j], 0, 0, 0);
   }
   __builtin_amdgcn_wave_barrier();
@@ -686,10 +804,18 @@ __device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, in
   return v;
 }
 
-// kAsym: the asymmetric 3-bit format (same records, an (s, m) pair per token; no append).
-template <bool kAppend, bool kAsym>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd)))
+// kFmt: IQ_FMT_U3 (the pages' records; the only one with the fused append), IQ_FMT_A3 (the same
+// records, an (s, m) pair per token), IQ_FMT_U4 or IQ_FMT_U2.
+// (4-bit records need more registers than three waves per SIMD leave: two waves per SIMD, and the
+// host sizes the plan for two work-groups per compute unit)
+template <int kFmt>
+constexpr int split_waves_per_simd() { return kFmt == IQ_FMT_U4 ? 2 : kWavesPerSimd; }
+
+template <bool kAppend, int kFmt>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<kFmt>())))
 void decode_split_kernel(DecodeKArgs a) {
+  constexpr bool kAsym = Fmt<kFmt>::kAsym;
+  constexpr int kRec = Fmt<kFmt>::kRec;
   __shared__ DecodeSmem sm;
   // blockIdx.x: (KV head, head group) column, so consecutive work-groups take the columns of one
   // work item (measured slightly faster than the transposed order)
@@ -701,7 +827,7 @@ void decode_split_kernel(DecodeKArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: block bases stay scalar
 
   // Token indices are 32-bit and a sequence's codes fit one buffer resource (the capacity is
-  // validated: cap * 48 < 0xF0000000): uniform token arithmetic stays on the scalar unit.
+  // validated: cap * record bytes < 0xF0000000): uniform token arithmetic stays on the scalar unit.
   const int cap = (int)a.cap;
   const int h0 = g * a.G + hg * 8;
   const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
@@ -738,16 +864,16 @@ void decode_split_kernel(DecodeKArgs a) {
   const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
 
   CacheBuffers cb;
-  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
-  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * 48), (short)0, cap * 48, kBufferConfig);
+  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
+  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
   constexpr int kSW = kAsym ? 2 : 1;                         // fp32 per token in the scale arrays
   cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
   cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
   const int n = lane & 15;          // MFMA column: token within a 16-token tile / V group
   const int g4 = lane >> 4;         // row group: quarter of the K record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
-  lo.kcode = (unsigned)(n * 48 + 12 * g4);
-  lo.vcode = (unsigned)(48 * (4 * g4 + (lane & 3)) + 12 * ((lane >> 2) & 3));
+  lo.kcode = (unsigned)(n * kRec + kRec / 4 * g4);
+  lo.vcode = (unsigned)(kRec * (4 * g4 + (lane & 3)) + kRec / 4 * ((lane >> 2) & 3));
   lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
   const bool vscale = g4 >= 2;
   lo.vside = vscale;
@@ -758,9 +884,9 @@ void decode_split_kernel(DecodeKArgs a) {
   // the queries.  In the work-group that appends a token to one of those blocks these loads read
   // zeros without a memory access (an end of 0), and the blocks are loaded after the append.
   const bool reload = kAppend && pos >= tok0 && pos < tok0 + 2 * step;   // uniform
-  BlockData buf, buf2, buf3;
-  load_block<kAsym>(buf, cb, t0, reload ? 0 : tok_end, lo);
-  load_block<kAsym>(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
+  BlockData<Fmt<kFmt>::kQW> buf, buf2, buf3;
+  load_block<kFmt>(buf, cb, t0, reload ? 0 : tok_end, lo);
+  load_block<kFmt>(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
 
   // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
   SetupSmem& ss = sm.u.setup;
@@ -853,7 +979,7 @@ void decode_split_kernel(DecodeKArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int s = 8 * kb + e;
-        const float v = ldexpf(ss.qrot[head][32 * g4 + slot_coord(s)], E - slot_pow(s));
+        const float v = ldexpf(ss.qrot[head][32 * g4 + slot_coord_f<kFmt>(s)], E - slot_pow_f<kFmt>(s));
         const _Float16 hi = (_Float16)v;
         hv[e] = part ? (_Float16)(v - (float)hi) : hi;
       }
@@ -899,7 +1025,8 @@ void decode_split_kernel(DecodeKArgs a) {
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
   const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
   // (asymmetric format: c2 = log2(e) sm sum q', the coefficient of the minimum m_K)
-  const float c2[2] = {a.sm_log2 * (kAsym ? 1.f : 3.5f) * qsum0, a.sm_log2 * (kAsym ? 1.f : 3.5f) * qsum1};
+  constexpr float kC = kAsym ? 1.f : Fmt<kFmt>::kCenter;
+  const float c2[2] = {a.sm_log2 * kC * qsum0, a.sm_log2 * kC * qsum1};
   // LDS addresses: this lane's P'' writes (token n of each tile, rows 4*g4..4*g4+3) and its
   // transposed P'' reads (token row 4*g4 + n/4, piece n%4; tile 1 is 16 rows further).
   const unsigned pwr = (unsigned)(n * kPRow + 8 * g4);
@@ -917,24 +1044,24 @@ void decode_split_kernel(DecodeKArgs a) {
   st.pmul = 0.f;
 
   if (reload) {                      // uniform; the barriers above ordered it after the append
-    load_block<kAsym>(buf, cb, t0, tok_end, lo);
-    load_block<kAsym>(buf2, cb, t0 + step, tok_end, lo);
+    load_block<kFmt>(buf, cb, t0, tok_end, lo);
+    load_block<kFmt>(buf2, cb, t0 + step, tok_end, lo);
   }
   // Three buffers: the first two are refilled three blocks ahead once their codes are unpacked;
   // the third is loaded at the top of each round of three blocks.  So the buffers carried around
   // the loop were refilled one or two blocks before its back-edge, never just before it.
   while (t0 < tok_end) {            // uniform
     progress_priority(t0 - tok0, tok_end - tok0);
-    load_block<kAsym>(buf3, cb, t0 + 2 * step, tok_end, lo);
-    process_block<true, kAsym>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+    load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    process_block<true, kFmt>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block<true, kAsym>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
+    process_block<true, kFmt>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block<false, kAsym>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
+    process_block<false, kFmt>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
                          n, g4, pwr, prd);
     t0 += step;
   }
@@ -961,12 +1088,12 @@ void decode_split_kernel(DecodeKArgs a) {
 #pragma unroll
     for (int j8 = 0; j8 < 8; ++j8) {
       const int coord = 8 * n + j8;
-      const float up = (float)(1 << (24 - field_pos(j8)));
+      const float up = (float)(1 << (24 - VField<kFmt>::pos(j8)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         sm.u.merge.o[wave][2 * g4 + j][coord] =
             kAsym ? fmaf(back * up, st.O[j8][2 * j] + st.O[j8][2 * j + 1], ls_tot[j])
-                  : back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -3.5f * ls_tot[j]);
+                  : back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -Fmt<kFmt>::kCenter * ls_tot[j]);
     }
   }
   __syncthreads();
@@ -993,59 +1120,38 @@ void decode_split_kernel(DecodeKArgs a) {
   }
 }
 
-// ---------------- other record formats (2- and 4-bit uniform, Lloyd-Max 3-bit) ----------------
-// (the asymmetric 3-bit format has the 3-bit records and runs decode_split_kernel<false, true>)
+// ---------------- Lloyd-Max 3-bit records (levels that the matrix cores cannot take as codes) ----------------
+// (the uniform 2-, 3- and 4-bit and the asymmetric 3-bit records run decode_split_kernel)
 // The same split of the context and the same partials as decode_split_kernel, computed on the
 // vector units: lanes are (token slot = lane / 8, coordinates 16e..16e+15 with e = lane % 8), every
 // wave walks all tokens of the chunk eight at a time and owns query heads 2*wave and 2*wave + 1 of
 // the group.  The rotated queries (times the softmax scale and log2 e) sit in LDS; each token
 // slot keeps its own online softmax, and the eight slots merge at the end.
-// The record bytes of this lane's 16 coordinates (2b bytes at 2b*e): 2 bits in .x; 3 bits in the
-// aligned words around bytes 6e..6e+5; 4 bits in .x (coordinates 16e..16e+7) and .y.
-template <int kFmt>
-__device__ __forceinline__ uint2 format_raw(const uint8_t* rec, int e) {
-  if constexpr (kFmt == IQ_FMT_U2) {
-    return make_uint2(reinterpret_cast<const unsigned*>(rec)[e], 0u);
-  } else if constexpr (kFmt == IQ_FMT_U4) {
-    return reinterpret_cast<const uint2*>(rec)[e];
-  } else {
-    const unsigned* wp = reinterpret_cast<const unsigned*>(rec + ((6 * e) & ~3));
-    return make_uint2(wp[0], wp[1]);
+// The record bytes of this lane's 16 coordinates (bytes 6e..6e+5): the aligned words around them.
+__device__ __forceinline__ uint2 lm3_raw(const uint8_t* rec, int e) {
+  const unsigned* wp = reinterpret_cast<const unsigned*>(rec + ((6 * e) & ~3));
+  return make_uint2(wp[0], wp[1]);
+}
+
+// Values of the 16 codes in units of the record's scale: the Lloyd-Max level L[c] (Max's table;
+// code 4 + m is +M[m] and 3 - m is -M[m]).
+__device__ __forceinline__ void lm3_values(uint2 raw, int e, float v[16]) {
+  const unsigned sh = 8 * ((6 * e) & 3);                   // 0 or 16
+  const unsigned lo = sh ? __builtin_amdgcn_alignbit(raw.y, raw.x, 16) : raw.x;   // bits 0..31 of the 48
+  const unsigned hi = sh ? (raw.y >> 16) : raw.y;                                   // bits 32..47
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
+                     : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
+                     : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
+    const unsigned mi = c >= 4u ? c - 4u : 3u - c;
+    const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
+    v[i] = c >= 4u ? mag : -mag;
   }
 }
 
-// Values of the 16 codes in units of the record's scale: c - (2^b - 1)/2 (uniform) or the
-// Lloyd-Max level L[c] (Max's table; code 4 + m is +M[m] and 3 - m is -M[m]).
-template <int kFmt>
-__device__ __forceinline__ void format_values(uint2 raw, int e, float v[16]) {
-  if constexpr (kFmt == IQ_FMT_U2) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = (float)((raw.x >> (2 * i)) & 3u) - 1.5f;
-  } else if constexpr (kFmt == IQ_FMT_U4) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[i] = (float)((raw.x >> (4 * i)) & 15u) - 7.5f;
-      v[8 + i] = (float)((raw.y >> (4 * i)) & 15u) - 7.5f;
-    }
-  } else {
-    const unsigned sh = 8 * ((6 * e) & 3);                 // 0 or 16
-    const unsigned lo = sh ? __builtin_amdgcn_alignbit(raw.y, raw.x, 16) : raw.x;   // bits 0..31 of the 48
-    const unsigned hi = sh ? (raw.y >> 16) : raw.y;                                   // bits 32..47
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
-                       : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
-                       : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
-      const unsigned mi = c >= 4u ? c - 4u : 3u - c;
-      const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
-      v[i] = c >= 4u ? mag : -mag;
-    }
-  }
-}
-
-template <int kFmt>
-__global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) {
-  constexpr int kRec = 16 * (kFmt == IQ_FMT_U2 ? 2 : kFmt == IQ_FMT_U4 ? 4 : 3);
+__global__ __launch_bounds__(kThreads) void decode_lm3_kernel(DecodeKArgs a) {
+  constexpr int kRec = 48;
   __shared__ float fold[32][16];
   __shared__ __attribute__((aligned(16))) float qs[8][128];
   const int x = blockIdx.y;
@@ -1109,15 +1215,15 @@ __global__ __launch_bounds__(kThreads) void decode_format_kernel(DecodeKArgs a) 
     // the next token's record words and scales are loaded one iteration ahead
     int t = tok0 + slot;
     const int tl = t < tok_end ? t : tok0;                 // an in-range token for idle slots
-    uint2 rk = format_raw<kFmt>(kc + (int64_t)tl * kRec, e), rv = format_raw<kFmt>(vc + (int64_t)tl * kRec, e);
+    uint2 rk = lm3_raw(kc + (int64_t)tl * kRec, e), rv = lm3_raw(vc + (int64_t)tl * kRec, e);
     float sk = ksc[tl], sv = vsc[tl];
     for (; t < tok_end; t += 8) {
       const int tn = t + 8 < tok_end ? t + 8 : t;
-      const uint2 nk = format_raw<kFmt>(kc + (int64_t)tn * kRec, e), nv = format_raw<kFmt>(vc + (int64_t)tn * kRec, e);
+      const uint2 nk = lm3_raw(kc + (int64_t)tn * kRec, e), nv = lm3_raw(vc + (int64_t)tn * kRec, e);
       const float nsk = ksc[tn], nsv = vsc[tn];
       float kvv[16], vvv[16];
-      format_values<kFmt>(rk, e, kvv);
-      format_values<kFmt>(rv, e, vvv);
+      lm3_values(rk, e, kvv);
+      lm3_values(rv, e, vvv);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         if (j < nj) {
@@ -1392,7 +1498,8 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.G = G;
   k.head_groups = geo.head_groups;
   k.cap = a.cache_cap;
-  k.target = geo.target;
+  // the plan fills one round of work-groups: 4-bit records run two per compute unit, not three
+  k.target = a.format == IQ_FMT_U4 ? (geo.target * 2 / kGroupsPerCU > 0 ? geo.target * 2 / kGroupsPerCU : 1) : geo.target;
   k.sm_log2 = sm * kLog2e;
   k.plan = plan;
   k.x_max = geo.x_max;
@@ -1407,17 +1514,17 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_stride_head = a.new_stride_head;
   const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)geo.x_max, 1u);
   if (a.format == IQ_FMT_U2)
-    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_U2>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U2>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_U4)
-    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_U4>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U4>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_LM3)
-    hipLaunchKernelGGL(decode_format_kernel<IQ_FMT_LM3>, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL(decode_lm3_kernel, grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_A3)
-    hipLaunchKernelGGL((decode_split_kernel<false, true>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_A3>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.positions)
-    hipLaunchKernelGGL((decode_split_kernel<true, false>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<true, IQ_FMT_U3>), grid1, dim3(kThreads), 0, stream, k);
   else
-    hipLaunchKernelGGL((decode_split_kernel<false, false>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U3>), grid1, dim3(kThreads), 0, stream, k);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
