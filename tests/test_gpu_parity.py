@@ -1,7 +1,9 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 five synthetic workloads, at their full sizes.  Quantize: every vector (tiny,
 gqa8k, long32k) or sampled (sequence, head) pairs (ragged, prefill).  Decode:
-every output row, with the oracle fed the codes the GPU produced.
+every output row, with the oracle fed the codes the GPU produced.  The
+benchmark's timed step (48 long32k layers, fused append) at its full size and
+launch configuration: sampled layers, every head.
 
 Tolerances are stated in tests/_parity.py.
 """
@@ -190,3 +192,50 @@ def test_prefill_full_size_sampled():
                 total += x.size
     assert flips <= P.FLIP_FRACTION * total
     _log("  prefill quantize: %d sampled codes, %d threshold flips" % (total, flips))
+
+
+def test_long32k_48_layer_append_step_sampled():
+    # The benchmark's timed step at its full size and launch configuration: 48 layers stacked as
+    # batch entries (32 query / 4 KV heads, 32768 cached tokens each) and one
+    # iq_decode_attention_append launch that writes the new token at position 32767 and attends over
+    # all 32768.  Every layer's appended records must equal iq_quantize_kv's; the outputs of three
+    # layers (every head) are checked against the oracle on the GPU's codes.
+    L = 48
+    _log("long32k x%d append step" % L)
+    w = W.decode_workload("long32k", batch=L)
+    B, Hkv, T = w["k"].shape[:3]
+    kt = P.torch_input(w["k"], w["dtype"])
+    vt = P.torch_input(w["v"], w["dtype"])
+    rot = torch.from_numpy(w["params"]).cuda()
+    kc, ks = P.empty_cache(B, Hkv, T)
+    vc, vs = P.empty_cache(B, Hkv, T)
+    iq.quantize_kv(kt[:, :, :T - 1], vt[:, :, :T - 1], rot, kc, ks, vc, vs)   # the prefilled context
+    kc[:, :, T - 1] = 0xAB                                                      # the slot the step writes
+    vc[:, :, T - 1] = 0xAB
+    q = P.torch_input(w["q"], w["dtype"])
+    positions = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(iq.decode_workspace_bytes(B, w["q"].shape[1], Hkv, T), dtype=torch.uint8, device="cuda")
+    out = iq.decode_attention_append(q, kt[:, :, T - 1], vt[:, :, T - 1], positions, kc, ks, vc, vs, rot, workspace=ws)
+    # the same records by the separate quantize call
+    kc2, ks2 = P.empty_cache(B, Hkv, 1)
+    vc2, vs2 = P.empty_cache(B, Hkv, 1)
+    iq.quantize_kv(kt[:, :, T - 1:], vt[:, :, T - 1:], rot, kc2, ks2, vc2, vs2)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :, T - 1], kc2[:, :, 0]) and torch.equal(vc[:, :, T - 1], vc2[:, :, 0])
+    assert torch.equal(ks[:, :, T - 1], ks2[:, :, 0]) and torch.equal(vs[:, :, T - 1], vs2[:, :, 0])
+    del kt, vt, kc2, vc2, ks2, vs2
+    g = dict(kc=kc.cpu().numpy(), ks=ks.cpu().numpy(), vc=vc.cpu().numpy(), vs=vs.cpu().numpy(),
+             out=out.cpu().numpy())
+    w["gpu"] = g
+    w["seq_lens"] = np.full(B, T, dtype=np.int32)
+    _check_decode(w, rows=(0, 23, 47))
+    # the appended records of the sampled layers against the oracle's quantization of the new token
+    flips = 0
+    for b in (0, 23, 47):
+        for h in range(Hkv):
+            for side, c, s in (("k", g["kc"], g["ks"]), ("v", g["vc"], g["vs"])):
+                x64 = W.to_f64(w[side][b, h, T - 1:T], w["dtype"])
+                n, _ = P.check_quantize(x64, w["params"][b, h], c[b, h, T - 1:T], s[b, h, T - 1:T],
+                                        what="appended %s b=%d h=%d" % (side, b, h))
+                flips += n
+    assert flips <= 1
