@@ -226,6 +226,21 @@ def main():
         print(json.dumps({"step_us": t_step * 1e6, "decode_us": t_decode * 1e6, "step_GBs": step_gbs}), flush=True)
         return
 
+    # the device's read-only streaming rate over as many bytes as the step reads (libiq_probe.so):
+    # the measured ceiling beside the nominal 8 TB/s
+    sbuf = torch.empty(decode_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+
+    def stream_pass():
+        iq.stream_read(sbuf, sink, 2048)
+
+    for _ in range(10):
+        stream_pass()
+    t_stream = time_calls(stream_pass, 50, stream)
+    stream_gbs = decode_bytes / t_stream / 1e9
+    del sbuf
+    log("read-only stream of %d bytes: %.1f us, %.0f GB/s" % (decode_bytes, t_stream * 1e6, stream_gbs))
+
     # single-layer decode call (the one-layer shape, unadjusted)
     ws1 = torch.empty(iq.decode_workspace_bytes(1, HQ, HKV, T), dtype=torch.uint8, device=dev)
     out1 = torch.empty((1, HQ, D), dtype=torch.float32, device=dev)
@@ -464,7 +479,10 @@ def main():
         "roofline": {"bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": step_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "iq_decode_attention_append (decode_split_kernel with the append, combine_kernel)",
-                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": t_step * 1e6},
+                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": t_step * 1e6,
+                     "frac_of_measured_stream": step_gbs / stream_gbs},
+        "stream_read": {"GBs": stream_gbs, "bytes": decode_bytes, "us": t_stream * 1e6,
+                        "kernel": "iq_probe_stream_read (libiq_probe.so): 16-byte loads, grid-stride, 2048 x 256 threads"},
         "decode_only": {"ms": t_decode * 1e3, "GBs": decode_bytes / t_decode / 1e9},
         "append_then_decode_ms": t_two * 1e3,
         "append_alone_ms": t_append * 1e3,

@@ -8,6 +8,6 @@ Compressed-Space Attention" (arXiv 2608.08081), Abstract.
 from .iq import (  # noqa: F401
     IQError, make_rotation, quantize_kv, decode_workspace_bytes, decode_attention, decode_attention_append,
     decode_attention_multi,
-    isotropy_workspace_bytes, isotropy_stats, TRANSFORMS, N_STATS, FORMATS, FORMAT_BITS, scale_shape,
+    isotropy_workspace_bytes, isotropy_stats, TRANSFORMS, N_STATS, FORMATS, FORMAT_BITS, scale_shape, stream_read,
     lib, LIB_PATH, HEAD_DIM, BITS, RECORD_BYTES, ROT_PARAMS,
 )

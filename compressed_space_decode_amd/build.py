@@ -1,4 +1,5 @@
-"""Build libiq.so (HIP kernels for gfx950 + the C-ABI host code) in-tree.
+"""Build libiq.so (HIP kernels for gfx950 + the C-ABI host code) in-tree, and the measurement
+library libiq_probe.so (a read-only streaming kernel, include/iq_probe.h) beside it.
 
 Usage: python -m compressed_space_decode_amd.build   (or via __graft_entry__.build()).
 Always recompiles.  Objects go to compressed_space_decode_amd/_build/, the
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libiq.so")
 SOURCES = ["iq_api.hip", "iq_quantize.hip", "iq_decode.hip", "iq_diag.hip", "iq_formats.hip", "iq_rotation.cpp"]
+PROBE_LIB = os.path.join(PKG, "libiq_probe.so")
+PROBE_SOURCES = ["iq_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -43,18 +46,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), res.stdout, res.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
         print("built", LIB)
+        print("built", PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,28 @@
+// Read-only streaming kernel: the HBM read ceiling of the device, measured beside the decode.
+// Built as its own library (libiq_probe.so); nothing on the decode path uses it.
+#include <hip/hip_runtime.h>
+
+#include "iq_probe.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, int64_t n, unsigned* sink) {
+  unsigned acc = 0;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u) *sink = acc;   // keeps the loads: the compiler cannot rule this out
+}
+
+}  // namespace
+
+extern "C" int iq_probe_stream_read(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream) {
+  if (buf == nullptr || sink == nullptr || bytes <= 0 || bytes % 16 != 0 || n_blocks < 1 || n_blocks > 65535 ||
+      reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return -1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint4*>(buf), bytes / 16, static_cast<unsigned*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}

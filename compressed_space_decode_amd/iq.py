@@ -317,3 +317,32 @@ def isotropy_stats(x, transform, rot=None, dense=None, shared=False, stats=None,
         stats.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(x))
     _check(rc)
     return stats
+
+
+# ---------------- measurement: the device's read-only streaming rate ----------------
+PROBE_LIB_PATH = os.path.join(_PKG, "libiq_probe.so")
+_probe = None
+
+
+def probe_lib():
+    """Load libiq_probe.so (include/iq_probe.h) once: a read-only streaming kernel used to
+    measure the HBM read ceiling beside the decode.  Not part of the decode path."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise ImportError("libiq_probe.so is not built (%s); run __graft_entry__.build()" % PROBE_LIB_PATH)
+        handle = ctypes.CDLL(PROBE_LIB_PATH)
+        handle.iq_probe_stream_read.restype = ctypes.c_int
+        handle.iq_probe_stream_read.argtypes = [_P, _I64, _I32, _P, _P]
+        _probe = handle
+    return _probe
+
+
+def stream_read(buf, sink, n_blocks=2048):
+    """Read every byte of the cuda tensor buf once (asynchronous, on the current stream); sink
+    is a cuda tensor of at least 4 bytes."""
+    rc = probe_lib().iq_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(n_blocks),
+                                          sink.data_ptr(), _stream(buf))
+    if rc != 0:
+        raise IQError(rc, "iq_probe_stream_read: invalid arguments (buf 16-byte aligned, bytes a positive "
+                          "multiple of 16, 1 <= n_blocks <= 65535) or launch failure")

@@ -273,3 +273,15 @@ def test_format_entry_points_validate():
                                         FAKE, 1 << 30, 128, 4, None)
     assert rc == binding.IQ_EINVAL and "(s, m)" in binding.last_error()
     assert _qfmt(5) == binding.IQ_EUNSUPPORTED                    # past the last format
+
+
+def test_probe_library_exports_and_validates():
+    # the measurement library beside libiq.so: its one symbol, and argument checks before any launch
+    probe = binding.probe_lib()
+    assert hasattr(probe, "iq_probe_stream_read")
+    assert probe.iq_probe_stream_read(None, 1024, 64, FAKE, None) == -1
+    assert probe.iq_probe_stream_read(FAKE, 1000, 64, FAKE, None) == -1       # not a multiple of 16
+    assert probe.iq_probe_stream_read(FAKE + 4, 1024, 64, FAKE, None) == -1   # misaligned
+    assert probe.iq_probe_stream_read(FAKE, 1024, 0, FAKE, None) == -1
+    assert probe.iq_probe_stream_read(FAKE, 1024, 70000, FAKE, None) == -1
+    assert probe.iq_probe_stream_read(FAKE, 1024, 64, None, None) == -1
