@@ -185,3 +185,45 @@ def test_decode_chunk_plan_over_ragged_batches(B, Hq, Hkv, cap, zero_frac):
     out, ref = _decode_case(rng, B, Hq, Hkv, cap, [int(n) for n in lens])
     P.check_output(out, ref, "chunk plan B=%d Hq=%d Hkv=%d cap=%d" % (B, Hq, Hkv, cap))
     assert np.all(out[lens == 0] == 0)
+
+
+def test_decode_at_the_largest_capacity():
+    # cache_cap = 83,886,016, the largest the C ABI accepts: one (sequence, head) slice holds 4 GB of
+    # K codes, so the kernels' 32-bit buffer offsets reach their limit.  Every position holds one
+    # background token; the last one (written by iq_quantize_kv at that offset) a planted token whose
+    # score is about ln(cap) above the background's.  Attention over every position is then the
+    # closed-form mixture of the two dequantized values, weighted by multiplicity; without the last
+    # position it is the background value.
+    cap = 83886016
+    rng = np.random.default_rng(100)      # the planted token carries about 43% of the weight
+    params = _params(rng, 1, 1)
+    rot = torch.from_numpy(params).cuda()
+    q = rng.standard_normal(128)
+    kbg, vbg, vp = rng.standard_normal(128), rng.standard_normal(128), rng.standard_normal(128) * 3.0
+    sm = 1.0 / np.sqrt(128)
+    kp = q / np.linalg.norm(q) * (np.log(cap) / sm / np.linalg.norm(q)) + 0.2 * kbg   # ~ln(cap) above
+    small = lambda x: torch.from_numpy(np.asarray(x, np.float32).reshape(1, 1, 1, 128)).cuda()
+    kc, ks = P.empty_cache(1, 1, cap)
+    vc, vs = P.empty_cache(1, 1, cap)
+    one = [P.empty_cache(1, 1, 1) for _ in range(2)]
+    iq.quantize_kv(small(kbg), small(vbg), rot, one[0][0], one[0][1], one[1][0], one[1][1])
+    kc[0, 0] = one[0][0][0, 0, 0]                         # the background record everywhere
+    ks[0, 0] = one[0][1][0, 0, 0]
+    vc[0, 0] = one[1][0][0, 0, 0]
+    vs[0, 0] = one[1][1][0, 0, 0]
+    iq.quantize_kv(small(kp), small(vp), rot, kc, ks, vc, vs, tok_offset=cap - 1)
+    qt = torch.from_numpy(q.astype(np.float32).reshape(1, 1, 128)).cuda()
+    outs = [iq.decode_attention(qt, kc, ks, vc, vs, rot, seq_lens=torch.tensor([n], dtype=torch.int32, device="cuda"))
+            for n in (cap, cap - 1)]
+    torch.cuda.synchronize()
+    recs = {name: (oracle.unpack(c[0, 0, t].cpu().numpy()[None])[0], float(s[0, 0, t]))
+            for name, c, s, t in (("kbg", kc, ks, 0), ("vbg", vc, vs, 0), ("kp", kc, ks, cap - 1), ("vp", vc, vs, cap - 1))}
+    del kc, vc, ks, vs
+    R = oracle.rotation_matrix(params[0, 0])
+    deq = {n: R.T @ (s * (c.astype(np.float64) - 3.5)) for n, (c, s) in recs.items()}   # unrotated K and V hats
+    z_bg, z_p = sm * q @ deq["kbg"], sm * q @ deq["kp"]
+    w_bg, w_p = (cap - 1) * np.exp(z_bg - z_p), 1.0
+    expect = (w_bg * deq["vbg"] + w_p * deq["vp"]) / (w_bg + w_p)
+    assert 0.1 < w_p / (w_bg + w_p) < 0.9, "the planted token should carry a real share of the weight"
+    P.check_output(outs[0].cpu().numpy()[0], expect[None], what="largest capacity, all positions")
+    P.check_output(outs[1].cpu().numpy()[0], deq["vbg"][None], what="largest capacity, last position excluded")
