@@ -44,10 +44,11 @@
 //   * the 4 waves merge in LDS and write one (max, sum, o') partial.
 // The same kernel reads the record variants (template parameter kFmt): 4-bit and 2-bit uniform
 // codes (fields at bits <= 6 and <= 8 of a half are exact fp16 subnormals too; other unpack
-// masks, byte windows and slot maps) and the asymmetric 3-bit format (the same records, an
-// (s, m) pair per token: q'.(m + s c) = s (q'.c) + m sum(q'), and sum p m_V is added to every
-// output coordinate).  Lloyd-Max 3-bit levels are not uniform, so that format runs a vector-unit
-// kernel (decode_lm3_kernel) on the same split and partials.
+// masks, byte windows and slot maps), the asymmetric 3-bit format (the same records, an (s, m)
+// pair per token: q'.(m + s c) = s (q'.c) + m sum(q'), and sum p m_V is added to every output
+// coordinate) and the Lloyd-Max 3-bit format (the same records; its levels are not uniform, so
+// each code is looked up in byte tables of the levels' fp16 hi and lo parts with v_perm, and
+// every product takes two MFMAs, one per part).
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
 // blocks followed by the Hadamard transform).
@@ -113,9 +114,44 @@ struct Fmt {
   static constexpr int kBits = kFmt == IQ_FMT_U4 ? 4 : kFmt == IQ_FMT_U2 ? 2 : 3;
   static constexpr int kRec = 16 * kBits;             // record bytes
   static constexpr int kQW = kBits;                   // dwords of a quarter (4 kBits bytes)
-  static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : 3.5f;
+  static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : kFmt == IQ_FMT_LM3 ? 0.f : 3.5f;
   static constexpr bool kAsym = kFmt == IQ_FMT_A3;
+  // Lloyd-Max levels are not uniform: the operands are the levels as fp16 (hi + lo parts, looked up
+  // from byte tables), not the codes as subnormals, so no 2^-24 and no centering term
+  static constexpr bool kTable = kFmt == IQ_FMT_LM3;
+  static constexpr int kSub = kTable ? 0 : 24;        // operand exponent offset undone in the scores
 };
+
+// fp16 hi and lo parts of Max's 8 Lloyd-Max levels (hi + lo equals the fp32 level to about 1e-7),
+// as byte tables for v_perm: hl / hh hold the low / high bytes of the hi parts of levels 0..7
+// (levels 0-3 in word 0, 4-7 in word 1), ll / lh those of the lo parts.
+struct LevelTable {
+  unsigned hl[2], hh[2], ll[2], lh[2];
+};
+__device__ __forceinline__ LevelTable lm3_table() {
+  const float L[8] = {-2.152f, -1.344f, -0.7560f, -0.2451f, 0.2451f, 0.7560f, 1.344f, 2.152f};
+  LevelTable t{};
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const _Float16 h = (_Float16)L[c];
+    const _Float16 l = (_Float16)(L[c] - (float)h);
+    const unsigned hb = __builtin_bit_cast(unsigned short, h), lb = __builtin_bit_cast(unsigned short, l);
+    const int w = c >> 2, sh = 8 * (c & 3);
+    t.hl[w] |= (hb & 0xFFu) << sh;
+    t.hh[w] |= (hb >> 8) << sh;
+    t.ll[w] |= (lb & 0xFFu) << sh;
+    t.lh[w] |= (lb >> 8) << sh;
+  }
+  return t;
+}
+// The fp16 hi and lo parts of the levels of two codes: code A at bits pos..pos+2 of the low half of
+// w, code B at the same bits of the high half (w already masked to those fields).
+__device__ __forceinline__ void level_pair(unsigned w, int pos, const LevelTable& t, unsigned& hi, unsigned& lo) {
+  const unsigned sa = (w >> pos) | 0x0C000C00u;            // bytes [A, zero, B, zero]
+  const unsigned sb = (sa << 8) | 0x0Cu;                   // bytes [zero, A, zero, B]
+  hi = __builtin_amdgcn_perm(t.hl[1], t.hl[0], sa) | __builtin_amdgcn_perm(t.hh[1], t.hh[0], sb);
+  lo = __builtin_amdgcn_perm(t.ll[1], t.ll[0], sa) | __builtin_amdgcn_perm(t.lh[1], t.lh[0], sb);
+}
 
 // K slot s (0..31) of a quarter: the coordinate it holds and the bit position of its field.
 //  3-bit: as slot_coord / slot_pow.
@@ -133,7 +169,8 @@ __device__ __forceinline__ int slot_coord_f(int s) {
 template <int kFmt>
 __device__ __forceinline__ int slot_pow_f(int s) {
   const int t = (s >> 1) & 7;
-  if constexpr (Fmt<kFmt>::kBits == 3) return slot_pow(s);
+  if constexpr (Fmt<kFmt>::kTable) return 0;
+  else if constexpr (Fmt<kFmt>::kBits == 3) return slot_pow(s);
   else if constexpr (Fmt<kFmt>::kBits == 4) return 4 * (t & 1);
   else return t <= 4 ? 2 * t : 2 * (t - 4);
 }
@@ -611,7 +648,7 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], float c1,
                                               const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
-                                              unsigned pwr, unsigned prd) {
+                                              unsigned pwr, unsigned prd, const LevelTable& lt) {
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
   if constexpr (kAsym) {
     ws.sc[lane] = __uint_as_float(cur.ksc);
@@ -627,10 +664,20 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
     unpack_k<kFmt>(cur.kw[tt], u);
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[kb][lane]),
-                                                  as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
-                                                  acc, 0, 0, 0);
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (Fmt<kFmt>::kTable) {     // word w holds field w % 8 of a group pair at field_pos
+        unsigned h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) level_pair(u[4 * kb + i], field_pos((4 * kb + i) & 7), lt, h[i], l[i]);
+        const half8 qa = __builtin_bit_cast(half8, qop[kb][lane]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_half8(h[0], h[1], h[2], h[3]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_half8(l[0], l[1], l[2], l[3]), acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[kb][lane]),
+                                                    as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
+                                                    acc, 0, 0, 0);
+      }
+    }
     S[tt] = acc;
   }
   // ---- V: each lane holds quarter y = (lane >> 2) & 3 (groups 4y..4y+3) of the tokens
@@ -768,8 +815,16 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
   for (int j = 0; j < 8; ++j) {
     const unsigned m = VField<kFmt>::mask(j);
     const int wj = VField<kFmt>::win(j);
-    const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
-    st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vb, st.O[j], 0, 0, 0);
+    if constexpr (Fmt<kFmt>::kTable) {
+      unsigned h[4], l[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) level_pair(vwin[p][wj] & m, VField<kFmt>::pos(j), lt, h[p], l[p]);
+      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(h[0], h[1], h[2], h[3]), st.O[j], 0, 0, 0);
+      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(l[0], l[1], l[2], l[3]), st.O[j], 0, 0, 0);
+    } else {
+      const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
+      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vb, st.O[j], 0, 0, 0);
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -1023,7 +1078,8 @@ void decode_split_kernel(DecodeKArgs a) {
   WaveLoopSmem& ws = sm.u.loop[wave];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
-  const float c1 = a.sm_log2 * ldexpf(1.f, 24 - E);
+  const float c1 = a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E);
+  const LevelTable lt = Fmt<kFmt>::kTable ? lm3_table() : LevelTable{};
   // (asymmetric format: c2 = log2(e) sm sum q', the coefficient of the minimum m_K)
   constexpr float kC = kAsym ? 1.f : Fmt<kFmt>::kCenter;
   const float c2[2] = {a.sm_log2 * kC * qsum0, a.sm_log2 * kC * qsum1};
@@ -1054,15 +1110,15 @@ void decode_split_kernel(DecodeKArgs a) {
     progress_priority(t0 - tok0, tok_end - tok0);
     load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
     process_block<true, kFmt>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, pwr, prd);
+                        ws, lane, n, g4, pwr, prd, lt);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<true, kFmt>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, pwr, prd);
+                        ws, lane, n, g4, pwr, prd, lt);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<false, kFmt>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
-                         n, g4, pwr, prd);
+                         n, g4, pwr, prd, lt);
     t0 += step;
   }
 
@@ -1088,7 +1144,7 @@ void decode_split_kernel(DecodeKArgs a) {
 #pragma unroll
     for (int j8 = 0; j8 < 8; ++j8) {
       const int coord = 8 * n + j8;
-      const float up = (float)(1 << (24 - VField<kFmt>::pos(j8)));
+      const float up = (float)(1 << (Fmt<kFmt>::kSub - (Fmt<kFmt>::kTable ? 0 : VField<kFmt>::pos(j8))));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         sm.u.merge.o[wave][2 * g4 + j][coord] =
@@ -1116,173 +1172,6 @@ void decode_split_kernel(DecodeKArgs a) {
     if (d == 0) {
       a.part_ml[pidx * 2] = M;
       a.part_ml[pidx * 2 + 1] = L;
-    }
-  }
-}
-
-// ---------------- Lloyd-Max 3-bit records (levels that the matrix cores cannot take as codes) ----------------
-// (the uniform 2-, 3- and 4-bit and the asymmetric 3-bit records run decode_split_kernel)
-// The same split of the context and the same partials as decode_split_kernel, computed on the
-// vector units: lanes are (token slot = lane / 8, coordinates 16e..16e+15 with e = lane % 8), every
-// wave walks all tokens of the chunk eight at a time and owns query heads 2*wave and 2*wave + 1 of
-// the group.  The rotated queries (times the softmax scale and log2 e) sit in LDS; each token
-// slot keeps its own online softmax, and the eight slots merge at the end.
-// The record bytes of this lane's 16 coordinates (bytes 6e..6e+5): the aligned words around them.
-__device__ __forceinline__ uint2 lm3_raw(const uint8_t* rec, int e) {
-  const unsigned* wp = reinterpret_cast<const unsigned*>(rec + ((6 * e) & ~3));
-  return make_uint2(wp[0], wp[1]);
-}
-
-// Values of the 16 codes in units of the record's scale: the Lloyd-Max level L[c] (Max's table;
-// code 4 + m is +M[m] and 3 - m is -M[m]).
-__device__ __forceinline__ void lm3_values(uint2 raw, int e, float v[16]) {
-  const unsigned sh = 8 * ((6 * e) & 3);                   // 0 or 16
-  const unsigned lo = sh ? __builtin_amdgcn_alignbit(raw.y, raw.x, 16) : raw.x;   // bits 0..31 of the 48
-  const unsigned hi = sh ? (raw.y >> 16) : raw.y;                                   // bits 32..47
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const unsigned c = 3 * i + 3 <= 32 ? (lo >> (3 * i)) & 7u
-                     : 3 * i >= 32 ? (hi >> (3 * i - 32)) & 7u
-                     : ((lo >> (3 * i)) | (hi << (32 - 3 * i))) & 7u;
-    const unsigned mi = c >= 4u ? c - 4u : 3u - c;
-    const float mag = (mi & 2u) ? ((mi & 1u) ? 2.152f : 1.344f) : ((mi & 1u) ? 0.7560f : 0.2451f);
-    v[i] = c >= 4u ? mag : -mag;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void decode_lm3_kernel(DecodeKArgs a) {
-  constexpr int kRec = 48;
-  __shared__ float fold[32][16];
-  __shared__ __attribute__((aligned(16))) float qs[8][128];
-  const int x = blockIdx.y;
-  const int g = blockIdx.x / a.head_groups;
-  const int hg = blockIdx.x % a.head_groups;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int e = lane & 7, slot = lane >> 3;
-  const int cap = (int)a.cap;
-  const int h0 = g * a.G + hg * 8;
-  const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
-  const LenSource src{nullptr, a.seq_lens, cap, a.batch, a.q_tokens};
-  const ChunkPlan plan = plan_chunks(src, len_at(src, lane), a.target, x, lane);
-  if (plan.b < 0) return;                                    // uniform
-  const int b = plan.b, len = plan.len;
-  if (tid == 0 && blockIdx.x == 0) {
-    if (x == 0) a.plan[0] = plan.chunk;
-    if (plan.j == 0) a.plan[64 + b] = x;
-  }
-  const int tok0 = plan.j * plan.chunk;
-  if (tok0 >= len) return;
-  const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
-  const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;
-  const int64_t kv = (int64_t)bc * a.Hkv + g;
-  const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
-
-  // set-up: the group's queries rotated by the same lane-parallel transform as the quantizer
-  if (tid < 32) vec::build_folded_block(rot + tid * 8, fold[tid]);
-  __syncthreads();
-  if (wave == 0) {
-    float F[4][16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) F[j][i] = fold[4 * e + j][i];
-    const int qi = slot;
-    const bool have = qi < nh;
-    const int64_t off = ((int64_t)b * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * e;
-    float xq[16], y[16];
-    if (a.q_bf16)
-      vec::load16<true>(a.q, off, true, xq);
-    else
-      vec::load16<false>(a.q, off, true, xq);
-    vec::rotate8(xq, F, e, y);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) qs[qi][16 * e + i] = have ? y[i] * a.sm_log2 : 0.f;
-  }
-  __syncthreads();
-
-  const uint8_t* kc = a.kc + kv * a.cap * kRec;
-  const uint8_t* vc = a.vc + kv * a.cap * kRec;
-  const float* ksc = a.ks + kv * a.cap;
-  const float* vsc = a.vs + kv * a.cap;
-  const int nj = min(2, max(0, nh - 2 * wave));          // heads of this wave (uniform)
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f}, o[2][16];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[j][i] = 0.f;
-  if (nj > 0) {
-    // the next token's record words and scales are loaded one iteration ahead
-    int t = tok0 + slot;
-    const int tl = t < tok_end ? t : tok0;                 // an in-range token for idle slots
-    uint2 rk = lm3_raw(kc + (int64_t)tl * kRec, e), rv = lm3_raw(vc + (int64_t)tl * kRec, e);
-    float sk = ksc[tl], sv = vsc[tl];
-    for (; t < tok_end; t += 8) {
-      const int tn = t + 8 < tok_end ? t + 8 : t;
-      const uint2 nk = lm3_raw(kc + (int64_t)tn * kRec, e), nv = lm3_raw(vc + (int64_t)tn * kRec, e);
-      const float nsk = ksc[tn], nsv = vsc[tn];
-      float kvv[16], vvv[16];
-      lm3_values(rk, e, kvv);
-      lm3_values(rv, e, vvv);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (j < nj) {
-          const float4* qp = reinterpret_cast<const float4*>(&qs[2 * wave + j][16 * e]);
-          float dot = 0.f;
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const float4 qv = qp[q4];
-            dot = fmaf(qv.x, kvv[4 * q4], dot);
-            dot = fmaf(qv.y, kvv[4 * q4 + 1], dot);
-            dot = fmaf(qv.z, kvv[4 * q4 + 2], dot);
-            dot = fmaf(qv.w, kvv[4 * q4 + 3], dot);
-          }
-          dot += dpp_xor1(dot);
-          dot += dpp_xor2(dot);
-          dot += swz_xor4(dot);
-          const float z = dot * sk;                       // score in log2 units
-          const float mn = fmaxf(m[j], z);
-          const float f = __builtin_amdgcn_exp2f(m[j] - mn);
-          const float p = __builtin_amdgcn_exp2f(z - mn);
-          l[j] = fmaf(l[j], f, p);
-          const float pv = p * sv;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[j][i] = fmaf(o[j][i], f, pv * vvv[i]);
-          m[j] = mn;
-        }
-      }
-      rk = nk;
-      rv = nv;
-      sk = nsk;
-      sv = nsv;
-    }
-  }
-  // merge the eight token slots (lanes e, e+8, ..., e+56), write this wave's heads
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    if (j >= nj) continue;                                 // uniform
-    float M = m[j];
-#pragma unroll
-    for (int d = 8; d < 64; d <<= 1) M = fmaxf(M, __shfl_xor(M, d, 64));
-    const float f = m[j] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[j] - M);
-    float L = l[j] * f;
-#pragma unroll
-    for (int d = 8; d < 64; d <<= 1) L += __shfl_xor(L, d, 64);
-    float ov[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      ov[i] = o[j][i] * f;
-#pragma unroll
-      for (int d = 8; d < 64; d <<= 1) ov[i] += __shfl_xor(ov[i], d, 64);
-    }
-    if (slot == 0) {
-      const int64_t pidx = (int64_t)(h0 + 2 * wave + j) * a.x_max + x;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) a.part_o[pidx * 128 + 16 * e + i] = ov[i];
-      if (e == 0) {
-        a.part_ml[pidx * 2] = M;
-        a.part_ml[pidx * 2 + 1] = L;
-      }
     }
   }
 }
@@ -1499,7 +1388,8 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.head_groups = geo.head_groups;
   k.cap = a.cache_cap;
   // the plan fills one round of work-groups: 4-bit records run two per compute unit, not three
-  k.target = a.format == IQ_FMT_U4 ? (geo.target * 2 / kGroupsPerCU > 0 ? geo.target * 2 / kGroupsPerCU : 1) : geo.target;
+  const bool two = a.format == IQ_FMT_U4;
+  k.target = two ? (geo.target * 2 / kGroupsPerCU > 0 ? geo.target * 2 / kGroupsPerCU : 1) : geo.target;
   k.sm_log2 = sm * kLog2e;
   k.plan = plan;
   k.x_max = geo.x_max;
@@ -1518,7 +1408,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   else if (a.format == IQ_FMT_U4)
     hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U4>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_LM3)
-    hipLaunchKernelGGL(decode_lm3_kernel, grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_LM3>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_A3)
     hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_A3>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.positions)

@@ -216,12 +216,12 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
  * iq_decode_attention_format -- iq_decode_attention on a cache written by
  * iq_quantize_kv_format with the same format (codes [batch][n_kv_heads]
  * [cache_cap][16*b]).  Source: Abstract (attention on the packed tensors).
- * IQ_FMT_U3 runs the same kernels as iq_decode_attention; IQ_FMT_A3 (the
- * same records), IQ_FMT_U4 and IQ_FMT_U2 run variants of its matrix-core
- * kernel; IQ_FMT_LM3 runs a vector-unit kernel with the same split of the
- * context and the same combine.  IQ_FMT_A3 scales are (s, m) pairs,
- * float[batch][n_kv_heads][cache_cap][2], 8-byte aligned.  IQ_FMT_U4 allows
- * cache_cap <= 62914432 (= 0xF0000000 / 64 - 64).  Other arguments and errors as
+ * IQ_FMT_U3 runs the same kernels as iq_decode_attention; the other formats
+ * run variants of its matrix-core kernel (IQ_FMT_LM3 through tables of its
+ * levels) with the same split of the context and the same combine.
+ * IQ_FMT_A3 scales are (s, m) pairs, float[batch][n_kv_heads][cache_cap][2],
+ * 8-byte aligned.  IQ_FMT_U4 allows cache_cap <= 62914432 (= 0xF0000000 / 64
+ * - 64).  Other arguments and errors as
  * iq_decode_attention, with format in place of bits.
  */
 int iq_decode_attention_format(const void* q, int32_t q_dtype,
