@@ -1046,29 +1046,29 @@ void decode_split_kernel(DecodeKArgs a) {
   // packed as by the quantize kernel and stored into the cache.  The barrier below makes the
   // stores visible to the whole work-group, and every load of the cache is issued after it.
   if (kAppend && pos >= tok0 && pos < tok_end && wave == 1) {
-    const int side = (lane >> 3) & 1, e = lane & 7;
+    const int side = (lane >> 3) & 1, c = vec::chunk_of(lane & 7);
     float* fold = &sm.u.merge.o[2][0][0];   // [32][16] folded blocks; clear of wave 0's set-up data
-    if (lane < 32) vec::build_folded_block(rot + lane * 8, fold + lane * 16);
+    if (lane < 32) vec::build_folded_block(rot + lane * 8, fold + lane * 16, vec::chunk_sign(lane >> 2));
     __builtin_amdgcn_wave_barrier();
-    const float (&F)[4][16] = *reinterpret_cast<const float(*)[4][16]>(fold + 64 * e);
+    const float (&F)[4][16] = *reinterpret_cast<const float(*)[4][16]>(fold + 64 * c);
     float x[16];
     const void* src = side ? a.v_new : a.k_new;
-    const int64_t off = (int64_t)b * a.new_stride_seq + (int64_t)g * a.new_stride_head + 16 * e;
+    const int64_t off = (int64_t)b * a.new_stride_seq + (int64_t)g * a.new_stride_head + 16 * c;
     if (a.new_bf16)
       vec::load16<true>(src, off, lane < 16, x);
     else
       vec::load16<false>(src, off, lane < 16, x);
     unsigned g0, g1, w[3];
-    const float scale = vec::quantize8(x, F, e, g0, g1);
+    const float scale = vec::quantize8(x, F, c, g0, g1);
     vec::quarter_words(g0, g1, w);
     if (lane < 16) {
       const int64_t rec = kv * a.cap + pos;
-      if ((e & 1) == 0) {
-        unsigned* dst = reinterpret_cast<unsigned*>(const_cast<uint8_t*>(side ? a.vc : a.kc) + rec * 48 + 6 * e);
+      if ((c & 1) == 0) {
+        unsigned* dst = reinterpret_cast<unsigned*>(const_cast<uint8_t*>(side ? a.vc : a.kc) + rec * 48 + 6 * c);
 #pragma unroll
         for (int i = 0; i < 3; ++i) dst[i] = w[i];
       }
-      if (e == 0) const_cast<float*>(side ? a.vs : a.ks)[rec] = scale;
+      if (c == 0) const_cast<float*>(side ? a.vs : a.ks)[rec] = scale;
     }
   }
   __syncthreads();

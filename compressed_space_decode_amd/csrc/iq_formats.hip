@@ -17,7 +17,8 @@
 // Records: one little-endian bit stream of b bits per code, 16 b bytes.
 //
 // Work split as in the 3-bit quantize kernel: 8 lanes per vector, lane e holds
-// coordinates 16e..16e+15, i.e. the 2b bytes 2b*e .. 2b*e + 2b - 1 of the record.
+// chunk c = chunk_of(e), coordinates 16c..16c+15, i.e. the 2b bytes 2b*c .. 2b*c +
+// 2b - 1 of the record.
 #include "iq.h"
 #include "iq_internal.h"
 #include "iq_vector.h"
@@ -35,17 +36,17 @@ constexpr float kLM[8] = {-2.152f, -1.344f, -0.7560f, -0.2451f, 0.2451f, 0.7560f
 __device__ __forceinline__ float max8(float v) {
   v = fmaxf(v, vec::dpp_xor1(v));
   v = fmaxf(v, vec::dpp_xor2(v));
-  return fmaxf(v, vec::swz_xor4(v));
+  return fmaxf(v, vec::dpp_mirror8(v));
 }
 __device__ __forceinline__ float min8(float v) {
   v = fminf(v, vec::dpp_xor1(v));
   v = fminf(v, vec::dpp_xor2(v));
-  return fminf(v, vec::swz_xor4(v));
+  return fminf(v, vec::dpp_mirror8(v));
 }
 __device__ __forceinline__ float sum8(float v) {
   v += vec::dpp_xor1(v);
   v += vec::dpp_xor2(v);
-  return v + vec::swz_xor4(v);
+  return v + vec::dpp_mirror8(v);
 }
 
 // Codes of the lane's 16 rotated values; returns the vector's scale (s or sigma) and, for the
@@ -107,16 +108,18 @@ __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunc
   const int h = blockIdx.y;
   const int64_t t_begin = (int64_t)blockIdx.x * kTokPerGroup;
   const int tid = threadIdx.x;
-  if (tid < 32) vec::build_folded_block(a.rot + (int64_t)s * a.rot_stride_seq + (int64_t)h * 256 + tid * 8, mats[tid]);
+  if (tid < 32)
+    vec::build_folded_block(a.rot + (int64_t)s * a.rot_stride_seq + (int64_t)h * 256 + tid * 8, mats[tid],
+                            vec::chunk_sign(tid >> 2));
   __syncthreads();
   const int lane = tid & 63;
-  const int e = lane & 7;
+  const int c = vec::chunk_of(lane & 7);   // coordinates 16c..16c+15
   const int vsub = (tid >> 6) * 8 + (lane >> 3);
   float F[4][16];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) F[j][i] = mats[4 * e + j][i];
+    for (int i = 0; i < 16; ++i) F[j][i] = mats[4 * c + j][i];
 
   for (int step = 0; step < kTokPerGroup / kVecPerStep; ++step) {
     const int64_t t0 = t_begin + (int64_t)step * kVecPerStep;
@@ -128,42 +131,42 @@ __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunc
       const QuantSide side = a.side[sd];
       if (side.src == nullptr) continue;          // uniform
       float x[16], y[16];
-      vec::load16<kBF16>(side.src, (int64_t)s * a.stride_seq + (int64_t)h * a.stride_head + t * a.stride_tok + 16 * e,
+      vec::load16<kBF16>(side.src, (int64_t)s * a.stride_seq + (int64_t)h * a.stride_head + t * a.stride_tok + 16 * c,
                          valid, x);
-      vec::rotate8(x, F, e, y);
-      unsigned c[16];
-      const float2 scale = codes16<kFmt>(y, c);
+      vec::rotate8(x, F, c, y);
+      unsigned q[16];
+      const float2 scale = codes16<kFmt>(y, q);
       const int64_t rec = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset + t;
       uint8_t* dst = side.codes + rec * kRec;
       if constexpr (kBits == 2) {
         unsigned w = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w |= c[i] << (2 * i);
-        if (valid) reinterpret_cast<unsigned*>(dst)[e] = w;
+        for (int i = 0; i < 16; ++i) w |= q[i] << (2 * i);
+        if (valid) reinterpret_cast<unsigned*>(dst)[c] = w;
       } else if constexpr (kBits == 4) {
         unsigned w0 = 0, w1 = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          w0 |= c[i] << (4 * i);
-          w1 |= c[8 + i] << (4 * i);
+          w0 |= q[i] << (4 * i);
+          w1 |= q[8 + i] << (4 * i);
         }
-        if (valid) reinterpret_cast<uint2*>(dst)[e] = make_uint2(w0, w1);
+        if (valid) reinterpret_cast<uint2*>(dst)[c] = make_uint2(w0, w1);
       } else {
         unsigned g0 = 0, g1 = 0, w[3];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          g0 |= c[k] << (3 * k);
-          g1 |= c[8 + k] << (3 * k);
+          g0 |= q[k] << (3 * k);
+          g1 |= q[8 + k] << (3 * k);
         }
         vec::quarter_words(g0, g1, w);          // every lane runs it (cross-lane move)
-        if (valid && (e & 1) == 0) {
-          unsigned* q = reinterpret_cast<unsigned*>(dst + 12 * (e >> 1));
-          q[0] = w[0];
-          q[1] = w[1];
-          q[2] = w[2];
+        if (valid && (c & 1) == 0) {
+          unsigned* d = reinterpret_cast<unsigned*>(dst + 12 * (c >> 1));
+          d[0] = w[0];
+          d[1] = w[1];
+          d[2] = w[2];
         }
       }
-      if (valid && e == 0) {
+      if (valid && c == 0) {
         if constexpr (kFmt == IQ_FMT_A3)
           reinterpret_cast<float2*>(side.scales)[rec] = scale;
         else
