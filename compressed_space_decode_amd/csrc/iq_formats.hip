@@ -121,58 +121,77 @@ __global__ __launch_bounds__(kThreads) void quantize_format_kernel(QuantizeLaunc
 #pragma unroll
     for (int i = 0; i < 16; ++i) F[j][i] = mats[4 * c + j][i];
 
-  for (int step = 0; step < kTokPerGroup / kVecPerStep; ++step) {
-    const int64_t t0 = t_begin + (int64_t)step * kVecPerStep;
-    if (t0 >= a.n_tokens) break;                  // uniform over the work-group
-    const int64_t t = t0 + vsub;
-    const bool valid = t < a.n_tokens;
+  const int64_t n_steps = (min((int64_t)kTokPerGroup, a.n_tokens - t_begin) + kVecPerStep - 1) / kVecPerStep;
+  // (step, side) items with the next input loaded after the current one is unpacked, as in the
+  // 3-bit quantize kernel
+  const bool two = a.side[0].src != nullptr && a.side[1].src != nullptr;
+  const QuantSide sa = a.side[0].src != nullptr ? a.side[0] : a.side[1];   // even items
+  const QuantSide sb = a.side[1].src != nullptr ? a.side[1] : a.side[0];   // odd items
+  const int64_t n_items = two ? 2 * n_steps : n_steps;
+  constexpr int kElem = kBF16 ? 2 : 4;
+  const int64_t in_step = (int64_t)kVecPerStep * a.stride_tok * kElem;
+  int64_t tok = t_begin + vsub;
+  const int64_t off_first =
+      ((int64_t)s * a.stride_seq + (int64_t)h * a.stride_head + 16 * c + t_begin * a.stride_tok) * kElem;
+  int64_t off = off_first + (int64_t)vsub * a.stride_tok * kElem;
+  const int64_t rec0 = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset;
+  vec::Raw16<kBF16> raw;
+  vec::load_raw16<kBF16>(static_cast<const char*>(sa.src) + (tok < a.n_tokens ? off : off_first), raw);
+#pragma unroll 1
+  for (int64_t i = 0; i < n_items; ++i) {
+    const bool odd = two && (i & 1);
+    const bool adv = !two || odd;
+    const int64_t tok_n = adv ? tok + kVecPerStep : tok;
+    const int64_t off_n = adv ? off + in_step : off;
+    float x[16], y[16];
+    vec::unpack16<kBF16>(raw, x);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool more = i + 1 < n_items && tok_n < a.n_tokens;
+    vec::load_raw16<kBF16>(static_cast<const char*>(two && !odd ? sb.src : sa.src) + (more ? off_n : off_first), raw);
+    __builtin_amdgcn_sched_barrier(0);
+    vec::rotate8(x, F, c, y);
+    unsigned q[16];
+    const float2 scale = codes16<kFmt>(y, q);
+    const bool valid = tok < a.n_tokens;
+    const int64_t rec = rec0 + tok;
+    uint8_t* dst = (odd ? sb.codes : sa.codes) + rec * kRec;
+    if constexpr (kBits == 2) {
+      unsigned w = 0;
 #pragma unroll
-    for (int sd = 0; sd < 2; ++sd) {
-      const QuantSide side = a.side[sd];
-      if (side.src == nullptr) continue;          // uniform
-      float x[16], y[16];
-      vec::load16<kBF16>(side.src, (int64_t)s * a.stride_seq + (int64_t)h * a.stride_head + t * a.stride_tok + 16 * c,
-                         valid, x);
-      vec::rotate8(x, F, c, y);
-      unsigned q[16];
-      const float2 scale = codes16<kFmt>(y, q);
-      const int64_t rec = ((int64_t)s * a.n_heads + h) * a.cache_cap + a.tok_offset + t;
-      uint8_t* dst = side.codes + rec * kRec;
-      if constexpr (kBits == 2) {
-        unsigned w = 0;
+      for (int k = 0; k < 16; ++k) w |= q[k] << (2 * k);
+      if (valid) reinterpret_cast<unsigned*>(dst)[c] = w;
+    } else if constexpr (kBits == 4) {
+      unsigned w0 = 0, w1 = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) w |= q[i] << (2 * i);
-        if (valid) reinterpret_cast<unsigned*>(dst)[c] = w;
-      } else if constexpr (kBits == 4) {
-        unsigned w0 = 0, w1 = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          w0 |= q[i] << (4 * i);
-          w1 |= q[8 + i] << (4 * i);
-        }
-        if (valid) reinterpret_cast<uint2*>(dst)[c] = make_uint2(w0, w1);
-      } else {
-        unsigned g0 = 0, g1 = 0, w[3];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          g0 |= q[k] << (3 * k);
-          g1 |= q[8 + k] << (3 * k);
-        }
-        vec::quarter_words(g0, g1, w);          // every lane runs it (cross-lane move)
-        if (valid && (c & 1) == 0) {
-          unsigned* d = reinterpret_cast<unsigned*>(dst + 12 * (c >> 1));
-          d[0] = w[0];
-          d[1] = w[1];
-          d[2] = w[2];
-        }
+      for (int k = 0; k < 8; ++k) {
+        w0 |= q[k] << (4 * k);
+        w1 |= q[8 + k] << (4 * k);
       }
-      if (valid && c == 0) {
-        if constexpr (kFmt == IQ_FMT_A3)
-          reinterpret_cast<float2*>(side.scales)[rec] = scale;
-        else
-          side.scales[rec] = scale.x;
+      if (valid) reinterpret_cast<uint2*>(dst)[c] = make_uint2(w0, w1);
+    } else {
+      unsigned g0 = 0, g1 = 0, w[3];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        g0 |= q[k] << (3 * k);
+        g1 |= q[8 + k] << (3 * k);
+      }
+      vec::quarter_words(g0, g1, w);          // every lane runs it (cross-lane move)
+      if (valid && (c & 1) == 0) {
+        unsigned* d = reinterpret_cast<unsigned*>(dst + 12 * (c >> 1));
+        d[0] = w[0];
+        d[1] = w[1];
+        d[2] = w[2];
       }
     }
+    if (valid && c == 0) {
+      float* scales = odd ? sb.scales : sa.scales;
+      if constexpr (kFmt == IQ_FMT_A3)
+        reinterpret_cast<float2*>(scales)[rec] = scale;
+      else
+        scales[rec] = scale.x;
+    }
+    tok = tok_n;
+    off = off_n;
   }
 }
 

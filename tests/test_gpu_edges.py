@@ -47,6 +47,34 @@ def test_quantize_ragged_tail_offset_and_untouched_cache(dtype):
     _check_all(W.to_f64(xin, dtype), params, rec[:, :, off:off + T], sc[:, :, off:off + T], "tail")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_k_and_v_together_match_each_alone(dtype):
+    # one call with both sides interleaves K and V vectors in the kernel's loop; the K-only and
+    # V-only calls take the one-side path.  Ragged token count (not a multiple of 32 or 256).
+    rng = np.random.default_rng(12)
+    n_seq, H, T, cap = 2, 3, 301, 320
+    k = rng.standard_normal((n_seq, H, T, 128)).astype(np.float32)
+    v = rng.standard_normal((n_seq, H, T, 128)).astype(np.float32) * 3.0
+    if dtype == "bf16":
+        k, v = W.f32_to_bf16_bits(k), W.f32_to_bf16_bits(v)
+    params = _params(rng, n_seq, H)
+    rot = torch.from_numpy(params).cuda()
+    kt, vt = P.torch_input(k, dtype), P.torch_input(v, dtype)
+    kc, ks = P.empty_cache(n_seq, H, cap, poison=True)
+    vc, vs = P.empty_cache(n_seq, H, cap, poison=True)
+    iq.quantize_kv(kt, vt, rot, kc, ks, vc, vs, tok_offset=7)
+    kc1, ks1 = P.empty_cache(n_seq, H, cap, poison=True)
+    vc1, vs1 = P.empty_cache(n_seq, H, cap, poison=True)
+    iq.quantize_kv(kt, None, rot, kc1, ks1, None, None, tok_offset=7)
+    iq.quantize_kv(None, vt, rot, None, None, vc1, vs1, tok_offset=7)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc1) and torch.equal(ks, ks1)
+    assert torch.equal(vc, vc1) and torch.equal(vs, vs1)
+    rec, sc = vc.cpu().numpy(), vs.cpu().numpy()
+    assert np.all(rec[:, :, :7] == 0xFF) and np.all(rec[:, :, 7 + T:] == 0xFF)
+    _check_all(W.to_f64(v, dtype), params, rec[:, :, 7:7 + T], sc[:, :, 7:7 + T], "V " + dtype)
+
+
 def test_quantize_one_token_appends_match_bulk():
     rng = np.random.default_rng(6)
     H, T = 2, 40
