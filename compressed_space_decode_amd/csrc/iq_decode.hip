@@ -241,13 +241,16 @@ struct DecodeKArgs {
   const float* rot;
   int64_t rot_stride_b;
   const int32_t* seq_lens;
-  int batch, Hq, Hkv, G, head_groups;   // batch: sequences times query tokens (work-item sequences)
-  int q_tokens;           // query tokens per cached sequence; sequence b reads cache b / q_tokens
+  int batch, Hq, Hkv, G, head_groups;   // batch: work-item sequences (see LenSource)
+  int q_tokens;           // query tokens per cached sequence
+  int q_group;            // query tokens per work-item sequence (1, or the multi-token kernel's kQ)
+  int n_groups;           // work-item sequences per cached sequence: ceil(q_tokens / q_group)
   int64_t cap;
   int target;             // most (sequence, chunk) pairs per (KV head, head group) column
   float sm_log2;          // softmax scale times log2(e)
   int* plan;              // [0]: chunk size; [64 + b]: index of sequence b's first chunk
-  int x_max;              // grid width: work items per column
+  int x_max;              // partial rows per query head: work items per column (times kQ in the
+                          // multi-token kernel, whose work item x writes rows x kQ + i)
   int guess_per_seq;      // chunks per sequence when every length is cap (a guess, see below)
   float* part_o;          // [Hq][x_max][128], x = index of the (sequence, chunk) pair
   float* part_ml;         // [Hq][x_max][2]  (max in log2 units, sum)
@@ -267,22 +270,26 @@ struct LenSource {
   const int32_t* positions;   // fused append: length = position + 1 (0 outside the cache)
   const int32_t* seq_lens;    // else the given lengths clamped to [0, cap]; NULL: every length cap
   int cap, batch;
-  int q_tokens;               // several query tokens per cached sequence: sequence i is token
-                              // i % q_tokens of cache i / q_tokens and sees len - q_tokens + i % q_tokens + 1
+  // Several query tokens per cached sequence (causal: they are its last q_tokens positions, token t
+  // sees len - (q_tokens - 1 - t) of them): sequence i is group i % n_groups of cache i / n_groups,
+  // the group holding tokens q_group (i % n_groups) .. q_group (i % n_groups + 1) - 1, and its
+  // length is that of its last token.  q_group = 1: one sequence per token.
+  int q_tokens, q_group, n_groups;
 };
 
 // The stored value for sequence i (a position or a length; 0 when there is none), then its length.
 __device__ __forceinline__ int len_raw(const LenSource& s, int i) {
   const int32_t* src = s.positions ? s.positions : s.seq_lens;
   if (src == nullptr || i >= s.batch) return 0;
-  return src[s.q_tokens > 1 ? i / s.q_tokens : i];
+  return src[s.n_groups > 1 ? i / s.n_groups : i];
 }
 __device__ __forceinline__ int len_of(const LenSource& s, int i, int raw) {
   if (i >= s.batch) return 0;
   if (s.positions) return (raw >= 0 && raw < s.cap) ? raw + 1 : 0;
   int l = s.seq_lens ? (raw < 0 ? 0 : (raw > s.cap ? s.cap : raw)) : s.cap;
-  if (s.q_tokens > 1) {
-    l -= s.q_tokens - 1 - i % s.q_tokens;       // causal: the last q_tokens positions are the queries
+  if (s.q_tokens > 1) {                          // causal: the last q_tokens positions are the queries
+    const int later = s.q_tokens - (i % s.n_groups + 1) * s.q_group;   // tokens after the group
+    if (later > 0) l -= later;
     if (l < 0) l = 0;
   }
   return l;
@@ -891,7 +898,7 @@ void decode_split_kernel(DecodeKArgs a) {
   // says otherwise: the query and rotation loads then overlap the plan.
   // (the lengths are loaded first: memory loads complete in order, so the plan then waits for
   // them alone)
-  const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch, a.q_tokens};
+  const LenSource src{kAppend ? a.positions : nullptr, a.seq_lens, cap, a.batch, a.q_tokens, 1, a.q_tokens};
   const int raw0 = len_raw(src, lane);                       // sequences 0..63
   int b_guess = x / a.guess_per_seq;
   if (b_guess > a.batch - 1) b_guess = a.batch - 1;
@@ -1176,6 +1183,444 @@ void decode_split_kernel(DecodeKArgs a) {
   }
 }
 
+// ---------------- several query tokens per work-group ----------------
+// With several query tokens per cached sequence (iq_decode_attention_multi) the kernel above would
+// read and unpack every block once per token.  Here a work item is a chunk of a group of kMultiQ
+// consecutive query tokens: each 32-token block's K and V codes are unpacked once and multiplied by
+// every token's operand (one QK and one PV product per token), and each token keeps its own online
+// softmax; the V scale bound is shared.  Wave w rotates token w's queries.  3-bit records, no
+// append.  Two tokens per group: their accumulators fill 256 registers, two waves per SIMD (four
+// tokens need more than the 256 architectural registers and spill to the accumulation registers,
+// which measured slower than one token per work item).
+constexpr int kMultiQ = 2;                    // tokens per group (one per wave at set-up)
+constexpr int kMultiWavesPerSimd = 2;
+constexpr int kMultiRounds = 3;               // work items per column: three rounds of work-groups
+constexpr float kNoMax = -1e30f;              // running max before any score: finite, so a token
+                                              // with nothing to attend to in a chunk gets p = 0
+struct MultiLoopSmem {
+  char p[kMultiQ][kBlock * kPRow];            // P'' staging of each token
+  float sc[64];
+};
+struct MultiSetupSmem {
+  float qrot[kWaves][8][128];
+  float blk[32][16];
+  float qsum[kWaves][8];
+  int E[kWaves];
+};
+union MultiSmemU {
+  MergeSmem merge;
+  MultiLoopSmem loop[kWaves];
+  MultiSetupSmem setup;
+};
+struct MultiSmem {
+  uint4v qop[kMultiQ][4][64];                 // QK A operand of each token
+  MultiSmemU u;
+};
+
+template <int kQ>
+struct MultiState {
+  floatx4 O[kQ][8];
+  float m_run[kQ][2], thr[kQ][2], l_run[kQ][2], ls_run[kQ][2];
+  int vexp;
+  float vlim, pmul;
+};
+
+// process_block for kQ tokens (3-bit records).  lim[i]: token i attends to the block's tokens below
+// lim[i].  A token the group does not have runs too, with lim = the chunk start: every score is
+// masked, so its p and its products are zero (straight-line code, no per-token branches).
+template <bool kRefill, int kQ>
+__device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, int tok_end, const int (&lim)[kQ],
+                                                    int t_refill, const CacheBuffers& cb,
+                                                    const LaneOffsets& lo, bool vscale, MultiState<kQ>& st,
+                                                    const uint4v (&qop)[kMultiQ][4][64], const float (&c1)[kQ],
+                                                    const float (&c2)[kQ][2], MultiLoopSmem& ws, int lane, int n,
+                                                    int g4, unsigned pwr, unsigned prd) {
+  constexpr int kFmt = IQ_FMT_U3;
+  ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
+  // ---- QK of every token on the same unpacked codes ----
+  floatx4 S[kQ][2];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    unsigned u[16];
+    unpack_k<kFmt>(cur.kw[tt], u);
+    half8 kb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kb[k] = as_half8(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[i][k][lane]), kb[k], acc, 0, 0, 0);
+      S[i][tt] = acc;
+    }
+  }
+  // ---- V byte windows, as in process_block ----
+  unsigned vwin[4][3];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    unsigned gq[4];
+    gq[0] = cur.vw[tt][0];
+    gq[1] = __builtin_amdgcn_alignbyte(cur.vw[tt][1], cur.vw[tt][0], 3);
+    gq[2] = __builtin_amdgcn_alignbyte(cur.vw[tt][2], cur.vw[tt][1], 2);
+    gq[3] = cur.vw[tt][2] >> 8;
+    quad_transpose(gq, lane);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      unsigned* vw = vwin[2 * tt + p];
+      vw[0] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x05040100u);
+      vw[1] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x06050201u);
+      vw[2] = __builtin_amdgcn_perm(gq[2 * p + 1], gq[2 * p], 0x07060302u);
+    }
+  }
+  if (kRefill) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_block<kFmt>(cur, cb, t_refill, tok_end, lo);
+  }
+  // ---- scores; tokens past the chunk carry no V scale, tokens past lim[i] no score ----
+  const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
+  float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
+  const int rem = tok_end - t0;
+  if (n >= rem) sv0 = 0.f;
+  if (16 + n >= rem) sv1 = 0.f;
+  float z[kQ][2][2];
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    const int ri = lim[i] - t0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      z[i][j][0] = n < ri ? sk0 * fmaf(S[i][0][2 * j] + S[i][0][2 * j + 1], c1[i], -c2[i][j]) : -INFINITY;
+      z[i][j][1] = 16 + n < ri ? sk1 * fmaf(S[i][1][2 * j] + S[i][1][2 * j + 1], c1[i], -c2[i][j]) : -INFINITY;
+    }
+  }
+  const float svmax = fmaxf(sv0, sv1);
+  bool grow = svmax >= st.vlim;
+#pragma unroll
+  for (int i = 0; i < kQ; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) grow |= fmaxf(z[i][j][0], z[i][j][1]) > st.thr[i][j];
+  if (__any(grow)) {
+    const float vmax = row_max(svmax);
+    float ratio = 1.f;
+    if (vmax >= st.vlim) {
+      int ex;
+      frexpf(vmax, &ex);
+      ex = ex < -60 ? -60 : ex;
+      ratio = st.vexp == -200 ? 0.f : ldexpf(1.f, st.vexp - ex);
+      st.vexp = ex;
+      st.vlim = ldexpf(1.f, ex);
+      st.pmul = ldexpf(kPScale, -ex);
+    }
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float m_new = fmaxf(st.m_run[i][j], row_max(fmaxf(z[i][j][0], z[i][j][1])));
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run[i][j] - m_new);
+        st.l_run[i][j] *= alpha;
+        st.ls_run[i][j] *= alpha * ratio;
+        st.m_run[i][j] = m_new;
+        st.thr[i][j] = m_new + kHeadroom;
+        const float f = alpha * ratio;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          st.O[i][nt][2 * j] *= f;
+          st.O[i][nt][2 * j + 1] *= f;
+        }
+      }
+    }
+  }
+  // ---- P'' of each token, staged and read back transposed; PV on the shared V windows ----
+  const float svm[2] = {sv0 * st.pmul, sv1 * st.pmul};
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      _Float16 h4[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float p = __builtin_amdgcn_exp2f(z[i][j][tt] - st.m_run[i][j]);
+        st.l_run[i][j] += p;
+        const float pp = p * svm[tt];
+        st.ls_run[i][j] += pp;
+        const _Float16 hi = (_Float16)pp;
+        h4[2 * j] = hi;
+        h4[2 * j + 1] = (_Float16)(pp - (float)hi);
+      }
+      *reinterpret_cast<short4v*>(ws.p[i] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, h4);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  half8 pop[kQ];
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[i] + prd));
+    const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[i] + prd + 16 * kPRow));
+    pop[i] = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const unsigned m = VField<kFmt>::mask(j);
+    const int wj = VField<kFmt>::win(j);
+    const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) st.O[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop[i], vb, st.O[i][j], 0, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <int kQ>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMultiWavesPerSimd, kMultiWavesPerSimd)))
+void decode_multi_kernel(DecodeKArgs a) {
+  static_assert(kQ <= kMultiQ && kQ <= kWaves, "one token per set-up wave");
+  constexpr int kFmt = IQ_FMT_U3;
+  constexpr int kRec = 48;
+  __shared__ MultiSmem sm;
+  const int x = blockIdx.y;          // (group sequence, chunk) pair
+  const int g = blockIdx.x / a.head_groups;
+  const int hg = blockIdx.x % a.head_groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cap = (int)a.cap;
+  const int h0 = g * a.G + hg * 8;
+  const int nh = (a.G - hg * 8) < 8 ? (a.G - hg * 8) : 8;
+  // work-item sequence b: group b % n_groups (tokens kQ (b % n_groups) ...) of cache b / n_groups,
+  // with the length of its last token
+  const LenSource src{nullptr, a.seq_lens, cap, a.batch, a.q_tokens, kQ, a.n_groups};
+  const int l0 = len_at(src, lane);
+  const ChunkPlan plan = plan_chunks(src, l0, a.target, x, lane);
+  if (plan.b < 0) return;                                    // uniform: past the last chunk
+  const int b = plan.b;
+  const int len = plan.len;          // > 0
+  if (tid == 0 && blockIdx.x == 0) {
+    if (x == 0) a.plan[0] = plan.chunk;
+    if (plan.j == 0) a.plan[64 + b] = x;
+  }
+  const int tok0 = plan.j * plan.chunk;
+  if (tok0 >= len) return;                                   // uniform; never taken
+  const int tok_end = (tok0 + plan.chunk < len) ? tok0 + plan.chunk : len;
+  const int bc = b / a.n_groups;
+  const int t_first = (b % a.n_groups) * kQ;                 // the group's first query token
+  const int nq = (a.q_tokens - t_first) < kQ ? (a.q_tokens - t_first) : kQ;   // its tokens (uniform)
+  int lim[kQ];                       // token i (length len - (nq - 1 - i)) attends below lim[i]
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    const int li = len - (nq - 1 - i);
+    lim[i] = i < nq ? (li < tok_end ? li : tok_end) : tok0;
+  }
+  const int64_t kv = (int64_t)bc * a.Hkv + g;
+  const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
+
+  CacheBuffers cb;
+  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
+  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
+  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, cap * 4, kBufferConfig);
+  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, cap * 4, kBufferConfig);
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+  LaneOffsets lo;
+  lo.kcode = (unsigned)(n * kRec + kRec / 4 * g4);
+  lo.vcode = (unsigned)(kRec * (4 * g4 + (lane & 3)) + kRec / 4 * ((lane >> 2) & 3));
+  lo.scale = (unsigned)(4 * (n + 16 * (g4 & 1)));
+  const bool vscale = g4 >= 2;
+  lo.vside = vscale;
+
+  const int step = kWaves * kBlock;
+  int t0 = tok0 + wave * kBlock;
+  BlockData<3> buf, buf2, buf3;
+  load_block<kFmt>(buf, cb, t0, tok_end, lo);
+  load_block<kFmt>(buf2, cb, t0 + step, tok_end, lo);
+
+  // ---------------- set-up: wave w rotates query token t_first + w ----------------
+  MultiSetupSmem& ss = sm.u.setup;
+  if (lane < 8) build_block(rot + (8 * wave + lane) * 8, ss.blk[8 * wave + lane]);
+  __syncthreads();
+  if (wave < nq) {                                           // uniform
+    const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
+    const bool have = qi < nh;
+    const int64_t off = (((int64_t)bc * a.q_tokens + t_first + wave) * a.Hq + h0 + (have ? qi : 0)) * 128 + 16 * qe;
+    float xq[16];
+    if (a.q_bf16) {
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
+      const uint4 q0 = qp[0], q1 = qp[1];
+      const unsigned w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        xq[2 * i] = __uint_as_float(w[i] << 16);
+        xq[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* qp = reinterpret_cast<const float4*>(static_cast<const float*>(a.q) + off);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 v = qp[i];
+        xq[4 * i] = v.x; xq[4 * i + 1] = v.y; xq[4 * i + 2] = v.z; xq[4 * i + 3] = v.w;
+      }
+    }
+    if (!have) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xq[i] = 0.f;
+    }
+    {
+      // Sylvester Hadamard (unnormalised), as in the single-token set-up
+      const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xq[i] = fmaf(sg1, xq[i], dpp_xor1(xq[i]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xq[i] = fmaf(sg2, xq[i], dpp_xor2(xq[i]));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xq[i] = fmaf(sg4, xq[i], swz_xor4(xq[i]));
+#pragma unroll
+      for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i & m) == 0) {
+            const float u = xq[i], v = xq[i + m];
+            xq[i] = u + v;
+            xq[i + m] = u - v;
+          }
+    }
+    float qamax = 0.f, qs = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float* M = ss.blk[4 * qe + j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float y = (M[4 * r] * xq[4 * j] + M[4 * r + 1] * xq[4 * j + 1] + M[4 * r + 2] * xq[4 * j + 2] +
+                         M[4 * r + 3] * xq[4 * j + 3]) * kInvSqrtD;
+        ss.qrot[wave][qi][16 * qe + 4 * j + r] = y;
+        qamax = fmaxf(qamax, fabsf(y));
+        qs += y;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) qamax = fmaxf(qamax, wave_xor(qamax, m));
+    qs += dpp_xor1(qs);
+    qs += dpp_xor2(qs);
+    qs += swz_xor4(qs);
+    int E = 0;
+    if (qamax > 0.f) {
+      int ex;
+      frexpf(qamax, &ex);
+      E = 14 - ex;
+    }
+    if (qe == 0) ss.qsum[wave][qi] = qs;
+    if (lane == 0) ss.E[wave] = E;
+    __builtin_amdgcn_wave_barrier();
+    const int head = n >> 1, part = n & 1;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      _Float16 hv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sl = 8 * kb + e;
+        const float v = ldexpf(ss.qrot[wave][head][32 * g4 + slot_coord_f<kFmt>(sl)], E - slot_pow_f<kFmt>(sl));
+        const _Float16 hi = (_Float16)v;
+        hv[e] = part ? (_Float16)(v - (float)hi) : hi;
+      }
+      sm.qop[wave][kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+    }
+  }
+  __syncthreads();
+  float c1[kQ], c2[kQ][2];
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    const bool in = i < nq;
+    c1[i] = in ? a.sm_log2 * ldexpf(1.f, 24 - ss.E[i]) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) c2[i][j] = in ? a.sm_log2 * 3.5f * ss.qsum[i][2 * g4 + j] : 0.f;
+  }
+  __syncthreads();                   // the set-up area is staging space from here on
+  MultiLoopSmem& ws = sm.u.loop[wave];
+  const unsigned pwr = (unsigned)(n * kPRow + 8 * g4);
+  const unsigned prd = (unsigned)((4 * g4 + (n >> 2)) * kPRow + 8 * (n & 3));
+
+  MultiState<kQ> st;
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) st.O[i][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      st.m_run[i][j] = kNoMax;
+      st.thr[i][j] = kNoMax;
+      st.l_run[i][j] = 0.f;
+      st.ls_run[i][j] = 0.f;
+    }
+  }
+  st.vexp = -200;
+  st.vlim = 0.f;                     // the first block always rescales
+  st.pmul = 0.f;
+
+  while (t0 < tok_end) {            // uniform
+    progress_priority(t0 - tok0, tok_end - tok0);
+    load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    process_block_multi<true, kQ>(buf, t0, tok_end, lim, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
+                                  n, g4, pwr, prd);
+    t0 += step;
+    if (t0 >= tok_end) break;
+    process_block_multi<true, kQ>(buf2, t0, tok_end, lim, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                                  lane, n, g4, pwr, prd);
+    t0 += step;
+    if (t0 >= tok_end) break;
+    process_block_multi<false, kQ>(buf3, t0, tok_end, lim, 0, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane, n, g4,
+                                   pwr, prd);
+    t0 += step;
+  }
+
+  // ---------------- per-token results: merge the 4 waves, write the token's partial row ----------------
+  const float back = ldexpf(1.f / kPScale, st.vexp);
+  __syncthreads();                     // every wave is done with the loop smem
+#pragma unroll
+  for (int i = 0; i < kQ; ++i) {
+    if (i >= nq) continue;             // uniform
+    float l_tot[2], ls_tot[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      l_tot[j] = row_sum(st.l_run[i][j]);
+      ls_tot[j] = row_sum(st.ls_run[i][j]);
+    }
+    if (n == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sm.u.merge.m[wave][2 * g4 + j] = st.m_run[i][j];
+        sm.u.merge.l[wave][2 * g4 + j] = l_tot[j];
+      }
+    }
+#pragma unroll
+    for (int j8 = 0; j8 < 8; ++j8) {
+      const int coord = 8 * n + j8;
+      const float up = (float)(1 << (24 - VField<kFmt>::pos(j8)));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sm.u.merge.o[wave][2 * g4 + j][coord] =
+            back * fmaf(st.O[i][j8][2 * j] + st.O[i][j8][2 * j + 1], up, -3.5f * ls_tot[j]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < nh * 128; idx += kThreads) {
+      const int hrow = idx >> 7, d = idx & 127;
+      float M = kNoMax;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hrow]);
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float f = __builtin_amdgcn_exp2f(sm.u.merge.m[w][hrow] - M);
+        L += f * sm.u.merge.l[w][hrow];
+        acc += f * sm.u.merge.o[w][hrow][d];
+      }
+      const int64_t pidx = (int64_t)(h0 + hrow) * a.x_max + (int64_t)x * kQ + i;
+      a.part_o[pidx * 128 + d] = acc;
+      if (d == 0) {
+        a.part_ml[pidx * 2] = M;
+        a.part_ml[pidx * 2 + 1] = L;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 struct CombineArgs {
   const float* part_o;
   const float* part_ml;
@@ -1186,6 +1631,8 @@ struct CombineArgs {
   const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
   int Hq, G;
   int q_tokens;                 // as in the split kernel
+  int q_group;                  // 1, or the multi-token kernel's kQ: the partial rows of query token t
+  int n_groups;                 // of a sequence are x kQ + t % kQ for the work items x of its group
   int64_t cap;
   int x_max;                    // partial rows per query head
   float* out;
@@ -1203,25 +1650,30 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the plan is read together with the length (both entries exist for every sequence; they are
   // used only when the sequence has tokens, and then the split kernel wrote them)
-  const int chunk = a.plan[0];
-  const int x0 = a.plan[64 + b];
-  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, a.q_tokens}, b);
+  // output row b is query token b % q_tokens of cache b / q_tokens; its chunks are the work items
+  // of work-item sequence sq, partial rows x rs + ri (rs = 1, ri = 0 with one token per sequence)
   const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;
+  const int tq = a.q_tokens > 1 ? b % a.q_tokens : 0;
+  const int sq = bc * a.n_groups + tq / a.q_group, rs = a.q_group, ri = tq % a.q_group;
+  const int chunk = a.plan[0];
+  const int x0 = a.plan[64 + sq];
+  const int len =
+      len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, a.q_tokens, 1, a.q_tokens}, b);
   float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
   if (len == 0) {                       // an empty sequence attends to nothing
     outp[tid] = 0.f;
     return;
   }
-  int nvalid = (len + chunk - 1) / chunk;         // <= kMaxChunks and x0 + nvalid <= x_max by the
-  nvalid = min(nvalid, min(kMaxChunks, a.x_max - x0));   // plan; the bound keeps every read in range
-  const int64_t first = (int64_t)h * a.x_max + x0;   // partial row of chunk 0; chunks are adjacent
-  const float* ml = a.part_ml + first * 2;
+  int nvalid = (len + chunk - 1) / chunk;         // <= kMaxChunks and x0 + nvalid <= x_max / rs by
+  nvalid = min(nvalid, min(kMaxChunks, a.x_max / rs - x0));   // the plan; the bound keeps every read in range
+  const int64_t first = (int64_t)h * a.x_max + (int64_t)x0 * rs + ri;   // partial row of chunk 0; chunk c
+  const float* ml = a.part_ml + first * 2;                             // is rs rows further
   if (nvalid <= kFewChunks) {           // uniform: every thread loads all (max, sum) pairs and its partials at once
     const float* po = a.part_o + first * 128 + tid;
     float mv[kFewChunks], lv[kFewChunks], ov[kFewChunks];
 #pragma unroll
     for (int c = 0; c < kFewChunks; ++c) {
-      const int cc = c < nvalid ? c : nvalid - 1;      // in range; weight 0 below
+      const int cc = (c < nvalid ? c : nvalid - 1) * rs;   // in range; weight 0 below
       mv[c] = ml[2 * cc];
       lv[c] = ml[2 * cc + 1];
       ov[c] = po[(int64_t)cc * 128];
@@ -1241,14 +1693,14 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     y[tid] = acc / L;
   } else if (wave == 0) {               // weights 2^(m_c - M) and 1/L
     float M = -INFINITY;
-    for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c]);
+    for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c * rs]);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, wave_xor(M, m));
     float L = 0.f;
     for (int c = lane; c < nvalid; c += 64) {
-      const float e = __builtin_amdgcn_exp2f(ml[2 * c] - M);
+      const float e = __builtin_amdgcn_exp2f(ml[2 * c * rs] - M);
       wgt[c] = e;
-      L = fmaf(e, ml[2 * c + 1], L);
+      L = fmaf(e, ml[2 * c * rs + 1], L);
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) L += wave_xor(L, m);
@@ -1263,9 +1715,9 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     int c = 0;
     for (; c + 8 <= nvalid; c += 8) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(wgt[c + u], po[(int64_t)(c + u) * 128], acc[u]);
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(wgt[c + u], po[(int64_t)(c + u) * rs * 128], acc[u]);
     }
-    for (; c < nvalid; ++c) acc[0] = fmaf(wgt[c], po[(int64_t)c * 128], acc[0]);
+    for (; c < nvalid; ++c) acc[0] = fmaf(wgt[c], po[(int64_t)c * rs * 128], acc[0]);
     y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
   }
   __syncthreads();
@@ -1356,7 +1808,15 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
     geo.guess_per_seq = (int)((cache_cap + c - 1) / c);
   }
   geo.plan_bytes = 256 + ((int64_t)batch * 4 + 255) / 256 * 256;
-  const int64_t parts = (int64_t)geo.x_max * n_q_heads;
+  // partial rows per query head: x_max, or, when batch counts the query tokens of
+  // iq_decode_attention_multi (B sequences of Q >= 2 tokens), kMultiQ rows for each work item of the
+  // multi-token kernel: its target, or one per group of kMultiQ tokens
+  // (B ceil(Q / kMultiQ) kMultiQ <= 2 B Q = 2 batch)
+  int64_t rows = geo.x_max;
+  const int64_t multi_target = (int64_t)kMultiRounds * kMultiWavesPerSimd * device_cu_count() / columns;
+  if (kMultiQ * multi_target > rows) rows = kMultiQ * multi_target;
+  if (2 * (int64_t)batch > rows) rows = 2 * (int64_t)batch;
+  const int64_t parts = rows * n_q_heads;
   geo.workspace_bytes = geo.plan_bytes + parts * 128 * 4 + parts * 2 * 4;
   return geo;
 }
@@ -1370,6 +1830,8 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   const float sm = a.sm_scale > 0.f ? a.sm_scale : kInvSqrtD;
 
   DecodeKArgs k{};
+  k.q_group = 1;
+  k.n_groups = a.q_tokens;
   k.q = a.q;
   k.q_bf16 = a.q_bf16;
   k.kc = a.k_codes;
@@ -1403,7 +1865,31 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_stride_seq = a.new_stride_seq;
   k.new_stride_head = a.new_stride_head;
   const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)geo.x_max, 1u);
-  if (a.format == IQ_FMT_U2)
+  // several query tokens (3-bit records): groups of kMultiQ tokens share each block's unpacked
+  // codes; partial rows x kMultiQ + i.  The plan aims at three rounds of work-groups: with one
+  // chunk per (sequence, token group) a single round left compute units idle.
+  const bool multi = a.q_tokens > 1 && a.format == IQ_FMT_U3 && a.positions == nullptr;
+  int xg = 0;
+  if (multi) {
+    const int ng = (a.q_tokens + kMultiQ - 1) / kMultiQ;
+    const int64_t vbg = (int64_t)a.batch * ng;
+    const int64_t columns = (int64_t)a.n_kv_heads * geo.head_groups;
+    int64_t tg = (int64_t)kMultiRounds * kMultiWavesPerSimd * device_cu_count() / columns;
+    const int64_t most = vbg * ((a.cache_cap + 255) / 256);
+    if (tg > most) tg = most;
+    if (tg > kMaxChunks) tg = kMaxChunks;
+    if (tg < 1) tg = 1;
+    xg = (int)(tg > vbg ? tg : vbg);
+    k.batch = (int)vbg;
+    k.q_group = kMultiQ;
+    k.n_groups = ng;
+    k.target = (int)tg;
+    k.x_max = xg * kMultiQ;
+    part_ml = part_o + (int64_t)k.x_max * a.n_q_heads * 128;
+    k.part_ml = part_ml;
+    hipLaunchKernelGGL((decode_multi_kernel<kMultiQ>), dim3((unsigned)columns, (unsigned)xg, 1u), dim3(kThreads), 0,
+                       stream, k);
+  } else if (a.format == IQ_FMT_U2)
     hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U2>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_U4)
     hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U4>), grid1, dim3(kThreads), 0, stream, k);
@@ -1429,8 +1915,10 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.Hq = a.n_q_heads;
   c.G = G;
   c.q_tokens = a.q_tokens;
+  c.q_group = multi ? kMultiQ : 1;
+  c.n_groups = multi ? (a.q_tokens + kMultiQ - 1) / kMultiQ : a.q_tokens;
   c.cap = a.cache_cap;
-  c.x_max = geo.x_max;
+  c.x_max = multi ? xg * kMultiQ : geo.x_max;
   c.out = a.out;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(vb * a.n_q_heads)), dim3(128), 0, stream, c);
   return hipGetLastError();
