@@ -49,6 +49,10 @@
 // coordinate) and the Lloyd-Max 3-bit format (the same records; its levels are not uniform, so
 // each code is looked up in byte tables of the levels' fp16 hi and lo parts with v_perm, and
 // every product takes two MFMAs, one per part).
+// Kernel 1b (decode_multi_kernel), several query tokens per sequence: the
+// same loop for a group of two consecutive query tokens, each block's codes
+// unpacked once and multiplied by both tokens' operands, each token with its
+// own causal length and online softmax.
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
 // log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
 // blocks followed by the Hadamard transform).
