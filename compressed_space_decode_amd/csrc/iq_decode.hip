@@ -619,18 +619,36 @@ __device__ __forceinline__ unsigned dpp_xor2_u(unsigned x) {
   return (unsigned)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);
 }
 __device__ __forceinline__ void quad_transpose(unsigned g[4], int lane) {
-  const bool odd = lane & 1, upper = lane & 2;
-  unsigned r0 = dpp_xor1_u(odd ? g[0] : g[1]), r1 = dpp_xor1_u(odd ? g[2] : g[3]);
-  g[0] = odd ? r0 : g[0];
-  g[1] = odd ? g[1] : r0;
-  g[2] = odd ? r1 : g[2];
-  g[3] = odd ? g[3] : r1;
-  r0 = dpp_xor2_u(upper ? g[0] : g[2]);
-  r1 = dpp_xor2_u(upper ? g[1] : g[3]);
-  g[0] = upper ? r0 : g[0];
-  g[1] = upper ? r1 : g[1];
-  g[2] = upper ? g[2] : r0;
-  g[3] = upper ? g[3] : r1;
+  (void)lane;
+  // Each round is four v_cndmask_b32 with a DPP source: dst = (lane keeps) ? own : partner's
+  // other register.  Round 1 (partner lane ^ 1): even lanes keep g[0], g[2] and take the partner's
+  // g[0], g[2] into g[1], g[3]; odd lanes the reverse.  Round 2 (partner lane ^ 2) does the same
+  // for the register pairs (0, 2) and (1, 3).  The masks go through VCC; the s_nop gives the DPP
+  // reads their wait states after the VALU writes of the sources.
+  const unsigned long long even = 0x5555555555555555ull, lower = 0x3333333333333333ull;
+  unsigned h[4];
+  asm("s_mov_b64 vcc, %8\n\t"
+      "s_nop 1\n\t"
+      "v_cndmask_b32_dpp %0, %5, %4, vcc quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %2, %7, %6, vcc quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "s_not_b64 vcc, vcc\n\t"
+      "s_nop 0\n\t"
+      "v_cndmask_b32_dpp %1, %4, %5, vcc quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %3, %6, %7, vcc quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf"
+      : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3])
+      : "v"(g[0]), "v"(g[1]), "v"(g[2]), "v"(g[3]), "s"(even)
+      : "vcc");
+  asm("s_mov_b64 vcc, %8\n\t"
+      "s_nop 1\n\t"
+      "v_cndmask_b32_dpp %0, %6, %4, vcc quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %1, %7, %5, vcc quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "s_not_b64 vcc, vcc\n\t"
+      "s_nop 0\n\t"
+      "v_cndmask_b32_dpp %2, %4, %6, vcc quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf\n\t"
+      "v_cndmask_b32_dpp %3, %5, %7, vcc quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf"
+      : "=&v"(g[0]), "=&v"(g[1]), "=&v"(g[2]), "=&v"(g[3])
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "s"(lower)
+      : "vcc");
 }
 
 
