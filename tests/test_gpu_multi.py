@@ -1,7 +1,8 @@
 """GPU parity of multi-token attention on the packed cache
 (iq_decode_attention_multi) against the oracle (multi_token_attention),
 through the C ABI: ragged lengths, a sequence shorter than the number of query
-tokens, fp32 queries with shared rotations, a 16-token chunk, and one token,
+tokens, fp32 queries with shared rotations, a 16-token chunk, an odd count with
+several chunks per token group, and one token,
 which must be exactly iq_decode_attention.  Tolerance as for decode
 (tests/_parity.py).
 """
@@ -57,6 +58,15 @@ def test_multi_token_ragged_lengths_and_short_sequence():
 def test_multi_token_f32_queries_shared_rotation_full_cache():
     rng = np.random.default_rng(62)
     _check(rng, 2, 3, 8, 4, 1500, None, qdtype="f32", shared=True, what="Q=3 f32 shared")
+
+
+def test_multi_token_odd_count_many_chunks_and_empty_tokens():
+    # Q = 5: token groups of 2, 2 and 1 (the last group's second token is absent); lengths long
+    # enough for several chunks per group, and a sequence of 4 whose first token sees nothing
+    rng = np.random.default_rng(66)
+    out, *_ = _check(rng, 3, 5, 16, 2, 2600, [2600, 700, 4], what="Q=5 ragged")
+    assert torch.all(out[2, 0] == 0)                 # position -1
+    assert not torch.all(out[2, 1] == 0)
 
 
 def test_multi_token_chunk_of_sixteen():
