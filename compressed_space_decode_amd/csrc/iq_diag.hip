@@ -14,8 +14,10 @@
 // A variance at most 1e-9 times the mean square of the same values counts as
 // zero and its kurtosis is reported as 0.
 //
-// Kernel 1 (diag_partial_kernel): 8 lanes per vector (lane e holds
-// coordinates 16e..16e+15), 32 vectors per step, one work-group per
+// Kernel 1 (diag_partial_kernel): 8 lanes per vector (lane e holds the 16
+// coordinates of chunk c = chunk_of(e), in the order 0 1 2 3 7 6 5 4, so that
+// every cross-lane Hadamard stage is a DPP operand), 32 vectors per step, one
+// work-group per
 // (sequence, head, 256 tokens).  The per-coordinate raw moments of
 // d = y - y_ref are summed, with y_ref the head's first transformed token, so
 // that a coordinate that never changes gives exactly zero; the per-vector
@@ -43,29 +45,28 @@ enum : int { kNone = 0, kWht = 1, kSo4 = 2, kWhtSo4 = 3, kDense = 4 };
 
 using vec::dpp_xor1;
 using vec::dpp_xor2;
-using vec::swz_xor4;
+using vec::dpp_mirror8;
 
 __device__ __forceinline__ float sum8(float v) {      // over the 8 lanes of a vector
   v += dpp_xor1(v);
   v += dpp_xor2(v);
-  return v + swz_xor4(v);
+  return v + dpp_mirror8(v);
 }
 __device__ __forceinline__ float max8(float v) {
   v = fmaxf(v, dpp_xor1(v));
   v = fmaxf(v, dpp_xor2(v));
-  return fmaxf(v, swz_xor4(v));
+  return fmaxf(v, dpp_mirror8(v));
 }
 
-// Normalised Walsh-Hadamard transform (Sylvester order) of the vector held by 8 lanes: strides
-// 16, 32, 64 pair lanes e^1, e^2, e^4 (new = partner + sg * mine), strides 8..1 stay in the lane.
-__device__ __forceinline__ void wht8(float x[16], int e) {
-  const float sg1 = (e & 1) ? -1.f : 1.f, sg2 = (e & 2) ? -1.f : 1.f, sg4 = (e & 4) ? -1.f : 1.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
+// Normalised Walsh-Hadamard transform (Sylvester order) of the vector held by 8 lanes (chunk c in
+// this lane): strides 16, 32, 64 pair chunks c^1, c^2, c^4 through fused DPP multiply-adds, which
+// leave chunk c with (-1)^popcount(c) times its values (taken out with the 1/sqrt(128)); strides
+// 8..1 stay in the lane.
+__device__ __forceinline__ void wht8(float x[16], int c) {
+  const float sg1 = (c & 1) ? -1.f : 1.f, sg2 = (c & 2) ? -1.f : 1.f, sg4 = (c & 4) ? -1.f : 1.f;
+  IQ_FMAC_DPP16(x, sg1, "quad_perm:[1,0,3,2]");
+  IQ_FMAC_DPP16(x, sg2, "quad_perm:[2,3,0,1]");
+  IQ_FMAC_DPP16(x, sg4, "row_half_mirror");
 #pragma unroll
   for (int h = 8; h >= 1; h >>= 1)
 #pragma unroll
@@ -75,8 +76,9 @@ __device__ __forceinline__ void wht8(float x[16], int e) {
         x[i] = u + v;
         x[i + h] = u - v;
       }
+  const float scale = kInvSqrt128 * vec::chunk_sign(c);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] *= kInvSqrt128;
+  for (int i = 0; i < 16; ++i) x[i] *= scale;
 }
 
 struct DiagArgs {
@@ -93,13 +95,13 @@ struct DiagArgs {
   double* stats;                                 // [n_seq][n_heads][260]
 };
 
-// y = T x for this lane's 16 coordinates.  M: the lane's SO(4) blocks 4e..4e+3 (row-major 4x4);
+// y = T x for this lane's 16 coordinates (chunk c).  M: the lane's SO(4) blocks 4c..4c+3 (row-major 4x4);
 // dt: the dense matrix transposed in LDS (dt[j * 128 + i] = T[i][j]); xs: this vector's 128
 // inputs staged in LDS.
 template <int kMode>
-__device__ __forceinline__ void transform(float x[16], float y[16], int e, const float (&M)[4][16],
+__device__ __forceinline__ void transform(float x[16], float y[16], int c, const float (&M)[4][16],
                                           const float* dt, float* xs) {
-  if constexpr (kMode == kWht || kMode == kWhtSo4) wht8(x, e);
+  if constexpr (kMode == kWht || kMode == kWhtSo4) wht8(x, c);
   if constexpr (kMode == kSo4 || kMode == kWhtSo4) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -113,13 +115,13 @@ __device__ __forceinline__ void transform(float x[16], float y[16], int e, const
       }
   } else if constexpr (kMode == kDense) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xs[16 * e + i] = x[i];
+    for (int i = 0; i < 16; ++i) xs[16 * c + i] = x[i];
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = 0.f;
     for (int j = 0; j < 128; ++j) {
       const float xj = xs[j];
-      const float4* col = reinterpret_cast<const float4*>(dt + j * 128 + 16 * e);
+      const float4* col = reinterpret_cast<const float4*>(dt + j * 128 + 16 * c);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 c = col[q];
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
 
   const int s = blockIdx.z, h = blockIdx.y, chunk = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int e = lane & 7;
+  const int c = vec::chunk_of(lane & 7);             // coordinates 16c..16c+15
   const int vsub = wave * 8 + (lane >> 3);           // vector slot within a step
   const int64_t head = (int64_t)s * a.n_heads + h;
   const int64_t base = (int64_t)s * a.stride_seq + (int64_t)h * a.stride_head;
@@ -166,26 +168,26 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) M[j][i] = kBlocks ? mats[kBlocks ? 4 * e + j : 0][i] : 0.f;
+    for (int i = 0; i < 16; ++i) M[j][i] = kBlocks ? mats[kBlocks ? 4 * c + j : 0][i] : 0.f;
 
   // the reference: the head's first token, transformed by wave 0 (vector slot 0)
   if (wave == 0) {
     float x[16], y[16];
-    vec::load16<kBF16>(a.x, base + 16 * e, true, x);
-    transform<kMode>(x, y, e, M, dt, xs[0]);
+    vec::load16<kBF16>(a.x, base + 16 * c, true, x);
+    transform<kMode>(x, y, c, M, dt, xs[0]);
     if (lane < 8) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) ref[16 * e + i] = y[i];
+      for (int i = 0; i < 16; ++i) ref[16 * c + i] = y[i];
       if (chunk == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) a.part[head * (128 + (int64_t)a.n_chunks * kPartFloats) + 16 * e + i] = y[i];
+        for (int i = 0; i < 16; ++i) a.part[head * (128 + (int64_t)a.n_chunks * kPartFloats) + 16 * c + i] = y[i];
       }
     }
   }
   __syncthreads();
   float yref[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) yref[i] = ref[16 * e + i];
+  for (int i = 0; i < 16; ++i) yref[i] = ref[16 * c + i];
 
   float S1[16], S2[16], S3[16], S4[16];
 #pragma unroll
@@ -199,8 +201,8 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
     const int64_t t = t0 + vsub;
     const bool valid = t < a.n_tokens;
     float x[16], y[16];
-    vec::load16<kBF16>(a.x, base + t * a.stride_tok + 16 * e, valid, x);
-    transform<kMode>(x, y, e, M, dt, xs[kD ? vsub : 0]);
+    vec::load16<kBF16>(a.x, base + t * a.stride_tok + 16 * c, valid, x);
+    transform<kMode>(x, y, c, M, dt, xs[kD ? vsub : 0]);
     // per coordinate, about the reference
     const float vm = valid ? 1.f : 0.f;
 #pragma unroll
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
     c2 = sum8(c2) * (1.f / 128.f);
     c4 = sum8(c4) * (1.f / 128.f);
     err = sum8(err);
-    if (e == 0 && valid) {
+    if (c == 0 && valid) {
       acc_kv += c2 > (float)kZeroVar * en * (1.f / 128.f) ? c4 / (c2 * c2) : 0.f;
       acc_err += err;
       acc_en += en;
@@ -268,10 +270,10 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
   if (lane < 8) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      red[wave][e][i] = S1[i];
-      red[wave][e][16 + i] = S2[i];
-      red[wave][e][32 + i] = S3[i];
-      red[wave][e][48 + i] = S4[i];
+      red[wave][c][i] = S1[i];
+      red[wave][c][16 + i] = S2[i];
+      red[wave][c][32 + i] = S3[i];
+      red[wave][c][48 + i] = S4[i];
     }
   }
   if (lane == 0) {
