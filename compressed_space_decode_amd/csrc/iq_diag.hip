@@ -95,12 +95,10 @@ struct DiagArgs {
   double* stats;                                 // [n_seq][n_heads][260]
 };
 
-// y = T x for this lane's 16 coordinates (chunk c).  M: the lane's SO(4) blocks 4c..4c+3 (row-major 4x4);
-// dt: the dense matrix transposed in LDS (dt[j * 128 + i] = T[i][j]); xs: this vector's 128
-// inputs staged in LDS.
+// y = T x for this lane's 16 coordinates (chunk c), for every transform but the dense one.
+// M: the lane's SO(4) blocks 4c..4c+3 (row-major 4x4).
 template <int kMode>
-__device__ __forceinline__ void transform(float x[16], float y[16], int c, const float (&M)[4][16],
-                                          const float* dt, float* xs) {
+__device__ __forceinline__ void transform(float x[16], float y[16], int c, const float (&M)[4][16]) {
   if constexpr (kMode == kWht || kMode == kWhtSo4) wht8(x, c);
   if constexpr (kMode == kSo4 || kMode == kWhtSo4) {
 #pragma unroll
@@ -113,29 +111,96 @@ __device__ __forceinline__ void transform(float x[16], float y[16], int c, const
         acc = fmaf(M[j][4 * r + 3], x[4 * j + 3], acc);
         y[4 * j + r] = acc;
       }
-  } else if constexpr (kMode == kDense) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) xs[16 * c + i] = x[i];
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) y[i] = 0.f;
-    for (int j = 0; j < 128; ++j) {
-      const float xj = xs[j];
-      const float4* col = reinterpret_cast<const float4*>(dt + j * 128 + 16 * c);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 c = col[q];
-        y[4 * q] = fmaf(c.x, xj, y[4 * q]);
-        y[4 * q + 1] = fmaf(c.y, xj, y[4 * q + 1]);
-        y[4 * q + 2] = fmaf(c.z, xj, y[4 * q + 2]);
-        y[4 * q + 3] = fmaf(c.w, xj, y[4 * q + 3]);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();    // xs is rewritten by the next vector
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) y[i] = x[i];
   }
+}
+
+// ---- the dense transform on the matrix cores ----
+// Y = X T^T for the work-group's 32 vectors (rows) on v_mfma_f32_16x16x32_f16: wave w computes
+// output coordinates 32w..32w+31 (two 16-wide tiles) for both 16-vector row tiles.  Operands are
+// split into fp16 hi and lo parts (22 bits each) and the products hi*hi + hi*lo + lo*hi are
+// summed in fp32.  Each vector is scaled by a power of two to an absmax in [1/2, 1) before the
+// split, so any fp32 range fits fp16, and scaled back on the output.
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+constexpr int kXs = 132;                      // padded LDS row (floats): rows start 4 banks apart
+
+struct DenseOperand {                         // B fragments T[i][j] for this wave's output tiles
+  half8 hi[2][4], lo[2][4];                   // [tile][32-coordinate step]
+};
+
+// Lane (n, g4) of wave w holds T[32w + 16 nt + n][32 ks + 8 g4 .. + 7] for tile nt and step ks.
+__device__ __forceinline__ void load_dense_operand(const float* T, int wave, int lane, DenseOperand& b) {
+  const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* row = T + (int64_t)(32 * wave + 16 * nt + n) * 128 + 32 * ks + 8 * g4;
+      half8 h, l;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = row[e];
+        const _Float16 hv = (_Float16)v;
+        h[e] = hv;
+        l[e] = (_Float16)(v - (float)hv);
+      }
+      b.hi[nt][ks] = h;
+      b.lo[nt][ks] = l;
+    }
+}
+
+// y = T x for the 32 vectors of a step (lane: vector slot vsub, chunk c).  Every thread of the
+// work-group must call it (barriers).  xs, ys: [32][kXs] staging; xe: [32] exponents.
+__device__ __forceinline__ void dense_step(const float x[16], float y[16], int c, int vsub, int wave, int lane,
+                                           const DenseOperand& b, float (*xs)[kXs], float (*ys)[kXs], int* xe) {
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = max8(amax);
+  int ex = 0;
+  if (amax > 0.f) frexpf(amax, &ex);           // amax < 2^ex
+  const float down = ldexpf(1.f, -ex);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) xs[vsub][16 * c + i] = x[i] * down;
+  if (c == 0) xe[vsub] = ex;
+  __syncthreads();
+  const int n = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    half8 ah[4], al[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const float* src = &xs[16 * mt + n][32 * ks + 8 * g4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = src[e];
+        const _Float16 hv = (_Float16)v;
+        ah[ks][e] = hv;
+        al[ks][e] = (_Float16)(v - (float)hv);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], b.hi[nt][ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[ks], b.lo[nt][ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[ks], b.hi[nt][ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {             // row 4 g4 + r of the tile: vector 16 mt + 4 g4 + r
+        const int v = 16 * mt + 4 * g4 + r;
+        ys[v][32 * wave + 16 * nt + n] = ldexpf(acc[r], xe[v]);
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) y[i] = ys[vsub][16 * c + i];
 }
 
 template <bool kBF16, int kMode>
@@ -143,8 +208,9 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
   constexpr bool kBlocks = kMode == kSo4 || kMode == kWhtSo4;
   constexpr bool kD = kMode == kDense;
   __shared__ float mats[kBlocks ? 32 : 1][16];
-  __shared__ __attribute__((aligned(16))) float dt[kD ? 128 * 128 : 4];
-  __shared__ __attribute__((aligned(16))) float xs[kD ? kVecPerStep : 1][128];
+  __shared__ __attribute__((aligned(16))) float xs[kD ? kVecPerStep : 1][kXs];
+  __shared__ __attribute__((aligned(16))) float ys[kD ? kVecPerStep : 1][kXs];
+  __shared__ int xe[kD ? kVecPerStep : 1];
   __shared__ float ref[128];
   __shared__ float red[kWaves][8][64];
   __shared__ float red_s[kWaves][kScalars];
@@ -159,10 +225,8 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
   if constexpr (kBlocks) {
     if (tid < 32) vec::build_so4_block(a.rot + (int64_t)s * a.rot_stride_seq + (int64_t)h * 256 + tid * 8, mats[tid]);
   }
-  if constexpr (kD) {
-    const float* T = a.dense + (int64_t)s * a.dense_stride_seq + (int64_t)h * 128 * 128;
-    for (int idx = tid; idx < 128 * 128; idx += kThreads) dt[(idx & 127) * 128 + (idx >> 7)] = T[idx];
-  }
+  DenseOperand bop;
+  if constexpr (kD) load_dense_operand(a.dense + (int64_t)s * a.dense_stride_seq + (int64_t)h * 128 * 128, wave, lane, bop);
   __syncthreads();
   float M[4][16];
 #pragma unroll
@@ -170,12 +234,16 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) M[j][i] = kBlocks ? mats[kBlocks ? 4 * c + j : 0][i] : 0.f;
 
-  // the reference: the head's first token, transformed by wave 0 (vector slot 0)
-  if (wave == 0) {
+  // the reference: the head's first token, transformed by wave 0 (vector slot 0); the dense
+  // transform runs it in every slot of one step (all threads take part in its barriers)
+  if (kD || wave == 0) {
     float x[16], y[16];
     vec::load16<kBF16>(a.x, base + 16 * c, true, x);
-    transform<kMode>(x, y, c, M, dt, xs[0]);
-    if (lane < 8) {
+    if constexpr (kD)
+      dense_step(x, y, c, vsub, wave, lane, bop, xs, ys, xe);
+    else
+      transform<kMode>(x, y, c, M);
+    if (wave == 0 && lane < 8) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) ref[16 * c + i] = y[i];
       if (chunk == 0) {
@@ -202,7 +270,10 @@ __global__ __launch_bounds__(kThreads) void diag_partial_kernel(DiagArgs a) {
     const bool valid = t < a.n_tokens;
     float x[16], y[16];
     vec::load16<kBF16>(a.x, base + t * a.stride_tok + 16 * c, valid, x);
-    transform<kMode>(x, y, c, M, dt, xs[kD ? vsub : 0]);
+    if constexpr (kD)
+      dense_step(x, y, c, vsub, wave, lane, bop, xs, ys, xe);
+    else
+      transform<kMode>(x, y, c, M);
     // per coordinate, about the reference
     const float vm = valid ? 1.f : 0.f;
 #pragma unroll
