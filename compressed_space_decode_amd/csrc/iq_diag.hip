@@ -22,6 +22,8 @@
 // d = y - y_ref are summed, with y_ref the head's first transformed token, so
 // that a coordinate that never changes gives exactly zero; the per-vector
 // moments are taken about the vector's own mean (two passes over registers).
+// The dense transform runs on the matrix cores for the work-group's 32
+// vectors of a step (dense_step), the others on the vector units.
 // Each work-group writes fp32 sums for its 256 tokens.
 // Kernel 2 (diag_finalize_kernel): one work-group per (sequence, head) adds
 // the partial sums in fp64 (two threads per coordinate, independent
