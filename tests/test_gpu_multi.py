@@ -2,7 +2,7 @@
 (iq_decode_attention_multi) against the oracle (multi_token_attention),
 through the C ABI: ragged lengths, a sequence shorter than the number of query
 tokens, fp32 queries with shared rotations, a 16-token chunk, an odd count with
-several chunks per token group, and one token,
+several chunks per token group, more than 64 token groups, and one token,
 which must be exactly iq_decode_attention.  Tolerance as for decode
 (tests/_parity.py).
 """
@@ -67,6 +67,15 @@ def test_multi_token_odd_count_many_chunks_and_empty_tokens():
     out, *_ = _check(rng, 3, 5, 16, 2, 2600, [2600, 700, 4], what="Q=5 ragged")
     assert torch.all(out[2, 0] == 0)                 # position -1
     assert not torch.all(out[2, 1] == 0)
+
+
+def test_multi_token_more_than_64_token_groups():
+    # 40 sequences of 4 tokens: 80 two-token groups, so the chunk plan takes its 64-at-a-time path
+    rng = np.random.default_rng(67)
+    lens = list(rng.integers(0, 601, size=40))
+    lens[3], lens[7] = 0, 2                        # an empty sequence and one shorter than Q
+    out, *_ = _check(rng, 40, 4, 8, 2, 600, lens, what="Q=4 B=40")
+    assert torch.all(out[3] == 0) and torch.all(out[7, :2] == 0)
 
 
 def test_multi_token_chunk_of_sixteen():
