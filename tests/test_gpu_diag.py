@@ -85,6 +85,20 @@ def test_isotropy_strided_input_shared_parameters_and_permutation():
     _compare(got.cpu().numpy(), x64, "dense", None, np.broadcast_to(P, (2, 2, 128, 128)), "permutation")
 
 
+def test_isotropy_dense_outside_fp16_range():
+    # the dense transform splits each vector into fp16 parts after scaling it by a power of two:
+    # values far above fp16's largest (6.5e4) and far below its normal range (6e-5) give the same
+    # statistics as the oracle; zero vectors stay zero
+    rng = np.random.default_rng(123)
+    x = _inputs(rng, 1, 2, 300)
+    x[0, 0] *= np.float32(3e6)
+    x[0, 1] *= np.float32(2e-9)
+    x[0, 1, 50:60] = 0.0
+    dense = _orthogonal(rng, 1, 2)
+    got = iq.isotropy_stats(torch.from_numpy(x).cuda(), "dense", dense=torch.from_numpy(dense).cuda())
+    _compare(got.cpu().numpy(), x.astype(np.float64), "dense", None, dense, "dense, wide range")
+
+
 def test_isotropy_degenerate_inputs():
     rng = np.random.default_rng(121)
     T = 300
