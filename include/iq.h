@@ -162,11 +162,12 @@ int iq_quantize_kv_format(const void* k, const void* v, int32_t dtype,
 
 /*
  * iq_decode_workspace_bytes -- device workspace that iq_decode_attention
- * (and iq_decode_attention_append) needs with these sizes on the current
- * device: the split plan (chunk size and each sequence's first chunk) and
- * the split-K partial results.  The kernels choose the chunk size on the
- * device from the sequence lengths, so that the batch's chunks fill one
- * round of work-groups; the bound depends only on these sizes and the
+ * (and iq_decode_attention_append, and iq_decode_attention_multi with batch
+ * times n_q_tokens as batch) needs with these sizes on the current device:
+ * the split plan (chunk size and each sequence's first chunk) and the
+ * split-K partial results.  The kernels choose the chunk size on the device
+ * from the sequence lengths, so that the batch's chunks fill a fixed number
+ * of rounds of work-groups; the bound depends only on these sizes and the
  * device's compute-unit count.  Negative IQ_E* code on invalid sizes.
  */
 int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
