@@ -80,6 +80,8 @@ constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1/sqrt(128)
 constexpr int kMaxChunks = 1024;    // most chunks of one sequence (the combine's LDS weights)
 constexpr int kFewChunks = 16;      // rows with at most this many chunks merge in registers
+constexpr int kMidChunks = 64;      // above kPreloadFrom and up to this many: partials preloaded,
+constexpr int kPreloadFrom = 32;    // weights through LDS
 
 // Field j (0..7) of a 24-bit group is taken from byte window j / 3 (bytes 0-1, 1-2 or 2-3 of the
 // group) at bit position field_pos(j) <= 7 of each 16-bit half.
@@ -1690,6 +1692,17 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   nvalid = min(nvalid, min(kMaxChunks, a.x_max / rs - x0));   // the plan; the bound keeps every read in range
   const int64_t first = (int64_t)h * a.x_max + (int64_t)x0 * rs + ri;   // partial row of chunk 0; chunk c
   const float* ml = a.part_ml + first * 2;                             // is rs rows further
+  // rows with kPreloadFrom < chunks <= kMidChunks: this thread's partials are loaded now, together
+  // with the weights' loads below, and kept in registers (with fewer chunks the extra registers
+  // measured slower than the loads after the barrier)
+  float om[kMidChunks];
+  const bool preload = nvalid > kPreloadFrom && nvalid <= kMidChunks;   // uniform
+  if (preload) {
+    const float* po = a.part_o + first * 128 + tid;
+#pragma unroll
+    for (int c = 0; c < kMidChunks; ++c)
+      if (c < nvalid) om[c] = po[(int64_t)c * rs * 128];   // uniform branches
+  }
   if (nvalid <= kFewChunks) {           // uniform: every thread loads all (max, sum) pairs and its partials at once
     const float* po = a.part_o + first * 128 + tid;
     float mv[kFewChunks], lv[kFewChunks], ov[kFewChunks];
@@ -1730,7 +1743,14 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   } else if (lane < 32) {               // the SO(4) blocks of this head's KV head
     build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
   }
-  if (nvalid > kFewChunks) {
+  if (preload) {
+    __syncthreads();
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMidChunks; ++c)
+      if (c < nvalid) acc[c & 7] = fmaf(wgt[c], om[c], acc[c & 7]);
+    y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
+  } else if (nvalid > kFewChunks) {
     __syncthreads();
     const float* po = a.part_o + first * 128 + tid;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
