@@ -197,3 +197,38 @@ def test_asymmetric_beats_symmetric_on_offset_data():
             codes, scales, _, _ = F.quantize_rotated(y + off, fmt)
             mse[fmt] = np.mean((y + off - F.levels(codes, scales, fmt)) ** 2)
         assert mse["a3"] * factor < mse["u3"], (off, mse)
+
+
+def test_uniform_levels_hand_written_and_within_half_a_step():
+    # the level of code c is s (c - (2^b - 1)/2): written out by hand for unit scale, so a
+    # centre of 2^(b-1) instead of (2^b - 1)/2 fails here
+    s = np.float32(1.0)
+    hand = {"u2": [-1.5, -0.5, 0.5, 1.5],
+            "u3": [-3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5],
+            "u4": [-7.5, -6.5, -5.5, -4.5, -3.5, -2.5, -1.5, -0.5, 0.5, 1.5, 2.5, 3.5, 4.5, 5.5, 6.5, 7.5]}
+    for fmt, want in hand.items():
+        n = len(want)
+        codes = (np.arange(128) % n).astype(np.uint8)[None]
+        got = F.levels(codes, np.array([s]), fmt)[0]
+        np.testing.assert_array_equal(got, np.array(want * (128 // n)), err_msg=fmt)
+    assert F.levels(np.full((1, 128), 15, np.uint8), np.array([2.0]), "u4")[0, 0] == 15.0
+    assert F.levels(np.zeros((1, 128), np.uint8), np.array([2.0]), "u4")[0, 0] == -15.0
+    assert F.levels(np.ones((1, 128), np.uint8), np.array([4.0]), "u2")[0, 0] == -2.0
+    # every uniform format reconstructs each coordinate within half a step: |y - level(c)| <= s/2
+    rng = np.random.default_rng(80)
+    y = rng.standard_normal((60, 128)) * np.exp(rng.uniform(-2, 2, size=(60, 1)))
+    for fmt in ("u2", "u3", "u4", "a3"):
+        codes, scales, s_exact, _ = F.quantize_rotated(y, fmt)
+        if fmt == "a3":
+            sc = np.stack([s_exact, y.min(axis=1)], axis=-1)
+        else:
+            sc = s_exact
+        err = np.abs(y - F.levels(codes, sc, fmt))
+        assert np.all(err <= s_exact[:, None] / 2 * (1 + 1e-12)), fmt
+    # Lloyd-Max: inside the outermost levels a coordinate is within half the gap to its neighbours
+    codes, sig, sig_exact, u = F.quantize_rotated(y, "lm3")
+    L = np.array(F.LLOYD_MAX_8)
+    inner = (u > L[0]) & (u < L[-1])
+    err = np.abs(u - L[codes])
+    gap = np.diff(L).max() / 2
+    assert np.all(err[inner] <= gap * (1 + 1e-12))

@@ -49,3 +49,31 @@ def test_make_rotation_deterministic_and_seed_dependent():
     assert np.any(a != c)
     # heads are consumed in order from one stream: a 3-head call starts with the 1-head call
     np.testing.assert_array_equal(oracle.make_rotation(123, 1)[0], a[0])
+
+
+def _uniform_from_published(z):
+    """(z >> 11) 2^-52 - 1 of a published SplitMix64 output, exact in fp64."""
+    return float(z >> 11) * 2.0 ** -52 - 1.0
+
+
+def test_make_rotation_draw_order_against_published_outputs():
+    # seed 1234567: the first two published outputs give x1, x2 of block 0's left quaternion
+    # (s1 = x1^2 + x2^2 is about 0.52 < 1, so the pair is accepted).  Drawing the right
+    # quaternion first would put later draws there.
+    with open(os.path.join(GOLDEN, "splitmix64.txt")) as f:
+        rows = [ln.split(":") for ln in f if ln.strip() and not ln.startswith("#")]
+    outs = {int(s): [int(t) for t in o.split()] for s, o in rows}
+    z = outs[1234567]
+    x1, x2 = _uniform_from_published(z[0]), _uniform_from_published(z[1])
+    assert x1 * x1 + x2 * x2 < 1.0
+    p = oracle.make_rotation(1234567, 1)
+    np.testing.assert_array_equal(p[0, 0, 0:2], np.float32([x1, x2]))
+    # the third published output is x3 of the same quaternion: the point is (x1, x2, x3 f, x4 f)
+    # with f = sqrt((1 - s1) / s2) > 0, so its third component has x3's sign
+    x3 = _uniform_from_published(z[2])
+    assert np.sign(p[0, 0, 2]) == np.sign(x3)
+    # the right quaternion starts after the left one's draws: with no rejection in either pair,
+    # draws 4 and 5 of the (published-pinned) generator are its x1, x2
+    d = [_uniform_from_published(oracle.splitmix64(1234567, i)) for i in range(6)]
+    if d[2] ** 2 + d[3] ** 2 < 1.0 and d[4] ** 2 + d[5] ** 2 < 1.0:
+        np.testing.assert_array_equal(p[0, 0, 4:6], np.float32([d[4], d[5]]))
