@@ -123,7 +123,8 @@ int quantize_impl(const char* fn, const void* k, const void* v, int32_t dtype, i
     iq::set_error("%s: rot is NULL or a stride is negative", fn);
     return IQ_EINVAL;
   }
-  if (cache_cap < 1 || tok_offset < 0 || tok_offset + n_tokens > cache_cap) {
+  // (n_tokens > cache_cap - tok_offset cannot overflow once 0 <= tok_offset <= cache_cap)
+  if (cache_cap < 1 || tok_offset < 0 || tok_offset > cache_cap || n_tokens > cache_cap - tok_offset) {
     iq::set_error("%s: need cache_cap >= 1, tok_offset >= 0, tok_offset + n_tokens <= cache_cap", fn);
     return IQ_EINVAL;
   }
@@ -152,6 +153,7 @@ int quantize_impl(const char* fn, const void* k, const void* v, int32_t dtype, i
   a.rot_stride_seq = rot_stride_seq;
   a.cache_cap = cache_cap;
   a.tok_offset = tok_offset;
+  (void)hipGetLastError();   // an earlier call's error is not this call's
   const hipError_t err = iq::launch_quantize_format(a, format, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
@@ -270,6 +272,7 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   a.sm_scale = sm_scale;
   a.out = out;
   a.workspace = workspace;
+  (void)hipGetLastError();   // an earlier call's error is not this call's
   const hipError_t err = iq::launch_decode(a, geo, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
@@ -390,6 +393,7 @@ extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const 
   a.new_bf16 = new_dtype == IQ_BF16;
   a.new_stride_seq = new_stride_seq;
   a.new_stride_head = new_stride_head;
+  (void)hipGetLastError();   // an earlier call's error is not this call's
   const hipError_t err = iq::launch_decode(a, geo, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));
@@ -473,6 +477,7 @@ extern "C" int iq_isotropy_stats(const void* x, int32_t dtype, int64_t n_seq, in
   a.dense_stride_seq = dense_stride_seq;
   a.stats = stats;
   a.workspace = workspace;
+  (void)hipGetLastError();   // an earlier call's error is not this call's
   const hipError_t err = iq::launch_diag(a, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) {
     iq::set_error("%s: launch failed: %s", fn, hipGetErrorString(err));

@@ -519,6 +519,11 @@ struct CacheBuffers {
 
 constexpr int kBufferConfig = 0x00020000;   // raw (untyped) buffer, 32-bit data format
 
+// Byte range of a buffer resource over `cap` records of `rec` bytes.  The product is formed in
+// unsigned arithmetic: at the largest accepted capacity it exceeds INT_MAX (but stays below
+// 0xF0000000), and the resource field takes its 32-bit pattern.
+__device__ __forceinline__ int range_bytes(int cap, int rec) { return (int)((unsigned)cap * (unsigned)rec); }
+
 // Block base for a block that is not to be read: beyond every slice (capacity times the record
 // size is validated to stay below it), so its loads return zeros without reaching memory.
 constexpr unsigned kNoBlock = 0xF0000000u;
@@ -950,11 +955,11 @@ void decode_split_kernel(DecodeKArgs a) {
   const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
 
   CacheBuffers cb;
-  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
-  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
+  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, range_bytes(cap, kRec), kBufferConfig);
+  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, range_bytes(cap, kRec), kBufferConfig);
   constexpr int kSW = kAsym ? 2 : 1;                         // fp32 per token in the scale arrays
-  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
-  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap * kSW), (short)0, cap * 4 * kSW, kBufferConfig);
+  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap * kSW), (short)0, range_bytes(cap, 4 * kSW), kBufferConfig);
+  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap * kSW), (short)0, range_bytes(cap, 4 * kSW), kBufferConfig);
   const int n = lane & 15;          // MFMA column: token within a 16-token tile / V group
   const int g4 = lane >> 4;         // row group: quarter of the K record; heads 2*g4, 2*g4+1
   LaneOffsets lo;
@@ -1437,10 +1442,10 @@ void decode_multi_kernel(DecodeKArgs a) {
   const float* rot = a.rot + bc * a.rot_stride_b + (int64_t)g * 256;
 
   CacheBuffers cb;
-  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
-  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, cap * kRec, kBufferConfig);
-  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, cap * 4, kBufferConfig);
-  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, cap * 4, kBufferConfig);
+  cb.kc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.kc + kv * a.cap * kRec), (short)0, range_bytes(cap, kRec), kBufferConfig);
+  cb.vc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vc + kv * a.cap * kRec), (short)0, range_bytes(cap, kRec), kBufferConfig);
+  cb.ks = __builtin_amdgcn_make_buffer_rsrc((void*)(a.ks + kv * a.cap), (short)0, range_bytes(cap, 4), kBufferConfig);
+  cb.vs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.vs + kv * a.cap), (short)0, range_bytes(cap, 4), kBufferConfig);
   const int n = lane & 15;
   const int g4 = lane >> 4;
   LaneOffsets lo;

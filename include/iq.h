@@ -18,7 +18,8 @@
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is
  *     the default stream) and is complete when the stream reaches it.
  *   - Every argument is validated before anything is launched, so an error
- *     return means nothing was enqueued.
+ *     return other than IQ_EHIP means nothing was enqueued.  A HIP error left
+ *     pending by earlier, unrelated work is cleared before the launches.
  *   - head_dim must be 128 and bits must be 3 (IQ_EUNSUPPORTED otherwise).
  *
  * Data layouts (the pages only say "packed 3-bit tensors"; these are this
@@ -54,7 +55,9 @@ enum {
   IQ_EINVAL = -1,        /* null pointer, bad count, stride or shape */
   IQ_EUNSUPPORTED = -2,  /* head_dim != 128, bits != 3, unknown dtype */
   IQ_EWORKSPACE = -3,    /* workspace missing or smaller than required */
-  IQ_EHIP = -4           /* a HIP runtime call or kernel launch failed */
+  IQ_EHIP = -4           /* a HIP runtime call or kernel launch failed; kernels of the call
+                            enqueued before the failing launch may still run, and the
+                            call's outputs are then undefined */
 };
 
 enum { IQ_F32 = 0, IQ_BF16 = 1 };
@@ -165,10 +168,14 @@ int iq_quantize_kv_format(const void* k, const void* v, int32_t dtype,
  * (and iq_decode_attention_append, and iq_decode_attention_multi with batch
  * times n_q_tokens as batch) needs with these sizes on the current device:
  * the split plan (chunk size and each sequence's first chunk) and the
- * split-K partial results.  The kernels choose the chunk size on the device
- * from the sequence lengths, so that the batch's chunks fill a fixed number
- * of rounds of work-groups; the bound depends only on these sizes and the
- * device's compute-unit count.  Negative IQ_E* code on invalid sizes.
+ * split-K partial results.  Source: Abstract (attention computed on the
+ * packed tensors); splitting the context over work-groups and merging their
+ * partial softmax results is this library's way of running that attention
+ * on a whole GPU.  The kernels choose the chunk size on the device from the
+ * sequence lengths, so that the batch's chunks fill a fixed number of rounds
+ * of work-groups per (KV head, group of up to 8 query heads): the bound
+ * depends only on these sizes (n_kv_heads sets the number of such columns)
+ * and the device's compute-unit count.  Negative IQ_E* code on invalid sizes.
  */
 int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
                                   int32_t n_kv_heads, int64_t cache_cap);

@@ -135,19 +135,33 @@ def test_long32k_decode(long32k):
 
 
 def test_long32k_planted_key_retrieval(long32k):
-    # Property, not parity: the planted key wins the 3-bit compressed-space scores of the
-    # query head it was planted for (its KV group's first head), as it does unquantized.
+    # Property, not parity: the stand-in for the Abstract's retrieval at 32K context.  For each KV
+    # head, is the planted position the argmax of the exact fp64 scores q.k (unquantized K) and of
+    # the 3-bit compressed-space scores (R q).k_hat on the GPU's codes, for the query head the key
+    # was planted for (its KV group's first head)?  Both results are logged per head.  The 3-bit
+    # scores must keep every head the exact scores retrieve.  On this seeded workload the exact
+    # scores themselves miss KV head 0: another key's channel-scaled score beats the planted key's
+    # before any quantization, so that head cannot count against the quantizer.
     w, g = long32k, long32k["gpu"]
     p = int(w["planted_pos"][0])
     q64 = W.to_f64(w["q"], w["dtype"])
-    hits = 0
+    G = w["n_q_heads"] // w["n_kv_heads"]
+    exact, packed = [], []
     for h in range(w["n_kv_heads"]):
+        qh = q64[0, h * G]
+        ze = W.to_f64(w["k"][0, h], w["dtype"]) @ qh
         R = oracle.rotation_matrix(w["params"][0, h])
-        qr = R @ q64[0, h * (w["n_q_heads"] // w["n_kv_heads"])]
-        z = oracle.dequantize_rotated(oracle.unpack(g["kc"][0, h]), g["ks"][0, h]) @ qr
-        hits += int(np.argmax(z) == p)
-    _log("  planted key retrieved in %d of %d KV heads" % (hits, w["n_kv_heads"]))
-    assert hits >= w["n_kv_heads"] - 1
+        z3 = oracle.dequantize_rotated(oracle.unpack(g["kc"][0, h]), g["ks"][0, h]) @ (R @ qh)
+        exact.append(int(np.argmax(ze)))
+        packed.append(int(np.argmax(z3)))
+        _log("  KV head %d: planted %d; exact argmax %d (%s), 3-bit argmax %d (%s)" %
+             (h, p, exact[-1], "hit" if exact[-1] == p else "miss", packed[-1], "hit" if packed[-1] == p else "miss"))
+    hits_exact = [e == p for e in exact]
+    hits_packed = [c == p for c in packed]
+    _log("  planted key retrieved: exact %d of %d, 3-bit %d of %d" %
+         (sum(hits_exact), len(exact), sum(hits_packed), len(packed)))
+    assert all(hp for he, hp in zip(hits_exact, hits_packed) if he), "3-bit lost a head the exact scores retrieve"
+    assert hits_exact == [False, True, True, True], "the seeded workload's exact retrieval changed"
 
 
 def test_ragged_quantize_sampled(ragged):

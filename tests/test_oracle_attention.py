@@ -143,6 +143,29 @@ def test_retrieval_of_a_planted_key_survives_quantization_in_oracle():
     assert int(np.argmax(z)) == pos
 
 
+def test_long32k_planted_key_retrieval_exact_and_3bit_in_oracle():
+    # The long-context workload at full size (one layer: 4 KV heads x 32768 tokens), the oracle's
+    # own codes: per KV head, the argmax of the exact fp64 scores q.k and of the 3-bit scores
+    # (R q).k_hat for the query head the key was planted for.  3-bit quantization keeps every head
+    # the exact scores retrieve; the exact scores miss KV head 0, where another key's
+    # channel-scaled score is higher than the planted key's before any quantization.
+    from compressed_space_decode_amd import workloads as W
+    w = W.decode_workload("long32k")
+    p = int(w["planted_pos"][0])
+    q64 = W.to_f64(w["q"], w["dtype"])
+    G = w["n_q_heads"] // w["n_kv_heads"]
+    exact, packed = [], []
+    for h in range(w["n_kv_heads"]):
+        k64 = W.to_f64(w["k"][0, h], w["dtype"])
+        qh = q64[0, h * G]
+        codes, scales, _, _ = oracle.quantize(k64, w["params"][0, h])
+        R = oracle.rotation_matrix(w["params"][0, h])
+        exact.append(int(np.argmax(k64 @ qh)) == p)
+        packed.append(int(np.argmax(oracle.dequantize_rotated(codes, scales) @ (R @ qh))) == p)
+    assert exact == [False, True, True, True]
+    assert packed == exact
+
+
 def test_multi_token_attention_matches_masked_torch_sdpa():
     # Q new tokens at the last Q positions, each attending to the positions up to its own:
     # PyTorch's fp64 attention with an explicit boolean mask on the dequantized, unrotated K/V.
