@@ -19,8 +19,15 @@ runs (profiles/decode_traffic.json), reported only while the decode kernel
 source is the one those counters were taken on.  Extra fields report the
 decode alone, the append then decode as two launches, a single-layer decode,
 the GQA 8K and ragged-batch decode shapes, and the bulk prefill quantization
-(48 layers x 4 KV heads x 32768 tokens, K and V Student-t(3), bf16).  The
-default warm-up (800 untimed steps) lets the GPU clocks settle before timing.
+(48 layers x 4 KV heads x 32768 tokens, K and V Student-t(3), bf16).
+
+Timing: a read-only stream probe and --settle seconds of untimed steps run
+first whatever --warmup says (the GPU's clocks need about a second of work to
+settle), then --warmup untimed steps, then --steps steps, each between its own
+pair of HIP events on the call's stream.  ms_per_step is the median; min and
+max are reported beside it, and the roofline uses the mean.  The CPU baseline
+times the oracle on bounded samples of every workload, single-threaded and on
+all of BLAS's threads, and states the host's CPU model and counts.
 """
 import argparse
 import hashlib
@@ -56,8 +63,11 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=800, help="untimed steps first (lets the clocks settle)")
+    ap.add_argument("--steps", type=int, default=200, help="timed steps, each between its own HIP events")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps right before the timed ones")
+    ap.add_argument("--settle", type=float, default=2.0,
+                    help="seconds of untimed steps before the warm-up, whatever --warmup says (the GPU's "
+                         "clocks need about a second of work to settle)")
     ap.add_argument("--layers", type=int, default=LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -65,7 +75,8 @@ def parse():
     ap.add_argument("--no-isotropy", action="store_true", help="skip the isotropy diagnostics")
     ap.add_argument("--no-formats", action="store_true",
                     help="skip the 2/4-bit, Lloyd-Max and asymmetric record formats")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="time budget of the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=1.0,
+                    help="time of each oracle sample (5 workloads, single-threaded and all cores)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (5 times) and exit: the "
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
@@ -103,6 +114,142 @@ def time_calls(fn, iters, stream):
     return start.elapsed_time(end) / 1e3 / iters
 
 
+def time_each(fn, iters, stream):
+    """Durations (s) of iters calls of fn(), each between its own pair of HIP events on `stream`
+    (the calls are still enqueued back to back).  Returns the sorted list."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for s_, e_ in ev:
+        s_.record(stream)
+        fn()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    return sorted(s_.elapsed_time(e_) / 1e3 for s_, e_ in ev)
+
+
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def settle(fn, seconds):
+    """Untimed calls of fn() for at least `seconds` of wall time (in batches, synchronised), so
+    that the GPU's clocks have reached their steady state before anything is timed.  Returns the
+    number of calls."""
+    import torch
+    calls, t0 = 0, time.time()
+    while True:
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        calls += 50
+        if time.time() - t0 >= seconds:
+            return calls
+
+
+def host_info():
+    """The host the CPU baseline runs on: CPU model, logical CPUs, CPUs this process may use and
+    the BLAS thread count."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cpus": affinity, "blas_threads": int(blas)}
+
+
+def cpu_baselines(seconds):
+    """The CPU oracle timed on bounded samples of every workload, single-threaded and with all of
+    BLAS's threads: decode (unpack of the packed K/V records + fp64 decode attention) in KV
+    tokens/s for the tiny, gqa8k, long32k and ragged shapes, and quantize (rotation, 3-bit codes,
+    packing) in vectors/s for the prefill shape.  The packed records are random bytes (every byte
+    pattern is a valid record; the oracle's work does not depend on the values), the rotations,
+    queries and prefill vectors come from the seeded workloads.  A sample that covers some of the
+    KV heads or sequences is scaled to the whole step by its share of the (token, KV head) pairs.
+    Each sample repeats until `seconds` have passed."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    from compressed_space_decode_amd import workloads as W
+    rng = np.random.default_rng(2024)
+    res = {}
+
+    def run(fn, work):
+        out = {}
+        for label, lim in (("single_thread", 1), ("all_cores", None)):
+            with threadpool_limits(lim):
+                n, t0 = 0, time.perf_counter()
+                while True:
+                    fn()
+                    n += 1
+                    el = time.perf_counter() - t0
+                    if el >= seconds:
+                        break
+            out[label] = work * n / el
+        return out
+
+    def decode_sample(name, B, Hq, Hkv, lens, heads):
+        G = Hq // Hkv
+        T = int(max(lens))
+        rec_k = rng.integers(0, 256, size=(B, heads, T, 48), dtype=np.uint8)
+        rec_v = rng.integers(0, 256, size=(B, heads, T, 48), dtype=np.uint8)
+        sk = rng.uniform(0.05, 1.0, size=(B, heads, T)).astype(np.float32)
+        sv = rng.uniform(0.05, 1.0, size=(B, heads, T)).astype(np.float32)
+        q = rng.standard_normal((B, heads * G, 128))
+        params = W.rotation_params(rng, B * heads).reshape(B, heads, 32, 8)
+        lens = np.asarray(lens)
+
+        def fn():
+            oracle.decode_attention(q, oracle.unpack(rec_k), sk, oracle.unpack(rec_v), sv, params, lens)
+
+        r = run(fn, float(np.sum(lens)) * heads / Hkv)     # KV tokens (all heads) per sample
+        return r
+
+    info = W.SHAPES
+    B, Hq, Hkv, T, _ = info["tiny"]
+    res["tiny"] = dict(decode_sample("tiny", B, Hq, Hkv, [T] * B, Hkv), unit="KV tokens/s",
+                       sample="the whole step: %d KV heads x %d tokens" % (Hkv, T))
+    B, Hq, Hkv, T, _ = info["gqa8k"]
+    res["gqa8k"] = dict(decode_sample("gqa8k", B, Hq, Hkv, [T] * B, Hkv), unit="KV tokens/s",
+                        sample="the whole step: %d KV heads x %d tokens, %d query heads" % (Hkv, T, Hq))
+    B, Hq, Hkv, T, _ = info["long32k"]
+    res["long32k"] = dict(decode_sample("long32k", 1, Hq, Hkv, [T], 1), unit="KV tokens/s",
+                          sample="1 of %d KV heads (with its %d query heads) x %d tokens, scaled by %d" %
+                                 (Hkv, Hq // Hkv, T, Hkv))
+    B, Hq, Hkv, T, _ = info["ragged"]
+    lens_r = W.decode_workload("ragged")["seq_lens"]
+    res["ragged"] = dict(decode_sample("ragged", 1, Hq, Hkv, [int(lens_r[0])], 1), unit="KV tokens/s",
+                         sample="sequence 0 of %d (%d tokens), 1 of %d KV heads (with its %d query heads); "
+                                "rate per (token, KV head) pair over %d KV heads" %
+                                (B, int(lens_r[0]), Hkv, Hq // Hkv, Hkv))
+    k, _, pparams = W.prefill_layer(0, tokens=8192)
+    x = W.to_f64(k[0], "bf16")
+    params = pparams[0]
+
+    def quant():
+        codes, _, _, _ = oracle.quantize(x, params)
+        oracle.pack(codes)
+
+    res["prefill"] = dict(run(quant, x.shape[0]), unit="vectors/s",
+                          sample="8192 K vectors of prefill layer 0, head 0 (Student-t(3), bf16): rotation, "
+                                 "codes, scale and packing")
+    return res
+
+
 def isotropy_summary(iq, W, x, rot, seed):
     """The isotropy statistics of x [S][H][T][128] under every transform, summarised over the
     heads: mean and largest per-coordinate kurtosis, mean 3-bit quantization error (relative) and
@@ -120,9 +267,10 @@ def isotropy_summary(iq, W, x, rot, seed):
 
 
 def time_graph(fn, per_graph, replays, stream):
-    """Average duration (s) of fn() with per_graph calls captured in one HIP graph that is
-    replayed `replays` times on `stream`: the GPU's time for a call without the host's per-call
-    overhead (which is larger than a small call's GPU time).  fn must allocate nothing."""
+    """Duration (s) of one fn() call from per_graph calls captured in one HIP graph, replayed
+    `replays` times on `stream` (the median replay over per_graph): the GPU's time for a call
+    without the host's per-call overhead (which is larger than a small call's GPU time).  fn must
+    allocate nothing."""
     import torch
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -138,14 +286,8 @@ def time_graph(fn, per_graph, replays, stream):
         for _ in range(3):
             graph.replay()
         torch.cuda.synchronize()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(replays):
-            graph.replay()
-        end.record(stream)
-        end.synchronize()
-    return start.elapsed_time(end) / 1e3 / (replays * per_graph)
+        t = time_each(graph.replay, replays, stream)
+    return median(t) / per_graph
 
 
 def main():
@@ -206,40 +348,51 @@ def main():
         append()
         decode()
 
+    decode_bytes = L * T * HKV * BYTES_PER_TOKEN_HEAD
+    step_bytes = decode_bytes + L * HKV * 2 * (2 * D + 48 + 4)   # + the new K/V: bf16 read, record written
+    tokens_per_step = L * T
+
+    # ---------------- untimed work first: the clocks settle ----------------
+    # the device's read-only streaming rate over as many bytes as the step reads (libiq_probe.so):
+    # the measured ceiling beside the nominal 8 TB/s.  It runs before the timed steps, and the step
+    # itself then runs untimed for --settle seconds, whatever --warmup says: a GPU that has just
+    # started needs about a second of work before its clocks are steady.
+    stream_gbs = t_stream = None
+    if not args.decode_only:
+        sbuf = torch.empty(decode_bytes, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(4, dtype=torch.uint8, device=dev)
+
+        def stream_pass():
+            iq.stream_read(sbuf, sink, 2048)
+
+        settle(stream_pass, 0.5)
+        t_stream = median(time_each(stream_pass, 50, stream))
+        stream_gbs = decode_bytes / t_stream / 1e9
+        del sbuf
+        log("read-only stream of %d bytes: %.1f us (median of 50), %.0f GB/s" %
+            (decode_bytes, t_stream * 1e6, stream_gbs))
+    n_settle = settle(step, args.settle)
+    log("settle: %d untimed steps in >= %.1f s" % (n_settle, args.settle))
+
     # ---------------- timed steps ----------------
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t_step = time_calls(step, args.steps, stream)
-    t_decode = time_calls(decode, args.steps, stream)
-    t_append = time_calls(append, args.steps, stream)
-    t_two = time_calls(two_calls, args.steps, stream)
-    log("step %.1f us (decode alone %.1f us, append alone %.1f us, append then decode %.1f us)" %
-        (t_step * 1e6, t_decode * 1e6, t_append * 1e6, t_two * 1e6))
-
-    decode_bytes = L * T * HKV * BYTES_PER_TOKEN_HEAD
-    step_bytes = decode_bytes + L * HKV * 2 * (2 * D + 48 + 4)   # + the new K/V: bf16 read, record written
+    steps_t = time_each(step, args.steps, stream)
+    t_step = median(steps_t)
+    t_decode = median(time_each(decode, args.steps, stream))
+    t_append = median(time_each(append, args.steps, stream))
+    t_two = median(time_each(two_calls, args.steps, stream))
+    log("step median %.1f us (min %.1f, max %.1f over %d); decode alone %.1f us, append alone %.1f us, "
+        "append then decode %.1f us" % (t_step * 1e6, steps_t[0] * 1e6, steps_t[-1] * 1e6, len(steps_t),
+                                        t_decode * 1e6, t_append * 1e6, t_two * 1e6))
     step_gbs = step_bytes / t_step / 1e9
-    tokens_per_step = L * T
+    t_step_mean = sum(steps_t) / len(steps_t)
+    step_gbs_mean = step_bytes / t_step_mean / 1e9
 
     if args.decode_only:
         print(json.dumps({"step_us": t_step * 1e6, "decode_us": t_decode * 1e6, "step_GBs": step_gbs}), flush=True)
         return
-
-    # the device's read-only streaming rate over as many bytes as the step reads (libiq_probe.so):
-    # the measured ceiling beside the nominal 8 TB/s
-    sbuf = torch.empty(decode_bytes, dtype=torch.uint8, device=dev)
-    sink = torch.zeros(4, dtype=torch.uint8, device=dev)
-
-    def stream_pass():
-        iq.stream_read(sbuf, sink, 2048)
-
-    for _ in range(10):
-        stream_pass()
-    t_stream = time_calls(stream_pass, 50, stream)
-    stream_gbs = decode_bytes / t_stream / 1e9
-    del sbuf
-    log("read-only stream of %d bytes: %.1f us, %.0f GB/s" % (decode_bytes, t_stream * 1e6, stream_gbs))
 
     # single-layer decode call (the one-layer shape, unadjusted)
     ws1 = torch.empty(iq.decode_workspace_bytes(1, HQ, HKV, T), dtype=torch.uint8, device=dev)
@@ -249,10 +402,9 @@ def main():
         iq.decode_attention(q[:1], kc[:1], ks[:1], vc[:1], vs[:1], rot[:1], seq_lens=lens[:1], out=out1,
                             workspace=ws1)
 
-    for _ in range(args.warmup):
-        decode1()
-    t_eager1 = time_calls(decode1, args.steps, stream)
-    t_decode1 = time_graph(decode1, 20, max(5, args.steps // 20), stream)
+    settle(decode1, 0.2)
+    t_eager1 = median(time_each(decode1, max(20, args.steps), stream))
+    t_decode1 = time_graph(decode1, 20, max(10, args.steps // 10), stream)
     single = {"ms": t_decode1 * 1e3, "GBs": T * HKV * BYTES_PER_TOKEN_HEAD / t_decode1 / 1e9,
               "kv_tokens_per_s": T / t_decode1, "timing": "graph of 20 calls, replayed",
               "eager_ms": t_eager1 * 1e3}
@@ -305,8 +457,8 @@ def main():
             iq.quantize_kv(kt, vt, rott, kct, kst, vct, vst, fmt=fmt)
             err_t = rel_err(iq.decode_attention(qt, kct, kst, vct, vst, rott, fmt=fmt)[0], ref_t)
             del kct, vct, kst, vst
-            t_qf = time_calls(quant_f, 5, stream)
-            t_df = time_calls(dec_f, 20, stream)
+            t_qf = median(time_each(quant_f, 7, stream))
+            t_df = median(time_each(dec_f, 21, stream))
             cache_b = L * HKV * T * 2 * (rb + 4 * sw)
             formats[fmt] = {"bits": iq.FORMAT_BITS[fmt], "record_bytes": rb,
                             "attention_rel_error_long32k_layer0": err, "attention_rel_error_gaussian": err_t,
@@ -330,7 +482,7 @@ def main():
 
             for _ in range(20):
                 dec_m()
-            t_m = time_calls(dec_m, max(20, args.steps // 8), stream)
+            t_m = median(time_each(dec_m, max(20, args.steps // 8), stream))
             flops = 2 * 2 * L * Qm * HQ * T * D       # QK and PV multiply-adds, causal tail ignored
             multi["q%d" % Qm] = {"query_tokens": Qm, "ms": t_m * 1e3, "kv_tokens_per_s": L * T / t_m,
                                  "query_token_kv_per_s": L * T * Qm / t_m,
@@ -367,10 +519,9 @@ def main():
             def dec_o():
                 iq.decode_attention(qo, kco, kso, vco, vso, roto, seq_lens=lo, out=outo, workspace=wso)
 
-            for _ in range(args.warmup // 4):
-                dec_o()
-            t_e = time_calls(dec_o, max(20, args.steps // 4), stream)
-            t_o = time_graph(dec_o, 20, max(5, args.steps // 20), stream)
+            settle(dec_o, 0.2)
+            t_e = median(time_each(dec_o, max(20, args.steps // 4), stream))
+            t_o = time_graph(dec_o, 20, max(10, args.steps // 10), stream)
             toks = int(wo["seq_lens"].sum())
             others[name] = {"batch": int(Bo), "n_q_heads": int(Hqo), "n_kv_heads": int(Hkvo), "cache_cap": int(To),
                             "kv_tokens": toks, "ms": t_o * 1e3, "kv_tokens_per_s": toks / t_o,
@@ -408,7 +559,8 @@ def main():
 
         quant()
         torch.cuda.synchronize()
-        t_q = time_calls(quant, max(3, args.steps // 4), stream)
+        settle(quant, 0.3)
+        t_q = median(time_each(quant, max(10, args.steps // 4), stream))
         qbytes = LAYERS * HKV * T * 2 * (D * 2 + 48 + 4)
         prefill = {"workload": "prefill 48x4x32768 K+V bf16 Student-t(3)", "ms": t_q * 1e3,
                    "GBs": qbytes / t_q / 1e9, "frac_of_hbm_peak": qbytes / t_q / 1e9 / HBM_PEAK_GBS,
@@ -436,28 +588,21 @@ def main():
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-        try:
-            from threadpoolctl import threadpool_info
-            blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-        except Exception:
-            blas_threads = 1
-        kcn, ksn, vcn, vsn = kc.cpu().numpy(), ks.cpu().numpy(), vc.cpu().numpy(), vs.cpu().numpy()
-        qn = q.float().cpu().numpy().astype(np.float64)
-        rotn = rot.cpu().numpy()
-        done, t0 = 0, time.time()
-        while done < L and (done == 0 or time.time() - t0 < args.cpu_seconds):
-            l = done
-            oracle.decode_attention(qn[l:l + 1], oracle.unpack(kcn[l:l + 1]), ksn[l:l + 1],
-                                    oracle.unpack(vcn[l:l + 1]), vsn[l:l + 1], rotn[l:l + 1], np.array([T]))
-            done += 1
-        el = time.time() - t0
-        cpu = {"value": done * T / el, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
-               "sample": "%d of %d layers (4 KV heads, 32 query heads, 32768 tokens each): oracle unpack of the "
-                         "packed caches + fp64 decode attention, %.1f s; numpy single-threaded except BLAS" %
-                         (done, L, el)}
-        log("cpu oracle: %d layers in %.1fs" % (done, el))
-
+        t0 = time.time()
+        host = host_info()
+        by_cfg = cpu_baselines(args.cpu_seconds)
+        log("cpu oracle baselines in %.1fs: %s" % (time.time() - t0, ", ".join(
+            "%s %.3g/%.3g %s (1 thread / all)" % (k, v["single_thread"], v["all_cores"], v["unit"])
+            for k, v in by_cfg.items())))
+        main_cfg = by_cfg["long32k"]
+        cpu = {"value": main_cfg["all_cores"], "unit": "KV tokens/s", "cores": host["blas_threads"],
+               "kind": "oracle",
+               "sample": "long32k shape, one layer: %s; oracle unpack of the packed K/V records + fp64 decode "
+                         "attention, repeated for %.1f s, with BLAS's %d threads (numpy itself single-threaded)" %
+                         (main_cfg["sample"], args.cpu_seconds, host["blas_threads"]),
+               "single_thread_value": main_cfg["single_thread"],
+               "host": host,
+               "by_workload": by_cfg}
     res = {
         "metric": "3-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% peak) at 32K",
         "value": tokens_per_step / t_step,
@@ -466,6 +611,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": t_step * 1e3,
+        "step_timing": {"how": "median of --steps calls, each between its own HIP event pair on the call's "
+                               "stream, after a read-only stream probe, %d untimed steps over >= %.1f s and "
+                               "--warmup more" % (n_settle, args.settle),
+                        "median_us": t_step * 1e6, "min_us": steps_t[0] * 1e6, "max_us": steps_t[-1] * 1e6},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -476,11 +625,12 @@ def main():
                                "K/V appended and layer-stacked decode attention in one launch)" % L,
                    "layers": L, "batch": 1, "n_q_heads": HQ, "n_kv_heads": HKV, "context": T,
                    "head_dim": D, "kv_bits": 3},
-        "roofline": {"bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": step_gbs / HBM_PEAK_GBS, "traffic": measured_traffic(),
+        "roofline": {"bound": "hbm", "achieved": step_gbs_mean, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": step_gbs_mean / HBM_PEAK_GBS, "traffic": measured_traffic(),
                      "kernel": "iq_decode_attention_append (decode_split_kernel with the append, combine_kernel)",
-                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": t_step * 1e6,
-                     "frac_of_measured_stream": step_gbs / stream_gbs},
+                     "algorithmic_bytes_per_launch": step_bytes, "avg_launch_us": t_step_mean * 1e6,
+                     "median_launch_us": t_step * 1e6, "frac_at_median": step_gbs / HBM_PEAK_GBS,
+                     "frac_of_measured_stream": step_gbs_mean / stream_gbs},
         "stream_read": {"GBs": stream_gbs, "bytes": decode_bytes, "us": t_stream * 1e6,
                         "kernel": "iq_probe_stream_read (libiq_probe.so): 16-byte loads, grid-stride, 2048 x 256 threads"},
         "decode_only": {"ms": t_decode * 1e3, "GBs": decode_bytes / t_decode / 1e9},
