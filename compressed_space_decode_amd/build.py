@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libiq.so")
-SOURCES = ["iq_api.hip", "iq_quantize.hip", "iq_decode.hip", "iq_diag.hip", "iq_formats.hip", "iq_rotation.cpp"]
+SOURCES = ["iq_api.hip", "iq_quantize.hip", "iq_decode.hip", "iq_diag.hip", "iq_formats.hip", "iq_noalloc.hip",
+           "iq_rotation.cpp"]
 PROBE_LIB = os.path.join(PKG, "libiq_probe.so")
 PROBE_SOURCES = ["iq_probe.hip"]
 ARCH = "gfx950"

@@ -200,15 +200,17 @@ extern "C" int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads, i
   return iq::decode_geometry(batch, n_q_heads, n_kv_heads, cache_cap).workspace_bytes;
 }
 
-namespace {
+namespace iq {
 
 // iq_decode_attention (q_tokens = 1) and iq_decode_attention_multi: the batch's q_tokens query
 // tokens per sequence run as batch * q_tokens sequences of the kernels that share their cache.
-int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens, const uint8_t* k_codes,
-                const float* k_scales, const uint8_t* v_codes, const float* v_scales, const float* rot,
-                int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
-                int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out, void* workspace,
-                int64_t workspace_bytes, int32_t format, void* stream) {
+// scratch_call: the workspace is the library's own scratch of workspace_bytes bytes
+// (iq_decode_attention_noalloc, one query token): it must hold what this call's kernels use.
+int decode_entry(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens, const uint8_t* k_codes,
+                 const float* k_scales, const uint8_t* v_codes, const float* v_scales, const float* rot,
+                 int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                 int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out, void* workspace,
+                 int64_t workspace_bytes, int32_t format, void* stream, bool scratch_call) {
   int rc = IQ_OK;
   if (q_dtype != IQ_F32 && q_dtype != IQ_BF16) {
     iq::set_error("%s: unknown q_dtype %d", fn, q_dtype);
@@ -248,7 +250,14 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
     return IQ_EINVAL;
   }
   const iq::DecodeGeometry geo = iq::decode_geometry(batch * q_tokens, n_q_heads, n_kv_heads, cache_cap);
-  if (!workspace || workspace_bytes < geo.workspace_bytes || !aligned(workspace, 256)) {
+  if (scratch_call) {
+    const int64_t need = iq::decode_single_bytes(geo, n_q_heads);
+    if (q_tokens != 1 || need > workspace_bytes) {
+      iq::set_error("%s: these sizes need %lld bytes of scratch, more than the library's %lld", fn,
+                    (long long)need, (long long)workspace_bytes);
+      return IQ_EWORKSPACE;
+    }
+  } else if (!workspace || workspace_bytes < geo.workspace_bytes || !aligned(workspace, 256)) {
     iq::set_error("%s: workspace must be 256-byte aligned and hold %lld bytes (got %lld)", fn,
                   (long long)geo.workspace_bytes, (long long)workspace_bytes);
     return IQ_EWORKSPACE;
@@ -281,7 +290,7 @@ int decode_impl(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens
   return IQ_OK;
 }
 
-}  // namespace
+}  // namespace iq
 
 extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t* k_codes, const float* k_scales,
                                    const uint8_t* v_codes, const float* v_scales, const float* rot,
@@ -293,8 +302,9 @@ extern "C" int iq_decode_attention(const void* q, int32_t q_dtype, const uint8_t
   iq::clear_error();
   const int rc = check_dims(fn, head_dim, bits);
   if (rc) return rc;
-  return decode_impl(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens, batch,
-                     n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, IQ_FMT_U3, stream);
+  return iq::decode_entry(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens,
+                          batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, IQ_FMT_U3,
+                          stream, false);
 }
 
 extern "C" int iq_decode_attention_format(const void* q, int32_t q_dtype, const uint8_t* k_codes,
@@ -307,8 +317,9 @@ extern "C" int iq_decode_attention_format(const void* q, int32_t q_dtype, const 
   iq::clear_error();
   const int rc = check_format(fn, head_dim, format);
   if (rc) return rc;
-  return decode_impl(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens, batch,
-                     n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, format, stream);
+  return iq::decode_entry(fn, q, q_dtype, 1, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch, seq_lens,
+                          batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes, format,
+                          stream, false);
 }
 
 extern "C" int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t n_q_tokens,
@@ -322,9 +333,9 @@ extern "C" int iq_decode_attention_multi(const void* q, int32_t q_dtype, int32_t
   iq::clear_error();
   const int rc = check_dims(fn, head_dim, bits);
   if (rc) return rc;
-  return decode_impl(fn, q, q_dtype, n_q_tokens, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch,
-                     seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes,
-                     IQ_FMT_U3, stream);
+  return iq::decode_entry(fn, q, q_dtype, n_q_tokens, k_codes, k_scales, v_codes, v_scales, rot, rot_stride_batch,
+                          seq_lens, batch, n_q_heads, n_kv_heads, cache_cap, sm_scale, out, workspace, workspace_bytes,
+                          IQ_FMT_U3, stream, false);
 }
 
 extern "C" int iq_decode_attention_append(const void* q, int32_t q_dtype, const void* k_new, const void* v_new,

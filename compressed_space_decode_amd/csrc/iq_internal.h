@@ -93,4 +93,18 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
 
 hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipStream_t stream);
 
+// Bytes of the workspace that one single-token call with this geometry uses: the plan head and
+// x_max partial rows per query head (the workspace query adds room for several query tokens).
+inline int64_t decode_single_bytes(const DecodeGeometry& geo, int n_q_heads) {
+  return geo.plan_bytes + (int64_t)geo.x_max * n_q_heads * (128 + 2) * 4;
+}
+
+// Validation and launch shared by the decode entry points (iq_api.hip).  scratch_call: workspace is
+// the library's own scratch of workspace_bytes bytes, which must hold what the call uses.
+int decode_entry(const char* fn, const void* q, int32_t q_dtype, int32_t q_tokens, const uint8_t* k_codes,
+                 const float* k_scales, const uint8_t* v_codes, const float* v_scales, const float* rot,
+                 int64_t rot_stride_batch, const int32_t* seq_lens, int32_t batch, int32_t n_q_heads,
+                 int32_t n_kv_heads, int64_t cache_cap, float sm_scale, float* out, void* workspace,
+                 int64_t workspace_bytes, int32_t format, void* stream, bool scratch_call);
+
 }  // namespace iq

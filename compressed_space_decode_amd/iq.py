@@ -42,6 +42,8 @@ SIGNATURES = {
                                                   _P]),
     "iq_decode_attention_multi": (ctypes.c_int, [_P, _I32, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
                                                  _I64, _F, _P, _P, _I64, _I32, _I32, _P]),
+    "iq_decode_attention_noalloc": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
+                                                   _I64, _F, _P, _I32, _I32, _P]),
     "iq_quantize_kv_format": (ctypes.c_int, [_P, _P, _I32, _I64, _I32, _I64, _I64, _I64, _I64, _P, _I64,
                                              _P, _P, _P, _P, _I64, _I64, _I32, _I32, _P]),
     "iq_decode_attention_format": (ctypes.c_int, [_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _I32, _I32, _I32,
@@ -196,6 +198,41 @@ def decode_attention(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None
         rc = lib().iq_decode_attention(*args, BITS, _stream(q))
     else:
         rc = lib().iq_decode_attention_format(*args, FORMATS[fmt], _stream(q))
+    _check(rc)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20   # IQ_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attention_noalloc(q, k_codes, k_scales, v_codes, v_scales, rot, seq_lens=None, sm_scale=0.0,
+                             out=None, shared_rot=False):
+    """decode_attention without a workspace (iq_decode_attention_noalloc): the library's own
+    per-device scratch holds the split-K partials.  Same arguments and result; `out` must be given
+    when no allocation may happen (else it is allocated here)."""
+    import torch
+    B, Hq, d = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    if d != HEAD_DIM or not q.is_contiguous():
+        raise ValueError("q must be contiguous [B][Hq][128]")
+    for t in (k_codes, k_scales, v_codes, v_scales, rot):
+        if not t.is_contiguous():
+            raise ValueError("cache and rotation tensors must be contiguous")
+    for c, sc in ((k_codes, k_scales), (v_codes, v_scales)):
+        if tuple(c.shape) != (B, Hkv, cap, RECORD_BYTES) or tuple(sc.shape) != (B, Hkv, cap):
+            raise ValueError("caches must be [B][Hkv][cap][48] codes and [B][Hkv][cap] scales")
+    if rot.numel() != (Hkv if shared_rot else B * Hkv) * ROT_PARAMS:
+        raise ValueError("rot has the wrong number of values")
+    if seq_lens is not None and (seq_lens.numel() != B or seq_lens.dtype != torch.int32
+                                 or not seq_lens.is_contiguous()):
+        raise ValueError("seq_lens must be a contiguous int32 tensor with one length per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    rc = lib().iq_decode_attention_noalloc(
+        q.data_ptr(), _dtype_code(q), k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
+        v_scales.data_ptr(), rot.data_ptr(), 0 if shared_rot else Hkv * ROT_PARAMS,
+        seq_lens.data_ptr() if seq_lens is not None else None, B, Hq, Hkv, cap, float(sm_scale), out.data_ptr(),
+        HEAD_DIM, BITS, _stream(q))
     _check(rc)
     return out
 

@@ -221,6 +221,33 @@ int iq_decode_attention(const void* q, int32_t q_dtype,
                         int32_t head_dim, int32_t bits, void* stream);
 
 /*
+ * iq_decode_attention_noalloc -- iq_decode_attention for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It takes no workspace: the split plan and
+ * the split-K partials live in a device array of IQ_NOALLOC_SCRATCH_BYTES
+ * inside the library, one per device, which holds it until the process ends.
+ * The call itself allocates and frees nothing.
+ *   Arguments, kernels and results as iq_decode_attention (the output is the
+ *   same bit for bit), without workspace and workspace_bytes.
+ *   Every call on a device shares that device's array: calls that overlap
+ *   on one device (on other streams or from other host threads) race and give
+ *   undefined results.  Nothing in the array needs clearing between calls.
+ * Errors: as iq_decode_attention; IQ_EWORKSPACE when the sizes need more than
+ * IQ_NOALLOC_SCRATCH_BYTES (plan head plus 520 bytes per query head per work
+ * item of the split: e.g. 48 stacked 32K layers of 32 query heads need about
+ * 3.2 MB), IQ_EHIP when the array's device address cannot be looked up.
+ */
+#define IQ_NOALLOC_SCRATCH_BYTES (8 << 20)
+int iq_decode_attention_noalloc(const void* q, int32_t q_dtype,
+                                const uint8_t* k_codes, const float* k_scales,
+                                const uint8_t* v_codes, const float* v_scales,
+                                const float* rot, int64_t rot_stride_batch,
+                                const int32_t* seq_lens,
+                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                int64_t cache_cap, float sm_scale, float* out,
+                                int32_t head_dim, int32_t bits, void* stream);
+
+/*
  * iq_decode_attention_format -- iq_decode_attention on a cache written by
  * iq_quantize_kv_format with the same format (codes [batch][n_kv_heads]
  * [cache_cap][16*b]).  Source: Abstract (attention on the packed tensors).

@@ -27,6 +27,7 @@ def test_header_declares_the_boundary():
     assert _declared() == sorted(["iq_last_error", "iq_make_rotation", "iq_quantize_kv",
                                   "iq_decode_workspace_bytes", "iq_decode_attention",
                                   "iq_decode_attention_append", "iq_decode_attention_multi",
+                                  "iq_decode_attention_noalloc",
                                   "iq_quantize_kv_format", "iq_decode_attention_format",
                                   "iq_isotropy_workspace_bytes",
                                   "iq_isotropy_stats"])
