@@ -449,13 +449,12 @@ struct WaveLoopSmem {
   float sc[64];           // the block's K scales (lanes 0-31) and V scales (lanes 32-63)
   float mn[64];           // asymmetric format: the matching minima m
 };
-// Computed once per work-group by wave 0: sum of q' per head and the operand exponent E, with
-// wave 0's scratch.  Shares storage with the loop staging (a barrier separates them).
+// Computed once per work-group: the rotated queries, the sum of q' and the operand exponent E of
+// each head.  Shares storage with the loop staging (a barrier separates them).
 struct SetupSmem {
   float qrot[8][128];
-  float blk[32][16];
   float qsum[8];
-  int E;
+  int E[8];
 };
 union DecodeSmemU {
   MergeSmem merge;
@@ -682,7 +681,7 @@ __device__ __forceinline__ void progress_priority(int done, int span) {
 template <bool kRefill, int kFmt>
 __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
-                                              WaveState& st, const uint4v (&qop)[4][64], float c1,
+                                              WaveState& st, const uint4v (&qop)[4][64], const float (&c1)[2],
                                               const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
                                               unsigned pwr, unsigned prd, const LevelTable& lt) {
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
@@ -778,14 +777,14 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
     mv[1] = ws.mn[48 + n];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      z[j][0] = fmaf(sk0 * c1, S[0][2 * j] + S[0][2 * j + 1], mk0 * c2[j]);
-      z[j][1] = fmaf(sk1 * c1, S[1][2 * j] + S[1][2 * j + 1], mk1 * c2[j]);
+      z[j][0] = fmaf(sk0 * c1[j], S[0][2 * j] + S[0][2 * j + 1], mk0 * c2[j]);
+      z[j][1] = fmaf(sk1 * c1[j], S[1][2 * j] + S[1][2 * j + 1], mk1 * c2[j]);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      z[j][0] = sk0 * fmaf(S[0][2 * j] + S[0][2 * j + 1], c1, -c2[j]);
-      z[j][1] = sk1 * fmaf(S[1][2 * j] + S[1][2 * j + 1], c1, -c2[j]);
+      z[j][0] = sk0 * fmaf(S[0][2 * j] + S[0][2 * j + 1], c1[j], -c2[j]);
+      z[j][1] = sk1 * fmaf(S[1][2 * j] + S[1][2 * j + 1], c1[j], -c2[j]);
     }
   }
   if (rem < kBlock) {                                         // last, partial block only
@@ -865,34 +864,52 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
   __builtin_amdgcn_wave_barrier();
 }
 
-// Wave 0's set-up loads for sequence b: this lane's 16 query coordinates (head h0 + lane/8, slice
-// lane%8; raw bf16 pairs in q0-q1 or fp32 words in q0-q3) and the 8 rotation parameters of SO(4)
-// block lane%32.
+// The set-up loads of thread (head row hr = tid / 32, SO(4) block kq = tid % 32) for sequence b:
+// query coordinates 4 kq .. 4 kq + 3 of head h0 + hr (raw bf16 pairs in q.x, q.y, or fp32 words)
+// and the 8 rotation parameters of block kq.
 struct SetupLoads {
-  uint4 q0, q1, q2, q3;
-  float4 r0, r1;
+  uint4 q;
+  float r[8];
 };
-__device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, int g, int h0, int nh, int lane) {
+__device__ __forceinline__ SetupLoads load_setup(const DecodeKArgs& a, int b, int g, int h0, int nh, int tid) {
   SetupLoads v;
-  const int qi = lane >> 3, qe = lane & 7;
+  const int hr = tid >> 5, kq = tid & 31;
   const int bc = a.q_tokens > 1 ? b / a.q_tokens : b;          // the cache (and rotation) of sequence b
-  const int64_t off = ((int64_t)b * a.Hq + h0 + (qi < nh ? qi : 0)) * 128 + 16 * qe;
+  const int64_t off = ((int64_t)b * a.Hq + h0 + (hr < nh ? hr : 0)) * 128 + 4 * kq;
   if (a.q_bf16) {
-    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + off);
-    v.q0 = qp[0];
-    v.q1 = qp[1];
-    v.q2 = v.q3 = make_uint4(0u, 0u, 0u, 0u);
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q) + off);
+    v.q = make_uint4(w.x, w.y, 0u, 0u);
   } else {
-    const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + off);
-    v.q0 = qp[0];
-    v.q1 = qp[1];
-    v.q2 = qp[2];
-    v.q3 = qp[3];
+    v.q = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.q) + off);
   }
-  const float* rq = a.rot + bc * a.rot_stride_b + (int64_t)g * 256 + (lane & 31) * 8;
-  v.r0 = make_float4(rq[0], rq[1], rq[2], rq[3]);
-  v.r1 = make_float4(rq[4], rq[5], rq[6], rq[7]);
+  const float* rq = a.rot + bc * a.rot_stride_b + (int64_t)g * 256 + kq * 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v.r[i] = rq[i];
   return v;
+}
+
+__device__ __forceinline__ float dpp_ror8(float x) {   // row_ror:8 = lane ^ 8 within a row of 16
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float swz_xor16(float x) {  // bitmask swizzle, xor 16 (within 32 lanes)
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (16 << 10) | 0x1F));
+}
+// x ^ m partner within the 32 lanes of a half-wave, m = 1, 2, 4, 8, 16.
+template <int kM>
+__device__ __forceinline__ float xor32(float x) {
+  if constexpr (kM == 1) return dpp_xor1(x);
+  else if constexpr (kM == 2) return dpp_xor2(x);
+  else if constexpr (kM == 4) return swz_xor4(x);
+  else if constexpr (kM == 8) return dpp_ror8(x);
+  else return swz_xor16(x);
+}
+// One cross-lane Hadamard stage over bit log2(kM) of the block index kq: the lane with that bit
+// set takes partner - mine, the other mine + partner.
+template <int kM>
+__device__ __forceinline__ void hadamard_stage(float (&x)[4], int kq) {
+  const float sg = (kq & kM) ? -1.f : 1.f;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] = fmaf(sg, x[r], xor32<kM>(x[r]));
 }
 
 // kFmt: IQ_FMT_U3 (the pages' records; the only one with the fused append), IQ_FMT_A3 (the same
@@ -931,14 +948,13 @@ void decode_split_kernel(DecodeKArgs a) {
   const int raw0 = len_raw(src, lane);                       // sequences 0..63
   int b_guess = x / a.guess_per_seq;
   if (b_guess > a.batch - 1) b_guess = a.batch - 1;
-  // (every wave issues them, so that all waves have the same loads in flight when the plan waits
-  // for the lengths; only wave 0 uses them)
-  SetupLoads sl = load_setup(a, b_guess, g, h0, nh, lane);
+  // (every thread rotates one SO(4) block of one query head)
+  SetupLoads sl = load_setup(a, b_guess, g, h0, nh, tid);
   const int l0 = len_of(src, lane, raw0);
   const ChunkPlan plan = plan_chunks(src, l0, a.target, x, lane);
   if (plan.b < 0) return;                                    // uniform: past the last chunk
   const int b = plan.b;
-  if (wave == 0 && b != b_guess) sl = load_setup(a, b, g, h0, nh, lane);   // uniform
+  if (b != b_guess) sl = load_setup(a, b, g, h0, nh, tid);   // uniform
   const int len = plan.len;          // > 0
   // the combine reads the plan from here
   if (tid == 0 && blockIdx.x == 0) {
@@ -979,102 +995,68 @@ void decode_split_kernel(DecodeKArgs a) {
   load_block<kFmt>(buf, cb, t0, reload ? 0 : tok_end, lo);
   load_block<kFmt>(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
 
-  // ---------------- set-up (wave 0): rotate the queries, build the QK operand ----------------
+  // ---------------- set-up (all waves): rotate the queries ----------------
+  // Thread (head row hr, block kq) holds coordinates 4 kq .. 4 kq + 3 of its head.  H_128 =
+  // (I_32 x H_4)(H_32 x I_4): H_4 inside the thread, then five butterfly stages across the 32
+  // lanes of the head, then SO(4) block kq and the 1/sqrt(128).
   SetupSmem& ss = sm.u.setup;
-  if (wave == 0) {
-    if (lane < 32) {
-      const float rp[8] = {sl.r0.x, sl.r0.y, sl.r0.z, sl.r0.w, sl.r1.x, sl.r1.y, sl.r1.z, sl.r1.w};
-      build_block(rp, ss.blk[lane]);
+  {
+    const int hr = tid >> 5, kq = tid & 31;
+    float xq[4];
+    if (a.q_bf16) {
+      xq[0] = __uint_as_float(sl.q.x << 16);
+      xq[1] = __uint_as_float(sl.q.x & 0xFFFF0000u);
+      xq[2] = __uint_as_float(sl.q.y << 16);
+      xq[3] = __uint_as_float(sl.q.y & 0xFFFF0000u);
+    } else {
+      xq[0] = __uint_as_float(sl.q.x);
+      xq[1] = __uint_as_float(sl.q.y);
+      xq[2] = __uint_as_float(sl.q.z);
+      xq[3] = __uint_as_float(sl.q.w);
     }
-    const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
-    float x[16];
+    if (hr >= nh) xq[0] = xq[1] = xq[2] = xq[3] = 0.f;
     {
-      const bool have = qi < nh;
-      if (a.q_bf16) {
-        const unsigned w[8] = {sl.q0.x, sl.q0.y, sl.q0.z, sl.q0.w, sl.q1.x, sl.q1.y, sl.q1.z, sl.q1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          x[2 * i] = __uint_as_float(w[i] << 16);
-          x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-      } else {
-        const uint4 qv[4] = {sl.q0, sl.q1, sl.q2, sl.q3};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[4 * i] = __uint_as_float(qv[i].x); x[4 * i + 1] = __uint_as_float(qv[i].y);
-          x[4 * i + 2] = __uint_as_float(qv[i].z); x[4 * i + 3] = __uint_as_float(qv[i].w);
-        }
-      }
-      if (!have) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = 0.f;
-      }
+      const float a0 = xq[0] + xq[1], a1 = xq[0] - xq[1], a2 = xq[2] + xq[3], a3 = xq[2] - xq[3];
+      xq[0] = a0 + a2;
+      xq[1] = a1 + a3;
+      xq[2] = a0 - a2;
+      xq[3] = a1 - a3;
     }
-    {
-      // Sylvester Hadamard (unnormalised): strides 16, 32, 64 across lanes qe^1, ^2, ^4,
-      // strides 8, 4, 2, 1 inside the lane.  new = partner + sg * mine.
-      const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
+    hadamard_stage<1>(xq, kq);
+    hadamard_stage<2>(xq, kq);
+    hadamard_stage<4>(xq, kq);
+    hadamard_stage<8>(xq, kq);
+    hadamard_stage<16>(xq, kq);
+    float Mb[16];
+    build_block(sl.r, Mb);
+    float y[4], qamax = 0.f, qs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
-#pragma unroll
-      for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if ((i & m) == 0) {
-            const float u = x[i], v = x[i + m];
-            x[i] = u + v;
-            x[i + m] = u - v;
-          }
+    for (int r = 0; r < 4; ++r) {
+      y[r] = (Mb[4 * r] * xq[0] + Mb[4 * r + 1] * xq[1] + Mb[4 * r + 2] * xq[2] + Mb[4 * r + 3] * xq[3]) * kInvSqrtD;
+      qamax = fmaxf(qamax, fabsf(y[r]));
+      qs += y[r];
     }
-    __builtin_amdgcn_wave_barrier();
-    float qamax = 0.f, qs = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* M = ss.blk[4 * qe + j];
-      float y[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        y[r] = (M[4 * r] * x[4 * j] + M[4 * r + 1] * x[4 * j + 1] + M[4 * r + 2] * x[4 * j + 2] +
-                M[4 * r + 3] * x[4 * j + 3]) * kInvSqrtD;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ss.qrot[qi][16 * qe + 4 * j + r] = y[r];
-        qamax = fmaxf(qamax, fabsf(y[r]));
-        qs += y[r];
+    *reinterpret_cast<float4*>(&ss.qrot[hr][4 * kq]) = make_float4(y[0], y[1], y[2], y[3]);
+    // per head: the sum of q' and the operand exponent E (largest |q'| 2^E in [2^13, 2^14))
+    qamax = fmaxf(qamax, xor32<1>(qamax));
+    qamax = fmaxf(qamax, xor32<2>(qamax));
+    qamax = fmaxf(qamax, xor32<4>(qamax));
+    qamax = fmaxf(qamax, xor32<8>(qamax));
+    qamax = fmaxf(qamax, xor32<16>(qamax));
+    qs += xor32<1>(qs);
+    qs += xor32<2>(qs);
+    qs += xor32<4>(qs);
+    qs += xor32<8>(qs);
+    qs += xor32<16>(qs);
+    if (kq == 0) {
+      int E = 0;
+      if (qamax > 0.f) {
+        int ex;
+        frexpf(qamax, &ex);
+        E = 14 - ex;
       }
-    }
-    // Operand scaling 2^E keeps the largest |q'| * 2^E in [2^13, 2^14).
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) qamax = fmaxf(qamax, wave_xor(qamax, m));
-    qs += dpp_xor1(qs);
-    qs += dpp_xor2(qs);
-    qs += swz_xor4(qs);               // sum of q' over head qi (all 8 lanes of the head)
-    int E = 0;
-    if (qamax > 0.f) {
-      int ex;
-      frexpf(qamax, &ex);
-      E = 14 - ex;
-    }
-    if (qe == 0) ss.qsum[qi] = qs;
-    if (lane == 0) ss.E = E;
-    __builtin_amdgcn_wave_barrier();
-    // A operand of the QK product: lane row n = (head n/2, part n%2), K slots of quarter g4.
-    const int head = n >> 1, part = n & 1;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      _Float16 hv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int s = 8 * kb + e;
-        const float v = ldexpf(ss.qrot[head][32 * g4 + slot_coord_f<kFmt>(s)], E - slot_pow_f<kFmt>(s));
-        const _Float16 hi = (_Float16)v;
-        hv[e] = part ? (_Float16)(v - (float)hi) : hi;
-      }
-      sm.qop[kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+      ss.qsum[hr] = qs;
+      ss.E[hr] = E;
     }
   }
   // ---------------- fused append (wave 1 of the chunk that holds the new token) ----------------
@@ -1108,13 +1090,28 @@ void decode_split_kernel(DecodeKArgs a) {
     }
   }
   __syncthreads();
-  const int E = ss.E;
+  // A operand of the QK product, built by wave w for K slots 8w .. 8w + 7 of every lane: lane row
+  // n = (head n/2, part n%2), K slots of quarter g4.
+  {
+    const int kb = wave, head = n >> 1, part = n & 1;
+    const int Eh = ss.E[head];
+    _Float16 hv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int sl8 = 8 * kb + e;
+      const float v = ldexpf(ss.qrot[head][32 * g4 + slot_coord_f<kFmt>(sl8)], Eh - slot_pow_f<kFmt>(sl8));
+      const _Float16 hi = (_Float16)v;
+      hv[e] = part ? (_Float16)(v - (float)hi) : hi;
+    }
+    sm.qop[kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+  }
+  const int E0 = ss.E[2 * g4], E1 = ss.E[2 * g4 + 1];
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
-  __syncthreads();                   // the set-up area is staging space from here on
+  __syncthreads();                   // the operand is complete; the set-up area is staging space from here on
   WaveLoopSmem& ws = sm.u.loop[wave];
 
-  // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E).
-  const float c1 = a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E);
+  // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E) for each head's E.
+  const float c1[2] = {a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E0), a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E1)};
   const LevelTable lt = Fmt<kFmt>::kTable ? lm3_table() : LevelTable{};
   // (asymmetric format: c2 = log2(e) sm sum q', the coefficient of the minimum m_K)
   constexpr float kC = kAsym ? 1.f : Fmt<kFmt>::kCenter;
@@ -1667,6 +1664,89 @@ struct CombineArgs {
   float* out;
 };
 
+// o = R^T o' = H (blockdiag M_b^T) o' of one merged row y[128] by one wave (8 lanes, 16 coordinates
+// each; lanes 8..63 repeat lanes 0..7), written to outp[128].
+__device__ __forceinline__ void combine_rotate_store(const float* y, const float (*mats)[16], float* outp, int lane) {
+  const int qe = lane & 7;
+  const float* yr = y + 16 * qe;
+  float x[16];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {       // transposed SO(4) blocks 4qe .. 4qe+3
+    const float* M4 = mats[4 * qe + j];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      x[4 * j + i] = M4[i] * yr[4 * j] + M4[4 + i] * yr[4 * j + 1] + M4[8 + i] * yr[4 * j + 2] +
+                     M4[12 + i] * yr[4 * j + 3];
+  }
+  const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if ((i & m) == 0) {
+        const float u = x[i], v = x[i + m];
+        x[i] = u + v;
+        x[i + m] = u - v;
+      }
+  if (lane < 8) {
+    float4* op = reinterpret_cast<float4*>(outp + 16 * qe);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      op[i] = make_float4(x[4 * i] * kInvSqrtD, x[4 * i + 1] * kInvSqrtD, x[4 * i + 2] * kInvSqrtD,
+                          x[4 * i + 3] * kInvSqrtD);
+  }
+}
+
+// One sequence with one query token: its chunks are partial rows 0 .. nvalid - 1 of every query head
+// (x_max <= kMidChunks of them), so every load (the rows, their (max, sum) pairs, the rotation) is
+// issued at once, unconditionally, before the length and the chunk size arrive: rows past x_max
+// repeat the last row, and rows past nvalid are loaded but not used.  Each wave reduces the (max,
+// sum) pairs itself: no weights through LDS.  An empty sequence gets zeros.
+__device__ __forceinline__ void combine_one_sequence(const CombineArgs& a, int h, float* outp, float* y,
+                                                     float (*mats)[16], int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nr = a.x_max;
+  const float* po = a.part_o + (int64_t)h * nr * 128 + tid;
+  float om[kMidChunks];
+#pragma unroll
+  for (int c = 0; c < kMidChunks; ++c) om[c] = po[(int64_t)min(c, nr - 1) * 128];
+  const float2 mlv = reinterpret_cast<const float2*>(a.part_ml)[(int64_t)h * nr + min(lane, nr - 1)];
+  float rp[8];
+  {
+    const float* rq = a.rot + (int64_t)(h / a.G) * 256 + (lane & 31) * 8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rp[i] = rq[i];
+  }
+  const int chunk = a.plan[0];
+  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, 1, 1, 1, 1}, 0);
+  const int nvalid = len > 0 ? min((len + chunk - 1) / chunk, nr) : 0;
+  const float m = lane < nvalid ? mlv.x : -INFINITY;
+  float M = m;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) M = fmaxf(M, wave_xor(M, sft));
+  const float e = lane < nvalid ? __builtin_amdgcn_exp2f(m - M) : 0.f;
+  float L = e * mlv.y;
+#pragma unroll
+  for (int sft = 1; sft < 64; sft <<= 1) L += wave_xor(L, sft);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < kMidChunks; ++c) {           // rows past nvalid may hold anything: selected out
+    const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), c));
+    acc[c & 7] = fmaf(w, c < nvalid ? om[c] : 0.f, acc[c & 7]);
+  }
+  const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+  y[tid] = nvalid > 0 ? sum / L : 0.f;
+  if (wave == 1 && lane < 32) build_block(rp, mats[lane]);
+  __syncthreads();
+  if (wave == 0) combine_rotate_store(y, mats, outp, lane);
+}
+
 // One work-group (2 waves) per (sequence, query head): log-sum-exp merge of the chunk partials with
 // one output coordinate per thread and independent loads, then o = R^T o' = H (blockdiag M_b^T) o'
 // by one wave (8 lanes, 16 coordinates each, as in the query set-up of the split kernel).
@@ -1677,6 +1757,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   __shared__ float inv_l;
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.q_tokens == 1 && (int)gridDim.x == a.Hq && a.x_max <= kMidChunks) {   // uniform
+    combine_one_sequence(a, h, a.out + (int64_t)h * 128, y, mats, tid);
+    return;
+  }
   // the plan is read together with the length (both entries exist for every sequence; they are
   // used only when the sequence has tokens, and then the split kernel wrote them)
   // output row b is query token b % q_tokens of cache b / q_tokens; its chunks are the work items
@@ -1768,42 +1852,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
   }
   __syncthreads();
-  if (wave == 0) {
-    const int qe = lane & 7;            // 16-coordinate slice; lanes 8..63 repeat lanes 0..7
-    const float* yr = y + 16 * qe;
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {       // transposed SO(4) blocks 4qe .. 4qe+3
-      const float* M4 = mats[4 * qe + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        x[4 * j + i] = M4[i] * yr[4 * j] + M4[4 + i] * yr[4 * j + 1] + M4[8 + i] * yr[4 * j + 2] +
-                       M4[12 + i] * yr[4 * j + 3];
-    }
-    const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if ((i & m) == 0) {
-          const float u = x[i], v = x[i + m];
-          x[i] = u + v;
-          x[i + m] = u - v;
-        }
-    if (lane < 8) {
-      float4* op = reinterpret_cast<float4*>(outp + 16 * qe);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        op[i] = make_float4(x[4 * i] * kInvSqrtD, x[4 * i + 1] * kInvSqrtD, x[4 * i + 2] * kInvSqrtD,
-                            x[4 * i + 3] * kInvSqrtD);
-    }
-  }
+  if (wave == 0) combine_rotate_store(y, mats, outp, lane);
 }
 
 }  // namespace
