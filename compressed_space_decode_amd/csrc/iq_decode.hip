@@ -1661,6 +1661,7 @@ struct CombineArgs {
   int n_groups;                 // of a sequence are x kQ + t % kQ for the work items x of its group
   int64_t cap;
   int x_max;                    // partial rows per query head
+  int guess_per_seq;            // chunks per sequence when every length is cap (the split kernel's guess)
   float* out;
 };
 
@@ -1760,6 +1761,56 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
   if (a.q_tokens == 1 && (int)gridDim.x == a.Hq && a.x_max <= kMidChunks) {   // uniform
     combine_one_sequence(a, h, a.out + (int64_t)h * 128, y, mats, tid);
     return;
+  }
+  // Several sequences of one query token, at most kFewChunks chunks each when every length is cap:
+  // the rows of sequence b under that guess (b gps .. b gps + gps - 1) and their (max, sum) pairs
+  // are loaded together with the plan and the length, and used when the plan agrees (one round
+  // trip instead of two); otherwise the general path below loads the right rows.
+  if (a.q_tokens == 1 && a.guess_per_seq <= kFewChunks) {   // uniform
+    const int gps = a.guess_per_seq, x0g = b * gps;
+    const int64_t hrow = (int64_t)h * a.x_max;
+    float mv[kFewChunks], lv[kFewChunks], ov[kFewChunks];
+#pragma unroll
+    for (int c = 0; c < kFewChunks; ++c) {
+      const int64_t row = hrow + min(x0g + min(c, gps - 1), a.x_max - 1);   // in range; unused past nvalid
+      const float2 v = reinterpret_cast<const float2*>(a.part_ml)[row];
+      mv[c] = v.x;
+      lv[c] = v.y;
+      ov[c] = a.part_o[row * 128 + tid];
+    }
+    float rp[8];
+    {
+      const float* rq = a.rot + b * a.rot_stride_b + (int64_t)(h / a.G) * 256 + (lane & 31) * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rp[i] = rq[i];
+    }
+    const int chunk = a.plan[0];
+    const int x0 = a.plan[64 + b];
+    const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, 1, 1, 1}, b);
+    float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
+    if (len == 0) {                     // an empty sequence attends to nothing
+      outp[tid] = 0.f;
+      return;
+    }
+    const int nvalid = (len + chunk - 1) / chunk;
+    if (x0 == x0g && nvalid <= gps) {   // uniform
+      float M = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < kFewChunks; ++c) M = c < nvalid ? fmaxf(M, mv[c]) : M;
+      float L = 0.f, acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kFewChunks; ++c)
+        if (c < nvalid) {               // uniform; rows past it may hold anything
+          const float w = __builtin_amdgcn_exp2f(mv[c] - M);
+          L = fmaf(w, lv[c], L);
+          acc = fmaf(w, ov[c], acc);
+        }
+      y[tid] = acc / L;
+      if (wave == 1 && lane < 32) build_block(rp, mats[lane]);
+      __syncthreads();
+      if (wave == 0) combine_rotate_store(y, mats, outp, lane);
+      return;
+    }
   }
   // the plan is read together with the length (both entries exist for every sequence; they are
   // used only when the sequence has tokens, and then the split kernel wrote them)
@@ -2020,6 +2071,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.n_groups = multi ? (a.q_tokens + kMultiQ - 1) / kMultiQ : a.q_tokens;
   c.cap = a.cache_cap;
   c.x_max = multi ? xg * kMultiQ : geo.x_max;
+  c.guess_per_seq = geo.guess_per_seq;
   c.out = a.out;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(vb * a.n_q_heads)), dim3(128), 0, stream, c);
   return hipGetLastError();
