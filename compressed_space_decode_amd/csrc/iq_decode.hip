@@ -808,6 +808,7 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
       st.vlim = ldexpf(1.f, ex);
       st.pmul = ldexpf(kPScale, -ex);
     }
+    float f[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float m_new = fmaxf(st.m_run[j], row_max(fmaxf(z[j][0], z[j][1])));
@@ -816,13 +817,12 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
       st.ls_run[j] *= kAsym ? alpha : alpha * ratio;
       st.m_run[j] = m_new;
       st.thr[j] = m_new + kHeadroom;
-      const float f = alpha * ratio;
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        st.O[nt][2 * j] *= f;
-        st.O[nt][2 * j + 1] *= f;
-      }
+      f[j] = alpha * ratio;
     }
+    // whole accumulator tuples (rows 0-1: head 2 g4, rows 2-3: head 2 g4 + 1)
+    const floatx4 fv = {f[0], f[0], f[1], f[1]};
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) st.O[nt] *= fv;
   }
   // ---- probabilities; P'' = p s_V 16 / vlim split hi/lo into the P staging rows ----
   const float svm[2] = {sv0 * st.pmul, sv1 * st.pmul};
@@ -1339,6 +1339,7 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
     }
 #pragma unroll
     for (int i = 0; i < kQ; ++i) {
+      float f[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float m_new = fmaxf(st.m_run[i][j], row_max(fmaxf(z[i][j][0], z[i][j][1])));
@@ -1347,13 +1348,12 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
         st.ls_run[i][j] *= alpha * ratio;
         st.m_run[i][j] = m_new;
         st.thr[i][j] = m_new + kHeadroom;
-        const float f = alpha * ratio;
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-          st.O[i][nt][2 * j] *= f;
-          st.O[i][nt][2 * j + 1] *= f;
-        }
+        f[j] = alpha * ratio;
       }
+      // whole accumulator tuples: no copies of them on the path without a rescale
+      const floatx4 fv = {f[0], f[0], f[1], f[1]};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) st.O[i][nt] *= fv;
     }
   }
   // ---- P'' of each token, staged and read back transposed; PV on the shared V windows ----
