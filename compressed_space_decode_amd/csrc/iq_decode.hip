@@ -73,7 +73,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBlock = 32;          // tokens per wave step
 constexpr int kWavesPerSimd = 3;    // occupancy the split kernel is built for (register budget)
-constexpr int kGroupsPerCU = kWavesPerSimd;   // one wave of each work-group per SIMD
+constexpr int kMaxSplitGroupsPerCU = kWavesPerSimd;   // most resident split work-groups per compute
+                                                      // unit (one wave of each per SIMD), any format
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 8.f;    // log2 units a score may exceed the running max before a rescale
 constexpr float kPScale = 16.f;     // P'' = p s_V 16 / vlim <= 2^8 * 16 = 4096 (fp16 hi and lo parts in range)
@@ -914,10 +915,12 @@ __device__ __forceinline__ void hadamard_stage(float (&x)[4], int kq) {
 
 // kFmt: IQ_FMT_U3 (the pages' records; the only one with the fused append), IQ_FMT_A3 (the same
 // records, an (s, m) pair per token), IQ_FMT_U4 or IQ_FMT_U2.
-// (4-bit records need more registers than three waves per SIMD leave: two waves per SIMD, and the
-// host sizes the plan for two work-groups per compute unit)
+// Waves per SIMD each format's kernel is built for (its register budget: 3 -> 168 VGPRs); the host
+// sizes the plan for as many resident work-groups per compute unit.  Measured at 48 layers: four
+// waves per SIMD (128 VGPRs) made U3 spill and run 167 us against 127 us, and U2 (no spills) 117
+// against 114 us; U4 runs at 155 us with three against 170 us with two.
 template <int kFmt>
-constexpr int split_waves_per_simd() { return kFmt == IQ_FMT_U4 ? 2 : kWavesPerSimd; }
+constexpr int split_waves_per_simd() { return kWavesPerSimd; }
 
 template <bool kAppend, int kFmt>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<kFmt>())))
@@ -1926,17 +1929,12 @@ int device_cu_count() {
 
 }  // namespace
 
-DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t cache_cap) {
-  DecodeGeometry geo{};
-  const int G = n_q_heads / n_kv_heads;
-  geo.head_groups = (G + 7) / 8;
-  // One round of work-groups: kGroupsPerCU are resident per compute unit, and each (KV head, head
-  // group) column of the grid gets `target` of them.  The kernels pick the chunk size from the
-  // lengths so that the batch's chunks number at most `target` per column (or one per sequence when
-  // the batch has more sequences than that): x_max = max(target, batch) work items per column.
-  const int64_t columns = (int64_t)n_kv_heads * geo.head_groups;
-  const int64_t slots = kGroupsPerCU * (int64_t)device_cu_count();
-  int64_t target = slots / columns;
+// Work items per (KV head, head group) column for one round of the split kernel at `groups_per_cu`
+// resident work-groups per compute unit.  The kernels pick the chunk size from the lengths so that
+// the batch's chunks number at most this many per column (or one per sequence when the batch has
+// more sequences than that).
+int64_t split_target(int batch, int64_t cache_cap, int64_t columns, int groups_per_cu) {
+  int64_t target = groups_per_cu * (int64_t)device_cu_count() / columns;
   // never more work items than the batch can have chunks (256 tokens at least)
   const int64_t most = (int64_t)batch * ((cache_cap + 255) / 256);
   if (target > most) target = most;
@@ -1947,18 +1945,44 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   if ((int64_t)batch * cache_cap < 512 * target && target > per_cu) target = per_cu;
   if (target < 1) target = 1;
   if (target > kMaxChunks) target = kMaxChunks;
+  return target;
+}
+
+// Chunks per sequence when every length is cap, by the kernels' first estimate of the chunk size
+// for this target (the kernels use it to start their set-up loads early; the combine to load the
+// rows of the guessed plan).
+int guess_chunks_per_seq(int batch, int64_t cache_cap, int64_t target) {
+  const int64_t units = (int64_t)batch * ((cache_cap + 127) / 128);
+  int64_t c = (units + target - 1) / target * 128;
+  const int64_t cmax = (cache_cap + 127) / 128 * 128 < 256 ? 256 : (cache_cap + 127) / 128 * 128;
+  if (c < 256) c = 256;
+  if (c > cmax) c = cmax;
+  return (int)((cache_cap + c - 1) / c);
+}
+
+// Resident split-kernel work-groups per compute unit (= waves per SIMD) of each record format.
+int split_groups_per_cu(int format) {
+  switch (format) {
+    case IQ_FMT_U2: return split_waves_per_simd<IQ_FMT_U2>();
+    case IQ_FMT_U4: return split_waves_per_simd<IQ_FMT_U4>();
+    case IQ_FMT_LM3: return split_waves_per_simd<IQ_FMT_LM3>();
+    case IQ_FMT_A3: return split_waves_per_simd<IQ_FMT_A3>();
+    default: return split_waves_per_simd<IQ_FMT_U3>();
+  }
+}
+
+DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t cache_cap) {
+  DecodeGeometry geo{};
+  const int G = n_q_heads / n_kv_heads;
+  geo.head_groups = (G + 7) / 8;
+  // One round of work-groups per (KV head, head group) column; x_max = max(target, batch) work
+  // items per column.
+  const int64_t columns = (int64_t)n_kv_heads * geo.head_groups;
+  // the partial rows are sized for the split kernel with the most work-groups per compute unit
+  const int64_t target = split_target(batch, cache_cap, columns, kMaxSplitGroupsPerCU);
   geo.target = (int)target;
   geo.x_max = (int)(target > batch ? target : batch);
-  // chunks per sequence when every length is cap, by the kernels' first estimate of the chunk size
-  // (the kernels use it only to start their set-up loads early)
-  {
-    const int64_t units = (int64_t)batch * ((cache_cap + 127) / 128);
-    int64_t c = (units + target - 1) / target * 128;
-    const int64_t cmax = (cache_cap + 127) / 128 * 128 < 256 ? 256 : (cache_cap + 127) / 128 * 128;
-    if (c < 256) c = 256;
-    if (c > cmax) c = cmax;
-    geo.guess_per_seq = (int)((cache_cap + c - 1) / c);
-  }
+  geo.guess_per_seq = guess_chunks_per_seq(batch, cache_cap, target);
   geo.plan_bytes = 256 + ((int64_t)batch * 4 + 255) / 256 * 256;
   // partial rows per query head: x_max, or, when batch counts the query tokens of
   // iq_decode_attention_multi (B sequences of Q >= 2 tokens), kMultiQ rows for each work item of the
@@ -2002,12 +2026,14 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.head_groups = geo.head_groups;
   k.cap = a.cache_cap;
   // the plan fills one round of work-groups: 4-bit records run two per compute unit, not three
-  const bool two = a.format == IQ_FMT_U4;
-  k.target = two ? (geo.target * 2 / kGroupsPerCU > 0 ? geo.target * 2 / kGroupsPerCU : 1) : geo.target;
+  // the plan fills one round of work-groups at the format's residency
+  const int64_t columns_s = (int64_t)a.n_kv_heads * geo.head_groups;
+  const int64_t target_f = split_target(vb, a.cache_cap, columns_s, split_groups_per_cu(a.format));
+  k.target = (int)target_f;
   k.sm_log2 = sm * kLog2e;
   k.plan = plan;
   k.x_max = geo.x_max;
-  k.guess_per_seq = geo.guess_per_seq;
+  k.guess_per_seq = guess_chunks_per_seq(vb, a.cache_cap, target_f);
   k.part_o = part_o;
   k.part_ml = part_ml;
   k.positions = a.positions;
@@ -2016,7 +2042,8 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   k.new_bf16 = a.new_bf16;
   k.new_stride_seq = a.new_stride_seq;
   k.new_stride_head = a.new_stride_head;
-  const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)geo.x_max, 1u);
+  // (x_max, the partial rows' stride, covers every format's work items)
+  const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)(target_f > vb ? target_f : vb), 1u);
   // several query tokens (3-bit records): groups of kMultiQ tokens share each block's unpacked
   // codes; partial rows x kMultiQ + i.  The plan aims at three rounds of work-groups: with one
   // chunk per (sequence, token group) a single round left compute units idle.
@@ -2071,7 +2098,7 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.n_groups = multi ? (a.q_tokens + kMultiQ - 1) / kMultiQ : a.q_tokens;
   c.cap = a.cache_cap;
   c.x_max = multi ? xg * kMultiQ : geo.x_max;
-  c.guess_per_seq = geo.guess_per_seq;
+  c.guess_per_seq = k.guess_per_seq;
   c.out = a.out;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(vb * a.n_q_heads)), dim3(128), 0, stream, c);
   return hipGetLastError();

@@ -133,13 +133,14 @@ def test_append_f32_inputs_and_shared_rotation():
 def test_append_inside_and_after_the_first_blocks_of_a_chunk():
     # Each wave loads its chunk's first two 32-token blocks before the query set-up; the
     # work-group whose first 256 tokens hold the new token loads them only after the append.
-    # With these lengths the kernels pick 640-token chunks (on 256 compute units): position
-    # 3850 is token 10 of chunk 6 (loaded after the append), 5520 is token 400 of chunk 8 (past
-    # the early blocks), 300 is in the first chunk, 8191 is the last slot.
+    # With these lengths the kernels pick 512-token chunks (640 at three work-groups per compute
+    # unit, on 256 compute units): position 2600 is token 40 of its chunk (loaded after the
+    # append), 5520 is token 400 of its chunk (past the early blocks), 300 is in the first chunk,
+    # 8191 is the last slot.
     rng = np.random.default_rng(45)
     cap = 8192
     s = _setup(rng, 8, 8, 8, cap)
-    positions = [3850, 5520, 300, 8000, 8000, 8000, 8000, cap - 1]
+    positions = [2600, 5520, 300, 8000, 8000, 8000, 8000, cap - 1]
     ws = torch.zeros(iq.decode_workspace_bytes(8, 8, 8, cap), dtype=torch.uint8, device="cuda")
     _check(s, positions, cap, "append in and past the early blocks", workspace=ws)
     chunk = int(ws[:4].view(torch.int32)[0])          # the plan at the start of the workspace
