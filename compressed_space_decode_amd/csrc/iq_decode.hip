@@ -5,7 +5,7 @@
 // the packed 3-bit tensors without materialising full-precision KV.
 // Because R is orthogonal, q.k_hat = (Rq).(s (c - 3.5)): the query is rotated
 // once, V levels are summed in rotated space, and R^T is applied once per
-// output row.
+// (output row, chunk) partial, never per token.
 //
 // Record layout: one little-endian bit stream, code i at bits 3i..3i+2, so
 // bytes 3g..3g+2 hold the codes of coordinates 8g..8g+7 (group g).
@@ -15,10 +15,10 @@
 // size is chosen on the device from the sequence lengths so that one round of
 // work-groups covers the whole batch, ragged or not (plan_chunks).  Each wave
 // works on its own, with no work-group barrier until the final merge:
-//   * set-up (wave 0, shared through LDS): the group's queries are rotated in
-//     registers (8 lanes per head, 16 coordinates per lane: cross-lane
-//     Hadamard stages through DPP / swizzle, in-lane stages, then the 4x4
-//     SO(4) blocks) and laid out as the fp16 A operand of the QK product, hi
+//   * set-up (all four waves, shared through LDS): one thread per (query head,
+//     SO(4) block) rotates 4 coordinates (H_4 in the thread, five cross-lane
+//     Hadamard stages through DPP / swizzle, then its 4x4 block); wave w then
+//     lays out K slots 8w .. 8w+7 of the fp16 A operand of the QK product, hi
 //     and lo parts (q = hi + lo) in rows 2h and 2h+1, so the product carries
 //     ~22 bits;
 //   * with the fused append, wave 1 of the work-group whose chunk holds the
@@ -41,7 +41,10 @@
 //     lanes (two DPP exchange rounds) leaves lane (n, g4) with group n of its 8
 //     tokens: exactly the B operand column n of O[head, part][coordinate 8n + j]
 //     += P'' x V for the 8 tiles j.  V never passes through LDS;
-//   * the 4 waves merge in LDS and write one (max, sum, o') partial.
+//   * the 4 waves merge in LDS; each thread takes 4 coordinates of the merged
+//     o' back through its transposed SO(4) block and the Hadamard (R^T is
+//     linear, so the chunk partials can be rotated before they are merged)
+//     and the work-group writes one (max, sum, R^T o') partial.
 // The same kernel reads the record variants (template parameter kFmt): 4-bit and 2-bit uniform
 // codes (fields at bits <= 6 and <= 8 of a half are exact fp16 subnormals too; other unpack
 // masks, byte windows and slot maps), the asymmetric 3-bit format (the same records, an (s, m)
@@ -54,8 +57,7 @@
 // unpacked once and multiplied by both tokens' operands, each token with its
 // own causal length and online softmax.
 // Kernel 2 (combine_kernel): one work-group per (sequence, query head):
-// log-sum-exp merge of the chunk partials, then o = R^T o' (transposed SO(4)
-// blocks followed by the Hadamard transform).
+// log-sum-exp merge of the chunk partials, already in output coordinates.
 #include "iq.h"
 #include "iq_internal.h"
 #include "iq_vector.h"
@@ -466,6 +468,7 @@ union DecodeSmemU {
 // every block, which keeps 16 registers per lane free for a second block in flight.
 struct DecodeSmem {
   uint4v qop[4][64];
+  float blk[32][16];      // the KV head's SO(4) blocks, for the inverse rotation of the partials
   DecodeSmemU u;
 };
 
@@ -912,6 +915,27 @@ __device__ __forceinline__ void hadamard_stage(float (&x)[4], int kq) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) x[r] = fmaf(sg, x[r], xor32<kM>(x[r]));
 }
+// o = R^T o' = H (blockdiag M_b^T) o' / sqrt(128) for the 32 threads of a half-wave, thread kq holding
+// coordinates 4 kq .. 4 kq + 3 of one row and M = its SO(4) block (row-major): the transposed block,
+// then H_128 = H_32 (x) H_4 as in the query set-up (H_4 inside the thread, five cross-lane stages).
+// Every lane of the wave must take part (cross-lane moves).
+__device__ __forceinline__ void unrotate4(float (&x)[4], const float* M, int kq) {
+  float z[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) z[c] = M[c] * x[0] + M[4 + c] * x[1] + M[8 + c] * x[2] + M[12 + c] * x[3];
+  const float a0 = z[0] + z[1], a1 = z[0] - z[1], a2 = z[2] + z[3], a3 = z[2] - z[3];
+  x[0] = a0 + a2;
+  x[1] = a1 + a3;
+  x[2] = a0 - a2;
+  x[3] = a1 - a3;
+  hadamard_stage<1>(x, kq);
+  hadamard_stage<2>(x, kq);
+  hadamard_stage<4>(x, kq);
+  hadamard_stage<8>(x, kq);
+  hadamard_stage<16>(x, kq);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) x[r] *= kInvSqrtD;
+}
 
 // kFmt: IQ_FMT_U3 (the pages' records; the only one with the fused append), IQ_FMT_A3 (the same
 // records, an (s, m) pair per token), IQ_FMT_U4 or IQ_FMT_U2.
@@ -1032,6 +1056,11 @@ void decode_split_kernel(DecodeKArgs a) {
     hadamard_stage<16>(xq, kq);
     float Mb[16];
     build_block(sl.r, Mb);
+    if (hr == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<float4*>(&sm.blk[kq][4 * i]) = make_float4(Mb[4 * i], Mb[4 * i + 1], Mb[4 * i + 2], Mb[4 * i + 3]);
+    }
     float y[4], qamax = 0.f, qs = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -1189,25 +1218,34 @@ void decode_split_kernel(DecodeKArgs a) {
     }
   }
   __syncthreads();
-  // ---------------- merge the 4 waves, write the chunk partial ----------------
-  for (int idx = tid; idx < nh * 128; idx += kThreads) {
-    const int hrow = idx >> 7, d = idx & 127;
+  // ---------------- merge the 4 waves, rotate back, write the chunk partial ----------------
+  // Thread (head row hr, block kq): coordinates 4 kq .. 4 kq + 3.  R^T is linear, so the partial
+  // rows carry R^T o' and the combine's weighted sum needs no rotation.
+  {
+    const int hr = tid >> 5, kq = tid & 31;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hrow]);
-    float L = 0.f, acc = 0.f;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hr]);
+    float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm.u.merge.m[w][hrow];
+      const float mw = sm.u.merge.m[w][hr];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * sm.u.merge.l[w][hrow];
-      acc += f * sm.u.merge.o[w][hrow][d];
+      L += f * sm.u.merge.l[w][hr];
+      const float4 v = *reinterpret_cast<const float4*>(&sm.u.merge.o[w][hr][4 * kq]);
+      o[0] += f * v.x;
+      o[1] += f * v.y;
+      o[2] += f * v.z;
+      o[3] += f * v.w;
     }
-    const int64_t pidx = (int64_t)(h0 + hrow) * a.x_max + x;
-    a.part_o[pidx * 128 + d] = acc;
-    if (d == 0) {
-      a.part_ml[pidx * 2] = M;
-      a.part_ml[pidx * 2 + 1] = L;
+    unrotate4(o, sm.blk[kq], kq);
+    if (hr < nh) {
+      const int64_t pidx = (int64_t)(h0 + hr) * a.x_max + x;
+      *reinterpret_cast<float4*>(a.part_o + pidx * 128 + 4 * kq) = make_float4(o[0], o[1], o[2], o[3]);
+      if (kq == 0) {
+        a.part_ml[pidx * 2] = M;
+        a.part_ml[pidx * 2 + 1] = L;
+      }
     }
   }
 }
@@ -1232,7 +1270,6 @@ struct MultiLoopSmem {
 };
 struct MultiSetupSmem {
   float qrot[kWaves][8][128];
-  float blk[32][16];
   float qsum[kWaves][8];
   int E[kWaves];
 };
@@ -1243,6 +1280,7 @@ union MultiSmemU {
 };
 struct MultiSmem {
   uint4v qop[kMultiQ][4][64];                 // QK A operand of each token
+  float blk[32][16];                          // the KV head's SO(4) blocks (set-up and the partials)
   MultiSmemU u;
 };
 
@@ -1463,7 +1501,7 @@ void decode_multi_kernel(DecodeKArgs a) {
 
   // ---------------- set-up: wave w rotates query token t_first + w ----------------
   MultiSetupSmem& ss = sm.u.setup;
-  if (lane < 8) build_block(rot + (8 * wave + lane) * 8, ss.blk[8 * wave + lane]);
+  if (lane < 8) build_block(rot + (8 * wave + lane) * 8, sm.blk[8 * wave + lane]);
   __syncthreads();
   if (wave < nq) {                                           // uniform
     const int qi = lane >> 3, qe = lane & 7;                 // head row, 16-coordinate slice
@@ -1513,7 +1551,7 @@ void decode_multi_kernel(DecodeKArgs a) {
     float qamax = 0.f, qs = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float* M = ss.blk[4 * qe + j];
+      const float* M = sm.blk[4 * qe + j];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float y = (M[4 * r] * xq[4 * j] + M[4 * r + 1] * xq[4 * j + 1] + M[4 * r + 2] * xq[4 * j + 2] +
@@ -1627,23 +1665,30 @@ void decode_multi_kernel(DecodeKArgs a) {
             back * fmaf(st.O[i][j8][2 * j] + st.O[i][j8][2 * j + 1], up, -3.5f * ls_tot[j]);
     }
     __syncthreads();
-    for (int idx = tid; idx < nh * 128; idx += kThreads) {
-      const int hrow = idx >> 7, d = idx & 127;
+    {                                  // as in the single-token kernel: merge, rotate back, write
+      const int hr = tid >> 5, kq = tid & 31;
       float M = kNoMax;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hrow]);
-      float L = 0.f, acc = 0.f;
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hr]);
+      float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float f = __builtin_amdgcn_exp2f(sm.u.merge.m[w][hrow] - M);
-        L += f * sm.u.merge.l[w][hrow];
-        acc += f * sm.u.merge.o[w][hrow][d];
+        const float f = __builtin_amdgcn_exp2f(sm.u.merge.m[w][hr] - M);
+        L += f * sm.u.merge.l[w][hr];
+        const float4 v = *reinterpret_cast<const float4*>(&sm.u.merge.o[w][hr][4 * kq]);
+        o[0] += f * v.x;
+        o[1] += f * v.y;
+        o[2] += f * v.z;
+        o[3] += f * v.w;
       }
-      const int64_t pidx = (int64_t)(h0 + hrow) * a.x_max + (int64_t)x * kQ + i;
-      a.part_o[pidx * 128 + d] = acc;
-      if (d == 0) {
-        a.part_ml[pidx * 2] = M;
-        a.part_ml[pidx * 2 + 1] = L;
+      unrotate4(o, sm.blk[kq], kq);
+      if (hr < nh) {
+        const int64_t pidx = (int64_t)(h0 + hr) * a.x_max + (int64_t)x * kQ + i;
+        *reinterpret_cast<float4*>(a.part_o + pidx * 128 + 4 * kq) = make_float4(o[0], o[1], o[2], o[3]);
+        if (kq == 0) {
+          a.part_ml[pidx * 2] = M;
+          a.part_ml[pidx * 2 + 1] = L;
+        }
       }
     }
     __syncthreads();
@@ -1654,8 +1699,6 @@ struct CombineArgs {
   const float* part_o;
   const float* part_ml;
   const int* plan;              // written by the split kernel: chunk size, first chunk per sequence
-  const float* rot;
-  int64_t rot_stride_b;
   const int32_t* seq_lens;
   const int32_t* positions;     // fused append: lengths are positions + 1 (seq_lens unused)
   int Hq, G;
@@ -1668,65 +1711,19 @@ struct CombineArgs {
   float* out;
 };
 
-// o = R^T o' = H (blockdiag M_b^T) o' of one merged row y[128] by one wave (8 lanes, 16 coordinates
-// each; lanes 8..63 repeat lanes 0..7), written to outp[128].
-__device__ __forceinline__ void combine_rotate_store(const float* y, const float (*mats)[16], float* outp, int lane) {
-  const int qe = lane & 7;
-  const float* yr = y + 16 * qe;
-  float x[16];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {       // transposed SO(4) blocks 4qe .. 4qe+3
-    const float* M4 = mats[4 * qe + j];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      x[4 * j + i] = M4[i] * yr[4 * j] + M4[4 + i] * yr[4 * j + 1] + M4[8 + i] * yr[4 * j + 2] +
-                     M4[12 + i] * yr[4 * j + 3];
-  }
-  const float sg1 = (qe & 1) ? -1.f : 1.f, sg2 = (qe & 2) ? -1.f : 1.f, sg4 = (qe & 4) ? -1.f : 1.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg1, x[i], dpp_xor1(x[i]));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg2, x[i], dpp_xor2(x[i]));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = fmaf(sg4, x[i], swz_xor4(x[i]));
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if ((i & m) == 0) {
-        const float u = x[i], v = x[i + m];
-        x[i] = u + v;
-        x[i + m] = u - v;
-      }
-  if (lane < 8) {
-    float4* op = reinterpret_cast<float4*>(outp + 16 * qe);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      op[i] = make_float4(x[4 * i] * kInvSqrtD, x[4 * i + 1] * kInvSqrtD, x[4 * i + 2] * kInvSqrtD,
-                          x[4 * i + 3] * kInvSqrtD);
-  }
-}
-
 // One sequence with one query token: its chunks are partial rows 0 .. nvalid - 1 of every query head
-// (x_max <= kMidChunks of them), so every load (the rows, their (max, sum) pairs, the rotation) is
-// issued at once, unconditionally, before the length and the chunk size arrive: rows past x_max
-// repeat the last row, and rows past nvalid are loaded but not used.  Each wave reduces the (max,
-// sum) pairs itself: no weights through LDS.  An empty sequence gets zeros.
-__device__ __forceinline__ void combine_one_sequence(const CombineArgs& a, int h, float* outp, float* y,
-                                                     float (*mats)[16], int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
+// (x_max <= kMidChunks of them), so every load (the rows and their (max, sum) pairs) is issued at
+// once, unconditionally, before the length and the chunk size arrive: rows past x_max repeat the
+// last row, and rows past nvalid are loaded but not used.  Each wave reduces the (max, sum) pairs
+// itself: no weights through LDS.  An empty sequence gets zeros.
+__device__ __forceinline__ void combine_one_sequence(const CombineArgs& a, int h, float* outp, int tid) {
+  const int lane = tid & 63;
   const int nr = a.x_max;
   const float* po = a.part_o + (int64_t)h * nr * 128 + tid;
   float om[kMidChunks];
 #pragma unroll
   for (int c = 0; c < kMidChunks; ++c) om[c] = po[(int64_t)min(c, nr - 1) * 128];
   const float2 mlv = reinterpret_cast<const float2*>(a.part_ml)[(int64_t)h * nr + min(lane, nr - 1)];
-  float rp[8];
-  {
-    const float* rq = a.rot + (int64_t)(h / a.G) * 256 + (lane & 31) * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) rp[i] = rq[i];
-  }
   const int chunk = a.plan[0];
   const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, 1, 1, 1, 1}, 0);
   const int nvalid = len > 0 ? min((len + chunk - 1) / chunk, nr) : 0;
@@ -1745,24 +1742,19 @@ __device__ __forceinline__ void combine_one_sequence(const CombineArgs& a, int h
     acc[c & 7] = fmaf(w, c < nvalid ? om[c] : 0.f, acc[c & 7]);
   }
   const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-  y[tid] = nvalid > 0 ? sum / L : 0.f;
-  if (wave == 1 && lane < 32) build_block(rp, mats[lane]);
-  __syncthreads();
-  if (wave == 0) combine_rotate_store(y, mats, outp, lane);
+  outp[tid] = nvalid > 0 ? sum / L : 0.f;
 }
 
 // One work-group (2 waves) per (sequence, query head): log-sum-exp merge of the chunk partials with
-// one output coordinate per thread and independent loads, then o = R^T o' = H (blockdiag M_b^T) o'
-// by one wave (8 lanes, 16 coordinates each, as in the query set-up of the split kernel).
+// one output coordinate per thread and independent loads.  The partial rows are already rotated
+// back (R^T o', by the kernels that write them), so the merged row is the output.
 __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
-  __shared__ float y[128];
-  __shared__ float mats[32][16];
   __shared__ float wgt[kMaxChunks];
   __shared__ float inv_l;
   const int b = blockIdx.x / a.Hq, h = blockIdx.x % a.Hq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (a.q_tokens == 1 && (int)gridDim.x == a.Hq && a.x_max <= kMidChunks) {   // uniform
-    combine_one_sequence(a, h, a.out + (int64_t)h * 128, y, mats, tid);
+    combine_one_sequence(a, h, a.out + (int64_t)h * 128, tid);
     return;
   }
   // Several sequences of one query token, at most kFewChunks chunks each when every length is cap:
@@ -1780,12 +1772,6 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
       mv[c] = v.x;
       lv[c] = v.y;
       ov[c] = a.part_o[row * 128 + tid];
-    }
-    float rp[8];
-    {
-      const float* rq = a.rot + b * a.rot_stride_b + (int64_t)(h / a.G) * 256 + (lane & 31) * 8;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rp[i] = rq[i];
     }
     const int chunk = a.plan[0];
     const int x0 = a.plan[64 + b];
@@ -1808,10 +1794,7 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
           L = fmaf(w, lv[c], L);
           acc = fmaf(w, ov[c], acc);
         }
-      y[tid] = acc / L;
-      if (wave == 1 && lane < 32) build_block(rp, mats[lane]);
-      __syncthreads();
-      if (wave == 0) combine_rotate_store(y, mats, outp, lane);
+      outp[tid] = acc / L;
       return;
     }
   }
@@ -1856,8 +1839,6 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
       lv[c] = ml[2 * cc + 1];
       ov[c] = po[(int64_t)cc * 128];
     }
-    if (wave == 1 && lane < 32)         // the SO(4) blocks of this head's KV head
-      build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
     float M = -INFINITY;
 #pragma unroll
     for (int c = 0; c < kFewChunks; ++c) M = c < nvalid ? fmaxf(M, mv[c]) : M;
@@ -1868,8 +1849,10 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
       L = fmaf(w, lv[c], L);
       acc = fmaf(w, ov[c], acc);
     }
-    y[tid] = acc / L;
-  } else if (wave == 0) {               // weights 2^(m_c - M) and 1/L
+    outp[tid] = acc / L;
+    return;
+  }
+  if (wave == 0) {                      // weights 2^(m_c - M) and 1/L
     float M = -INFINITY;
     for (int c = lane; c < nvalid; c += 64) M = fmaxf(M, ml[2 * c * rs]);
 #pragma unroll
@@ -1883,8 +1866,6 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) L += wave_xor(L, m);
     if (lane == 0) inv_l = 1.f / L;
-  } else if (lane < 32) {               // the SO(4) blocks of this head's KV head
-    build_block(a.rot + bc * a.rot_stride_b + (int64_t)(h / a.G) * 256 + lane * 8, mats[lane]);
   }
   if (preload) {
     __syncthreads();
@@ -1892,8 +1873,8 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
 #pragma unroll
     for (int c = 0; c < kMidChunks; ++c)
       if (c < nvalid) acc[c & 7] = fmaf(wgt[c], om[c], acc[c & 7]);
-    y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
-  } else if (nvalid > kFewChunks) {
+    outp[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
+  } else {                              // nvalid > kFewChunks
     __syncthreads();
     const float* po = a.part_o + first * 128 + tid;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -1903,10 +1884,8 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
       for (int u = 0; u < 8; ++u) acc[u] = fmaf(wgt[c + u], po[(int64_t)(c + u) * rs * 128], acc[u]);
     }
     for (; c < nvalid; ++c) acc[0] = fmaf(wgt[c], po[(int64_t)c * rs * 128], acc[0]);
-    y[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
+    outp[tid] = (((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]))) * inv_l;
   }
-  __syncthreads();
-  if (wave == 0) combine_rotate_store(y, mats, outp, lane);
 }
 
 }  // namespace
@@ -2087,8 +2066,6 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   c.part_o = part_o;
   c.part_ml = part_ml;
   c.plan = plan;
-  c.rot = a.rot;
-  c.rot_stride_b = a.rot_stride_batch;
   c.seq_lens = a.seq_lens;
   c.positions = a.positions;
   c.Hq = a.n_q_heads;

@@ -187,7 +187,7 @@ int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
  * query is rotated into the compressed space, codes are turned into
  * numbers only in registers, softmax is online and split over the
  * sequence, V is accumulated in rotated space and rotated back once per
- * output row.
+ * (output row, chunk) partial, never per token.
  *   q            [batch][n_q_heads][128], q_dtype IQ_F32 or IQ_BF16,
  *                16-byte aligned.
  *   k_*, v_*     the cache written by iq_quantize_kv, [batch][n_kv_heads]
