@@ -439,11 +439,13 @@ __device__ ChunkPlan plan_chunks(const LenSource& s, int l0, int target, int x, 
   return p;
 }
 
-struct MergeSmem {
-  float o[kWaves][8][128];
-  float m[kWaves][8];
-  float l[kWaves][8];
+template <int kW>
+struct MergeSmemT {
+  float o[kW][8][128];
+  float m[kW][8];
+  float l[kW][8];
 };
+using MergeSmem = MergeSmemT<kWaves>;
 // Per-wave loop staging: the P'' block [32 tokens][16 (head, part)] fp16 (32-byte rows) and the
 // block's K/V scales.
 constexpr int kPRow = 32;
@@ -459,17 +461,19 @@ struct SetupSmem {
   float qsum[8];
   int E[8];
 };
+template <int kW>
 union DecodeSmemU {
-  MergeSmem merge;
-  WaveLoopSmem loop[kWaves];
+  MergeSmemT<kW> merge;
+  WaveLoopSmem loop[kW];
   SetupSmem setup;
 };
-// The QK A operand in lane order (the same for the 4 waves), built once and read from LDS for
+// The QK A operand in lane order (the same for every wave), built once and read from LDS for
 // every block, which keeps 16 registers per lane free for a second block in flight.
+template <int kW>
 struct DecodeSmem {
   uint4v qop[4][64];
   float blk[32][16];      // the KV head's SO(4) blocks, for the inverse rotation of the partials
-  DecodeSmemU u;
+  DecodeSmemU<kW> u;
 };
 
 __device__ __forceinline__ void build_block(const float* p, float* out16) {
@@ -946,12 +950,18 @@ __device__ __forceinline__ void unrotate4(float (&x)[4], const float* M, int kq)
 template <int kFmt>
 constexpr int split_waves_per_simd() { return kWavesPerSimd; }
 
-template <bool kAppend, int kFmt>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<kFmt>())))
+// kW: waves per work-group.  4 (the grid fills three work-groups per compute unit), or 8 for a grid
+// of at most one work-group per compute unit (a single short sequence): the chunk's blocks are
+// spread over twice the waves, two per SIMD, so each wave's chain of dependent blocks is half as
+// long.  Waves 0-3 do the set-up and the final rotation in either case.
+template <bool kAppend, int kFmt, int kW>
+__global__ __launch_bounds__(64 * kW)
+__attribute__((amdgpu_waves_per_eu(kW == kWaves ? split_waves_per_simd<kFmt>() : 2)))
 void decode_split_kernel(DecodeKArgs a) {
+  static_assert(kW == kWaves || kW == 2 * kWaves, "four or eight waves");
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
   constexpr int kRec = Fmt<kFmt>::kRec;
-  __shared__ DecodeSmem sm;
+  __shared__ DecodeSmem<kW> sm;
   // blockIdx.x: (KV head, head group) column, so consecutive work-groups take the columns of one
   // work item (measured slightly faster than the transposed order)
   const int x = blockIdx.y;          // (sequence, chunk) pair
@@ -1012,10 +1022,10 @@ void decode_split_kernel(DecodeKArgs a) {
   const bool vscale = g4 >= 2;
   lo.vside = vscale;
 
-  const int step = kWaves * kBlock;
+  const int step = kW * kBlock;
   int t0 = tok0 + wave * kBlock;
-  // The first two blocks of every wave are loaded now, so that they stream while wave 0 rotates
-  // the queries.  In the work-group that appends a token to one of those blocks these loads read
+  // The first two blocks of every wave are loaded now, so that they stream while the queries are
+  // rotated.  In the work-group that appends a token to one of those blocks these loads read
   // zeros without a memory access (an end of 0), and the blocks are loaded after the append.
   const bool reload = kAppend && pos >= tok0 && pos < tok0 + 2 * step;   // uniform
   BlockData<Fmt<kFmt>::kQW> buf, buf2, buf3;
@@ -1027,7 +1037,7 @@ void decode_split_kernel(DecodeKArgs a) {
   // (I_32 x H_4)(H_32 x I_4): H_4 inside the thread, then five butterfly stages across the 32
   // lanes of the head, then SO(4) block kq and the 1/sqrt(128).
   SetupSmem& ss = sm.u.setup;
-  {
+  if (wave < kWaves) {               // uniform: threads 0..255, one per (head, block)
     const int hr = tid >> 5, kq = tid & 31;
     float xq[4];
     if (a.q_bf16) {
@@ -1124,7 +1134,7 @@ void decode_split_kernel(DecodeKArgs a) {
   __syncthreads();
   // A operand of the QK product, built by wave w for K slots 8w .. 8w + 7 of every lane: lane row
   // n = (head n/2, part n%2), K slots of quarter g4.
-  {
+  if (wave < kWaves) {               // uniform
     const int kb = wave, head = n >> 1, part = n & 1;
     const int Eh = ss.E[head];
     _Float16 hv[8];
@@ -1221,14 +1231,14 @@ void decode_split_kernel(DecodeKArgs a) {
   // ---------------- merge the 4 waves, rotate back, write the chunk partial ----------------
   // Thread (head row hr, block kq): coordinates 4 kq .. 4 kq + 3.  R^T is linear, so the partial
   // rows carry R^T o' and the combine's weighted sum needs no rotation.
-  {
+  if (wave < kWaves) {               // uniform: threads 0..255
     const int hr = tid >> 5, kq = tid & 31;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.u.merge.m[w][hr]);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.u.merge.m[w][hr]);
     float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float mw = sm.u.merge.m[w][hr];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L += f * sm.u.merge.l[w][hr];
@@ -2048,17 +2058,26 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
     hipLaunchKernelGGL((decode_multi_kernel<kMultiQ>), dim3((unsigned)columns, (unsigned)xg, 1u), dim3(kThreads), 0,
                        stream, k);
   } else if (a.format == IQ_FMT_U2)
-    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U2>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U2, kWaves>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_U4)
-    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U4>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U4, kWaves>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_LM3)
-    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_LM3>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_LM3, kWaves>), grid1, dim3(kThreads), 0, stream, k);
   else if (a.format == IQ_FMT_A3)
-    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_A3>), grid1, dim3(kThreads), 0, stream, k);
-  else if (a.positions)
-    hipLaunchKernelGGL((decode_split_kernel<true, IQ_FMT_U3>), grid1, dim3(kThreads), 0, stream, k);
-  else
-    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U3>), grid1, dim3(kThreads), 0, stream, k);
+    hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_A3, kWaves>), grid1, dim3(kThreads), 0, stream, k);
+  else {
+    // 3-bit records: eight waves per work-group when the grid is at most one work-group per
+    // compute unit (the set-up and the block chain of one short sequence are the critical path)
+    const bool wide = (int64_t)grid1.x * grid1.y <= device_cu_count();
+    if (a.positions && wide)
+      hipLaunchKernelGGL((decode_split_kernel<true, IQ_FMT_U3, 2 * kWaves>), grid1, dim3(2 * kThreads), 0, stream, k);
+    else if (a.positions)
+      hipLaunchKernelGGL((decode_split_kernel<true, IQ_FMT_U3, kWaves>), grid1, dim3(kThreads), 0, stream, k);
+    else if (wide)
+      hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U3, 2 * kWaves>), grid1, dim3(2 * kThreads), 0, stream, k);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<false, IQ_FMT_U3, kWaves>), grid1, dim3(kThreads), 0, stream, k);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
