@@ -1755,6 +1755,47 @@ __device__ __forceinline__ void combine_one_sequence(const CombineArgs& a, int h
   outp[tid] = nvalid > 0 ? sum / L : 0.f;
 }
 
+// Several sequences of one query token, at most kN chunks each when every length is cap: the rows
+// of sequence b under that guess (b gps .. b gps + gps - 1) and their (max, sum) pairs are loaded
+// together with the plan and the length, and used when the plan agrees (one round trip instead
+// of two).  Returns false (nothing written) when the plan differs.
+template <int kN>
+__device__ __forceinline__ bool combine_guessed(const CombineArgs& a, int b, int h, float* outp, int tid) {
+  const int gps = a.guess_per_seq, x0g = b * gps;
+  const int64_t hrow = (int64_t)h * a.x_max;
+  float mv[kN], lv[kN], ov[kN];
+#pragma unroll
+  for (int c = 0; c < kN; ++c) {
+    const int64_t row = hrow + min(x0g + min(c, gps - 1), a.x_max - 1);   // in range; unused past nvalid
+    const float2 v = reinterpret_cast<const float2*>(a.part_ml)[row];
+    mv[c] = v.x;
+    lv[c] = v.y;
+    ov[c] = a.part_o[row * 128 + tid];
+  }
+  const int chunk = a.plan[0];
+  const int x0 = a.plan[64 + b];
+  const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, 1, 1, 1}, b);
+  if (len == 0) {                       // an empty sequence attends to nothing
+    outp[tid] = 0.f;
+    return true;
+  }
+  const int nvalid = (len + chunk - 1) / chunk;
+  if (x0 != x0g || nvalid > gps) return false;   // uniform
+  float M = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kN; ++c) M = c < nvalid ? fmaxf(M, mv[c]) : M;
+  float L = 0.f, acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < kN; ++c)
+    if (c < nvalid) {                   // uniform; rows past it may hold anything
+      const float w = __builtin_amdgcn_exp2f(mv[c] - M);
+      L = fmaf(w, lv[c], L);
+      acc = fmaf(w, ov[c], acc);
+    }
+  outp[tid] = acc / L;
+  return true;
+}
+
 // One work-group (2 waves) per (sequence, query head): log-sum-exp merge of the chunk partials with
 // one output coordinate per thread and independent loads.  The partial rows are already rotated
 // back (R^T o', by the kernels that write them), so the merged row is the output.
@@ -1768,45 +1809,18 @@ __global__ __launch_bounds__(128) void combine_kernel(CombineArgs a) {
     return;
   }
   // Several sequences of one query token, at most kFewChunks chunks each when every length is cap:
-  // the rows of sequence b under that guess (b gps .. b gps + gps - 1) and their (max, sum) pairs
-  // are loaded together with the plan and the length, and used when the plan agrees (one round
-  // trip instead of two); otherwise the general path below loads the right rows.
+  // the guessed rows first (combine_guessed, as many loads as the guess has rows, rounded up to 4,
+  // 8 or 16); otherwise the general path below loads the right rows.
   if (a.q_tokens == 1 && a.guess_per_seq <= kFewChunks) {   // uniform
-    const int gps = a.guess_per_seq, x0g = b * gps;
-    const int64_t hrow = (int64_t)h * a.x_max;
-    float mv[kFewChunks], lv[kFewChunks], ov[kFewChunks];
-#pragma unroll
-    for (int c = 0; c < kFewChunks; ++c) {
-      const int64_t row = hrow + min(x0g + min(c, gps - 1), a.x_max - 1);   // in range; unused past nvalid
-      const float2 v = reinterpret_cast<const float2*>(a.part_ml)[row];
-      mv[c] = v.x;
-      lv[c] = v.y;
-      ov[c] = a.part_o[row * 128 + tid];
-    }
-    const int chunk = a.plan[0];
-    const int x0 = a.plan[64 + b];
-    const int len = len_at(LenSource{a.positions, a.seq_lens, (int)a.cap, (int)gridDim.x / a.Hq, 1, 1, 1}, b);
     float* outp = a.out + ((int64_t)b * a.Hq + h) * 128;
-    if (len == 0) {                     // an empty sequence attends to nothing
-      outp[tid] = 0.f;
-      return;
-    }
-    const int nvalid = (len + chunk - 1) / chunk;
-    if (x0 == x0g && nvalid <= gps) {   // uniform
-      float M = -INFINITY;
-#pragma unroll
-      for (int c = 0; c < kFewChunks; ++c) M = c < nvalid ? fmaxf(M, mv[c]) : M;
-      float L = 0.f, acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < kFewChunks; ++c)
-        if (c < nvalid) {               // uniform; rows past it may hold anything
-          const float w = __builtin_amdgcn_exp2f(mv[c] - M);
-          L = fmaf(w, lv[c], L);
-          acc = fmaf(w, ov[c], acc);
-        }
-      outp[tid] = acc / L;
-      return;
-    }
+    bool done;
+    if (a.guess_per_seq <= 4)
+      done = combine_guessed<4>(a, b, h, outp, tid);
+    else if (a.guess_per_seq <= 8)
+      done = combine_guessed<8>(a, b, h, outp, tid);
+    else
+      done = combine_guessed<kFewChunks>(a, b, h, outp, tid);
+    if (done) return;                   // uniform
   }
   // the plan is read together with the length (both entries exist for every sequence; they are
   // used only when the sequence has tokens, and then the split kernel wrote them)
