@@ -82,6 +82,9 @@ def parse():
                          "reference reading for the FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the timed steps (for counter runs); prints a short JSON line")
+    ap.add_argument("--multi-only", type=int, default=0, metavar="Q",
+                    help="only --warmup then --steps multi-token decode calls of Q query tokens on the "
+                         "48-layer cache (for counter runs); prints a short JSON line")
     return ap.parse_args()
 
 
@@ -334,6 +337,22 @@ def main():
     v_new = v_all[:, :, T - 1]                # [L][Hkv][128] views
     positions = torch.full((L,), T - 1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
+
+    if args.multi_only:                       # counter runs of the multi-token kernel
+        Qm = args.multi_only
+        qm = bf16(W.multi_token_queries(L, Qm, HQ))
+        outm = torch.empty((L, Qm, HQ, D), dtype=torch.float32, device=dev)
+        wsm = torch.empty(iq.decode_workspace_bytes(L * Qm, HQ, HKV, T), dtype=torch.uint8, device=dev)
+
+        def dec_m():
+            iq.decode_attention_multi(qm, kc, ks, vc, vs, rot, seq_lens=lens, out=outm, workspace=wsm)
+
+        for _ in range(args.warmup):
+            dec_m()
+        torch.cuda.synchronize()
+        t_m = median(time_each(dec_m, args.steps, stream))
+        print(json.dumps({"multi_query_tokens": Qm, "ms": t_m * 1e3}), flush=True)
+        return
 
     def step():                               # one launch: append the new token, then attend
         iq.decode_attention_append(q, k_new, v_new, positions, kc, ks, vc, vs, rot, out=out, workspace=ws)
