@@ -347,6 +347,7 @@ def main():
         def dec_m():
             iq.decode_attention_multi(qm, kc, ks, vc, vs, rot, seq_lens=lens, out=outm, workspace=wsm)
 
+        settle(dec_m, args.settle)
         for _ in range(args.warmup):
             dec_m()
         torch.cuda.synchronize()
@@ -476,7 +477,10 @@ def main():
             iq.quantize_kv(kt, vt, rott, kct, kst, vct, vst, fmt=fmt)
             err_t = rel_err(iq.decode_attention(qt, kct, kst, vct, vst, rott, fmt=fmt)[0], ref_t)
             del kct, vct, kst, vst
+            # each timing starts on steady clocks, like the headline's (the calls before were short)
+            settle(quant_f, 0.2)
             t_qf = median(time_each(quant_f, 7, stream))
+            settle(dec_f, 0.3)
             t_df = median(time_each(dec_f, 21, stream))
             cache_b = L * HKV * T * 2 * (rb + 4 * sw)
             formats[fmt] = {"bits": iq.FORMAT_BITS[fmt], "record_bytes": rb,
@@ -501,6 +505,7 @@ def main():
 
             for _ in range(20):
                 dec_m()
+            settle(dec_m, 0.3)
             t_m = median(time_each(dec_m, max(20, args.steps // 8), stream))
             flops = 2 * 2 * L * Qm * HQ * T * D       # QK and PV multiply-adds, causal tail ignored
             multi["q%d" % Qm] = {"query_tokens": Qm, "ms": t_m * 1e3, "kv_tokens_per_s": L * T / t_m,

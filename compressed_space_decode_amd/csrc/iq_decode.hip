@@ -100,21 +100,52 @@ __device__ __forceinline__ int slot_pow(int s) { return field_pos((s >> 1) & 7);
 
 // Unpack one 12-byte quarter (groups 0..3, little-endian words w0..w2) into 16 words of fp16
 // pairs: word 8P + j holds field j of group 2P (low half) and of group 2P + 1 (high half).
-__device__ __forceinline__ void unpack_quarter(unsigned w0, unsigned w1, unsigned w2, unsigned o[16]) {
+// Window j / 3 of group pair P holds field j of both groups at field_pos(j) of its 16-bit halves.
+__device__ __forceinline__ void quarter_windows(unsigned w0, unsigned w1, unsigned w2, unsigned (&win)[2][3]) {
   // __builtin_amdgcn_perm(hi, lo, sel): selector bytes 0-3 pick bytes of lo, 4-7 bytes of hi.
-  const unsigned win[2][3] = {
-      {__builtin_amdgcn_perm(w1, w0, 0x04030100u),    // bytes 0,1 | 3,4
-       __builtin_amdgcn_perm(w1, w0, 0x05040201u),    // bytes 1,2 | 4,5
-       __builtin_amdgcn_perm(w1, w0, 0x06050302u)},   // bytes 2,3 | 5,6
-      {__builtin_amdgcn_perm(w2, w1, 0x06050302u),    // bytes 6,7 | 9,10
-       __builtin_amdgcn_perm(w2, w1, 0x07060403u),    // bytes 7,8 | 10,11
-       __builtin_amdgcn_perm(w2, w1, 0x07070404u)}};  // byte 8 | byte 11 (upper bytes unused)
+  win[0][0] = __builtin_amdgcn_perm(w1, w0, 0x04030100u);    // bytes 0,1 | 3,4
+  win[0][1] = __builtin_amdgcn_perm(w1, w0, 0x05040201u);    // bytes 1,2 | 4,5
+  win[0][2] = __builtin_amdgcn_perm(w1, w0, 0x06050302u);    // bytes 2,3 | 5,6
+  win[1][0] = __builtin_amdgcn_perm(w2, w1, 0x06050302u);    // bytes 6,7 | 9,10
+  win[1][1] = __builtin_amdgcn_perm(w2, w1, 0x07060403u);    // bytes 7,8 | 10,11
+  win[1][2] = __builtin_amdgcn_perm(w2, w1, 0x07070404u);    // byte 8 | byte 11 (upper bytes unused)
+}
+__device__ __forceinline__ void unpack_quarter(unsigned w0, unsigned w1, unsigned w2, unsigned o[16]) {
+  unsigned win[2][3];
+  quarter_windows(w0, w1, w2, win);
 #pragma unroll
   for (int P = 0; P < 2; ++P)
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[8 * P + j] = win[P][j / 3] & field_mask(j);
 }
 
+// Max's 8-level Lloyd-Max quantizer for a unit Gaussian (J. Max, 1960), levels of codes 0..7.
+constexpr float kLmLevels[8] = {-2.152f, -1.344f, -0.7560f, -0.2451f, 0.2451f, 0.7560f, 1.344f, 2.152f};
+// Every function of a 3-bit code c that is odd about the middle of the code range, plus a constant,
+// is a combination of c, c & 6, c & 4 and the parity of c: the odd functions of the three bits
+// form a 4-dimensional space spanned by the bits and their parity.  Max's levels are symmetric
+// about 0 (level 7 - c = -level c), so
+//   level(c) = k0 c + k1 (c & 6) + k2 (c & 4) + k3 parity(c) - A0   for all eight codes,
+// with A0 = -level 0 and k0..k3 from codes 1, 2, 3 and 4.  Each plane is an exact subnormal operand
+// like a uniform code, so the products stay on the matrix cores.
+constexpr float kLmA0 = -kLmLevels[0];
+constexpr float kLmK0 = 0.5f * ((kLmLevels[1] - kLmLevels[0]) + (kLmLevels[3] - kLmLevels[2]));
+constexpr float kLmK3 = 0.5f * ((kLmLevels[1] - kLmLevels[0]) - (kLmLevels[3] - kLmLevels[2]));
+constexpr float kLmK1 = 0.5f * (kLmLevels[2] - kLmLevels[0] - 2.f * kLmK0 - kLmK3);
+constexpr float kLmK2 = 0.25f * (kLmLevels[4] - kLmLevels[0] - 4.f * kLmK0 - 4.f * kLmK1 - kLmK3);
+// the other planes' coefficients relative to the first
+constexpr float kLmR[4] = {1.f, kLmK1 / kLmK0, kLmK2 / kLmK0, kLmK3 / kLmK0};
+constexpr float lm_level_of(int c) {
+  return kLmK0 * c + kLmK1 * (c & 6) + kLmK2 * (c & 4) + kLmK3 * (((c >> 2) ^ (c >> 1) ^ c) & 1) - kLmA0;
+}
+constexpr bool lm_planes_exact() {
+  for (int c = 0; c < 8; ++c) {
+    const float d = lm_level_of(c) - kLmLevels[c];
+    if (d > 1e-6f || d < -1e-6f) return false;
+  }
+  return true;
+}
+static_assert(lm_planes_exact(), "the four planes reproduce every Lloyd-Max level");
 // Record geometry of the formats the matrix-core kernel reads: 3-bit (U3, and A3 with the same
 // records), 4-bit and 2-bit uniform.  A quarter is the 32 coordinates 32 g4 .. 32 g4 + 31 of a
 // record, kQW dwords; a group is 8 coordinates.
@@ -123,45 +154,28 @@ struct Fmt {
   static constexpr int kBits = kFmt == IQ_FMT_U4 ? 4 : kFmt == IQ_FMT_U2 ? 2 : 3;
   static constexpr int kRec = 16 * kBits;             // record bytes
   static constexpr int kQW = kBits;                   // dwords of a quarter (4 kBits bytes)
-  static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : kFmt == IQ_FMT_LM3 ? 0.f : 3.5f;
   static constexpr bool kAsym = kFmt == IQ_FMT_A3;
-  // Lloyd-Max levels are not uniform: the operands are the levels as fp16 (hi + lo parts, looked up
-  // from byte tables), not the codes as subnormals, so no 2^-24 and no centering term
+  // Lloyd-Max levels are not uniform: each code enters as four subnormal operands (the planes below),
+  // whose products are combined with the planes' coefficients
   static constexpr bool kTable = kFmt == IQ_FMT_LM3;
-  static constexpr int kSub = kTable ? 0 : 24;        // operand exponent offset undone in the scores
+  static constexpr int kPlanes = kTable ? 4 : 1;
+  static constexpr int kSub = 24;                     // operand exponent offset undone in the scores
+  // level(c) = kGain (code + planes) - kCenter: the centre of the uniform codes, A0 for Lloyd-Max
+  static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : kFmt == IQ_FMT_LM3 ? kLmA0 : 3.5f;
+  static constexpr float kGain = kFmt == IQ_FMT_LM3 ? kLmK0 : 1.f;
 };
 
-// fp16 hi and lo parts of Max's 8 Lloyd-Max levels (hi + lo equals the fp32 level to about 1e-7),
-// as byte tables for v_perm: hl / hh hold the low / high bytes of the hi parts of levels 0..7
-// (levels 0-3 in word 0, 4-7 in word 1), ll / lh those of the lo parts.
-struct LevelTable {
-  unsigned hl[2], hh[2], ll[2], lh[2];
-};
-__device__ __forceinline__ LevelTable lm3_table() {
-  const float L[8] = {-2.152f, -1.344f, -0.7560f, -0.2451f, 0.2451f, 0.7560f, 1.344f, 2.152f};
-  LevelTable t{};
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const _Float16 h = (_Float16)L[c];
-    const _Float16 l = (_Float16)(L[c] - (float)h);
-    const unsigned hb = __builtin_bit_cast(unsigned short, h), lb = __builtin_bit_cast(unsigned short, l);
-    const int w = c >> 2, sh = 8 * (c & 3);
-    t.hl[w] |= (hb & 0xFFu) << sh;
-    t.hh[w] |= (hb >> 8) << sh;
-    t.ll[w] |= (lb & 0xFFu) << sh;
-    t.lh[w] |= (lb >> 8) << sh;
-  }
-  return t;
-}
-// The fp16 hi and lo parts of the levels of two codes: code A at bits pos..pos+2 of the low half of
-// w, code B at the same bits of the high half (w already masked to those fields).
-__device__ __forceinline__ void level_pair(unsigned w, int pos, const LevelTable& t, unsigned& hi, unsigned& lo) {
-  const unsigned sa = (w >> pos) | 0x0C000C00u;            // bytes [A, zero, B, zero]
-  const unsigned sb = (sa << 8) | 0x0Cu;                   // bytes [zero, A, zero, B]
-  hi = __builtin_amdgcn_perm(t.hl[1], t.hl[0], sa) | __builtin_amdgcn_perm(t.hh[1], t.hh[0], sb);
-  lo = __builtin_amdgcn_perm(t.ll[1], t.ll[0], sa) | __builtin_amdgcn_perm(t.lh[1], t.lh[0], sb);
-}
 
+// The four planes of one window word w (two codes at bits pos..pos+2 of each 16-bit half) given its
+// parity fold f = w ^ (w >> 1) ^ (w >> 2): the codes, the codes & 6, the codes & 4 and their parities,
+// each at the codes' bit position (so one query operand serves all four).
+__device__ __forceinline__ void planes_of(unsigned w, unsigned f, int pos, unsigned (&o)[4]) {
+  o[0] = w & (0x00070007u << pos);
+  o[1] = w & (0x00060006u << pos);
+  o[2] = w & (0x00040004u << pos);
+  o[3] = f & (0x00010001u << pos);
+}
+__device__ __forceinline__ unsigned parity_fold(unsigned w) { return w ^ (w >> 1) ^ (w >> 2); }
 // K slot s (0..31) of a quarter: the coordinate it holds and the bit position of its field.
 //  3-bit: as slot_coord / slot_pow.
 //  4-bit: word w = s/2 holds (dword w/4 = group w/4) & 0x000F000F or & 0x00F000F0, unshifted (w%4 <
@@ -178,8 +192,7 @@ __device__ __forceinline__ int slot_coord_f(int s) {
 template <int kFmt>
 __device__ __forceinline__ int slot_pow_f(int s) {
   const int t = (s >> 1) & 7;
-  if constexpr (Fmt<kFmt>::kTable) return 0;
-  else if constexpr (Fmt<kFmt>::kBits == 3) return slot_pow(s);
+  if constexpr (Fmt<kFmt>::kBits == 3) return slot_pow(s);
   else if constexpr (Fmt<kFmt>::kBits == 4) return 4 * (t & 1);
   else return t <= 4 ? 2 * t : 2 * (t - 4);
 }
@@ -449,8 +462,9 @@ using MergeSmem = MergeSmemT<kWaves>;
 // Per-wave loop staging: the P'' block [32 tokens][16 (head, part)] fp16 (32-byte rows) and the
 // block's K/V scales.
 constexpr int kPRow = 32;
-struct WaveLoopSmem {
-  char p[kBlock * kPRow];
+template <int kP>
+struct WaveLoopSmemT {
+  char p[kP][kBlock * kPRow];   // one staging block per operand plane
   float sc[64];           // the block's K scales (lanes 0-31) and V scales (lanes 32-63)
   float mn[64];           // asymmetric format: the matching minima m
 };
@@ -461,19 +475,19 @@ struct SetupSmem {
   float qsum[8];
   int E[8];
 };
-template <int kW>
+template <int kW, int kP>
 union DecodeSmemU {
   MergeSmemT<kW> merge;
-  WaveLoopSmem loop[kW];
+  WaveLoopSmemT<kP> loop[kW];
   SetupSmem setup;
 };
 // The QK A operand in lane order (the same for every wave), built once and read from LDS for
 // every block, which keeps 16 registers per lane free for a second block in flight.
-template <int kW>
+template <int kW, int kP>
 struct DecodeSmem {
   uint4v qop[4][64];
   float blk[32][16];      // the KV head's SO(4) blocks, for the inverse rotation of the partials
-  DecodeSmemU<kW> u;
+  DecodeSmemU<kW, kP> u;
 };
 
 __device__ __forceinline__ void build_block(const float* p, float* out16) {
@@ -690,9 +704,10 @@ template <bool kRefill, int kFmt>
 __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, int rem, int t_refill, int tok_end,
                                               const CacheBuffers& cb, const LaneOffsets& lo, bool vscale,
                                               WaveState& st, const uint4v (&qop)[4][64], const float (&c1)[2],
-                                              const float (&c2)[2], WaveLoopSmem& ws, int lane, int n, int g4,
-                                              unsigned pwr, unsigned prd, const LevelTable& lt) {
+                                              const float (&c2)[2], WaveLoopSmemT<Fmt<kFmt>::kPlanes>& ws, int lane,
+                                              int n, int g4, unsigned pwr, unsigned prd) {
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
+  constexpr int kP = Fmt<kFmt>::kPlanes;
   if constexpr (kAsym) {
     ws.sc[lane] = __uint_as_float(cur.ksc);
     ws.mn[lane] = __uint_as_float(cur.vsc);
@@ -703,25 +718,44 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
   floatx4 S[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    unsigned u[16];
-    unpack_k<kFmt>(cur.kw[tt], u);
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (Fmt<kFmt>::kTable) {
+      // each plane on the same query operand into its own accumulator, then combined with the
+      // planes' coefficients relative to the first (the first's goes into the score scale)
+      unsigned win[2][3], fold[2][3];
+      quarter_windows(cur.kw[tt][0], cur.kw[tt][1], cur.kw[tt][2], win);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      if constexpr (Fmt<kFmt>::kTable) {     // word w holds field w % 8 of a group pair at field_pos
-        unsigned h[4], l[4];
+      for (int P = 0; P < 2; ++P)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) level_pair(u[4 * kb + i], field_pos((4 * kb + i) & 7), lt, h[i], l[i]);
+        for (int k = 0; k < 3; ++k) fold[P][k] = parity_fold(win[P][k]);
+      floatx4 acc[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {             // words 4 kb .. 4 kb + 3 of unpack_quarter's order
+        unsigned pl[4][4];                          // [word][plane]
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int w = 4 * kb + i, P = w >> 3, j = w & 7;
+          planes_of(win[P][j / 3], fold[P][j / 3], field_pos(j), pl[i]);
+        }
         const half8 qa = __builtin_bit_cast(half8, qop[kb][lane]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_half8(h[0], h[1], h[2], h[3]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_half8(l[0], l[1], l[2], l[3]), acc, 0, 0, 0);
-      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa, as_half8(pl[0][e], pl[1][e], pl[2][e], pl[3][e]),
+                                                          acc[e], 0, 0, 0);
+      }
+      S[tt] = acc[0] + kLmR[1] * acc[1] + kLmR[2] * acc[2] + kLmR[3] * acc[3];
+    } else {
+      unsigned u[16];
+      unpack_k<kFmt>(cur.kw[tt], u);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[kb][lane]),
                                                     as_half8(u[4 * kb], u[4 * kb + 1], u[4 * kb + 2], u[4 * kb + 3]),
                                                     acc, 0, 0, 0);
-      }
+      S[tt] = acc;
     }
-    S[tt] = acc;
   }
   // ---- V: each lane holds quarter y = (lane >> 2) & 3 (groups 4y..4y+3) of the tokens
   //      16t + 4 g4 + x, x = lane & 3; a 4x4 transpose inside each quad of lanes leaves lane x with
@@ -836,39 +870,63 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
   const float svm[2] = {sv0 * st.pmul, sv1 * st.pmul};
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    _Float16 h4[4];
+    float pp[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float p = __builtin_amdgcn_exp2f(z[j][tt] - st.m_run[j]);
       st.l_run[j] += p;
-      const float pp = p * svm[tt];
-      st.ls_run[j] = kAsym ? fmaf(p, mv[tt], st.ls_run[j]) : st.ls_run[j] + pp;
-      const _Float16 hi = (_Float16)pp;
-      h4[2 * j] = hi;
-      h4[2 * j + 1] = (_Float16)(pp - (float)hi);
+      pp[j] = p * svm[tt];
+      st.ls_run[j] = kAsym ? fmaf(p, mv[tt], st.ls_run[j]) : st.ls_run[j] + pp[j];
     }
-    *reinterpret_cast<short4v*>(ws.p + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, h4);
+    // plane e stages P'' times its coefficient relative to the first plane's
+#pragma unroll
+    for (int e = 0; e < kP; ++e) {
+      _Float16 h4[4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float v = e == 0 ? pp[j] : pp[j] * kLmR[e];
+        const _Float16 hi = (_Float16)v;
+        h4[2 * j] = hi;
+        h4[2 * j + 1] = (_Float16)(v - (float)hi);
+      }
+      *reinterpret_cast<short4v*>(ws.p[e] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, h4);
+    }
   }
   __builtin_amdgcn_wave_barrier();
   // ---- PV: A = P'' (rows (head, part)) read transposed, B = V field j of the token pairs ----
-  const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd));
-  const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p + prd + 16 * kPRow));
-  const half8 pop = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
+  half8 pop[kP];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const unsigned m = VField<kFmt>::mask(j);
-    const int wj = VField<kFmt>::win(j);
-    if constexpr (Fmt<kFmt>::kTable) {
-      unsigned h[4], l[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) level_pair(vwin[p][wj] & m, VField<kFmt>::pos(j), lt, h[p], l[p]);
-      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(h[0], h[1], h[2], h[3]), st.O[j], 0, 0, 0);
-      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, as_half8(l[0], l[1], l[2], l[3]), st.O[j], 0, 0, 0);
-    } else {
-      const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
-      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop, vb, st.O[j], 0, 0, 0);
-    }
+  for (int e = 0; e < kP; ++e) {
+    const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[e] + prd));
+    const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[e] + prd + 16 * kPRow));
+    pop[e] = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
   }
+  unsigned vfold[4][kWin];                                          // parity folds (planes only)
+  if constexpr (Fmt<kFmt>::kTable) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int k = 0; k < kWin; ++k) vfold[p][k] = parity_fold(vwin[p][k]);
+  }
+  // (planes: plane-major, so consecutive products go to different accumulators)
+#pragma unroll
+  for (int e = 0; e < kP; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int wj = VField<kFmt>::win(j);
+      unsigned bw[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        if constexpr (Fmt<kFmt>::kTable) {
+          unsigned pl[4];
+          planes_of(vwin[p][wj], vfold[p][wj], VField<kFmt>::pos(j), pl);
+          bw[p] = pl[e];
+        } else {
+          bw[p] = vwin[p][wj] & VField<kFmt>::mask(j);
+        }
+      }
+      st.O[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop[e], as_half8(bw[0], bw[1], bw[2], bw[3]), st.O[j], 0, 0, 0);
+    }
   __builtin_amdgcn_wave_barrier();
 }
 
@@ -961,7 +1019,7 @@ void decode_split_kernel(DecodeKArgs a) {
   static_assert(kW == kWaves || kW == 2 * kWaves, "four or eight waves");
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
   constexpr int kRec = Fmt<kFmt>::kRec;
-  __shared__ DecodeSmem<kW> sm;
+  __shared__ DecodeSmem<kW, Fmt<kFmt>::kPlanes> sm;
   // blockIdx.x: (KV head, head group) column, so consecutive work-groups take the columns of one
   // work item (measured slightly faster than the transposed order)
   const int x = blockIdx.y;          // (sequence, chunk) pair
@@ -1150,11 +1208,12 @@ void decode_split_kernel(DecodeKArgs a) {
   const int E0 = ss.E[2 * g4], E1 = ss.E[2 * g4 + 1];
   const float qsum0 = ss.qsum[2 * g4], qsum1 = ss.qsum[2 * g4 + 1];
   __syncthreads();                   // the operand is complete; the set-up area is staging space from here on
-  WaveLoopSmem& ws = sm.u.loop[wave];
+  WaveLoopSmemT<Fmt<kFmt>::kPlanes>& ws = sm.u.loop[wave];
 
   // z2 = log2(e) * sm * s_K * (q'.c - 3.5 sum q'), with q'.c = raw * 2^(24-E) for each head's E.
-  const float c1[2] = {a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E0), a.sm_log2 * ldexpf(1.f, Fmt<kFmt>::kSub - E1)};
-  const LevelTable lt = Fmt<kFmt>::kTable ? lm3_table() : LevelTable{};
+  // (Lloyd-Max: the first plane's coefficient kGain scales the combined planes)
+  const float c1[2] = {a.sm_log2 * Fmt<kFmt>::kGain * ldexpf(1.f, Fmt<kFmt>::kSub - E0),
+                       a.sm_log2 * Fmt<kFmt>::kGain * ldexpf(1.f, Fmt<kFmt>::kSub - E1)};
   // (asymmetric format: c2 = log2(e) sm sum q', the coefficient of the minimum m_K)
   constexpr float kC = kAsym ? 1.f : Fmt<kFmt>::kCenter;
   const float c2[2] = {a.sm_log2 * kC * qsum0, a.sm_log2 * kC * qsum1};
@@ -1185,15 +1244,15 @@ void decode_split_kernel(DecodeKArgs a) {
     progress_priority(t0 - tok0, tok_end - tok0);
     load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
     process_block<true, kFmt>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, pwr, prd, lt);
+                        ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<true, kFmt>(buf2, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
-                        ws, lane, n, g4, pwr, prd, lt);
+                        ws, lane, n, g4, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
     process_block<false, kFmt>(buf3, min(tok_end - t0, kBlock), 0, tok_end, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
-                         n, g4, pwr, prd, lt);
+                         n, g4, pwr, prd);
     t0 += step;
   }
 
@@ -1212,14 +1271,14 @@ void decode_split_kernel(DecodeKArgs a) {
       sm.u.merge.l[wave][2 * g4 + j] = l_tot[j];
     }
   }
-  // o'[coord] = vlim/16 * (O * 2^(24 - p) - 3.5 * ls), O = hi row + lo row; tile j column n is
+  // o'[coord] = vlim/16 * (kGain O 2^(24 - p) - kCenter ls), O = hi row + lo row; tile j column n is
   // coordinate 8n + j, taken at bit position field_pos(j).
   {
     const float back = ldexpf(1.f / kPScale, st.vexp);
 #pragma unroll
     for (int j8 = 0; j8 < 8; ++j8) {
       const int coord = 8 * n + j8;
-      const float up = (float)(1 << (Fmt<kFmt>::kSub - (Fmt<kFmt>::kTable ? 0 : VField<kFmt>::pos(j8))));
+      const float up = Fmt<kFmt>::kGain * (float)(1 << (Fmt<kFmt>::kSub - VField<kFmt>::pos(j8)));
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         sm.u.merge.o[wave][2 * g4 + j][coord] =
