@@ -50,8 +50,8 @@
 // masks, byte windows and slot maps), the asymmetric 3-bit format (the same records, an (s, m)
 // pair per token: q'.(m + s c) = s (q'.c) + m sum(q'), and sum p m_V is added to every output
 // coordinate) and the Lloyd-Max 3-bit format (the same records; its levels are not uniform, so
-// each code is looked up in byte tables of the levels' fp16 hi and lo parts with v_perm, and
-// every product takes two MFMAs, one per part).
+// each code enters as four exact subnormal planes, c, c & 6, c & 4 and parity(c), whose products
+// are combined with fixed coefficients into the level's).
 // Kernel 1b (decode_multi_kernel), several query tokens per sequence: the
 // same loop for a group of two consecutive query tokens, each block's codes
 // unpacked once and multiplied by both tokens' operands, each token with its
@@ -155,12 +155,13 @@ struct Fmt {
   static constexpr int kRec = 16 * kBits;             // record bytes
   static constexpr int kQW = kBits;                   // dwords of a quarter (4 kBits bytes)
   static constexpr bool kAsym = kFmt == IQ_FMT_A3;
-  // Lloyd-Max levels are not uniform: each code enters as four subnormal operands (the planes below),
-  // whose products are combined with the planes' coefficients
-  static constexpr bool kTable = kFmt == IQ_FMT_LM3;
-  static constexpr int kPlanes = kTable ? 4 : 1;
+  // Lloyd-Max levels are not uniform: each code enters as four subnormal operand planes (above),
+  // whose products are combined with the planes' relative coefficients kLmR
+  static constexpr bool kLloydMax = kFmt == IQ_FMT_LM3;
+  static constexpr int kPlanes = kLloydMax ? 4 : 1;
   static constexpr int kSub = 24;                     // operand exponent offset undone in the scores
-  // level(c) = kGain (code + planes) - kCenter: the centre of the uniform codes, A0 for Lloyd-Max
+  // level(c) = kGain (sum over planes e of kLmR[e] plane_e(c)) - kCenter; a uniform code is its own
+  // single plane (kGain 1, kCenter the middle of the code range)
   static constexpr float kCenter = kFmt == IQ_FMT_U4 ? 7.5f : kFmt == IQ_FMT_U2 ? 1.5f : kFmt == IQ_FMT_LM3 ? kLmA0 : 3.5f;
   static constexpr float kGain = kFmt == IQ_FMT_LM3 ? kLmK0 : 1.f;
 };
@@ -718,7 +719,7 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
   floatx4 S[2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
-    if constexpr (Fmt<kFmt>::kTable) {
+    if constexpr (Fmt<kFmt>::kLloydMax) {
       // each plane on the same query operand into its own accumulator, then combined with the
       // planes' coefficients relative to the first (the first's goes into the score scale)
       unsigned win[2][3], fold[2][3];
@@ -902,7 +903,7 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
     pop[e] = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
   }
   unsigned vfold[4][kWin];                                          // parity folds (planes only)
-  if constexpr (Fmt<kFmt>::kTable) {
+  if constexpr (Fmt<kFmt>::kLloydMax) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
@@ -917,7 +918,7 @@ __device__ __forceinline__ void process_block(BlockData<Fmt<kFmt>::kQW>& cur, in
       unsigned bw[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        if constexpr (Fmt<kFmt>::kTable) {
+        if constexpr (Fmt<kFmt>::kLloydMax) {
           unsigned pl[4];
           planes_of(vwin[p][wj], vfold[p][wj], VField<kFmt>::pos(j), pl);
           bw[p] = pl[e];
