@@ -1324,18 +1324,18 @@ void decode_split_kernel(DecodeKArgs a) {
 // With several query tokens per cached sequence (iq_decode_attention_multi) the kernel above would
 // read and unpack every block once per token.  Here a work item is a chunk of a group of kMultiQ
 // consecutive query tokens: each 32-token block's K and V codes are unpacked once and multiplied by
-// every token's operand (one QK and one PV product per token), and each token keeps its own online
-// softmax; the V scale bound is shared.  Wave w rotates token w's queries.  3-bit records, no
-// append.  Two tokens per group: their accumulators fill 256 registers, two waves per SIMD (four
-// tokens need more than the 256 architectural registers and spill to the accumulation registers,
-// which measured slower than one token per work item).
-constexpr int kMultiQ = 2;                    // tokens per group (one per wave at set-up)
+// every token's operands, and each token keeps its own online softmax; the V scale bound is shared.
+// Wave w rotates token w's queries.  3-bit records, no append.  The tokens go in pairs: the 16 rows
+// of a product are (token, query head) of two tokens, and the hi and lo parts of q' and of P'' are
+// the two halves of its K dimension (two products into one accumulator), so a token's accumulators
+// take 16 registers.  Four tokens per group fill the 256 registers of two waves per SIMD.
+constexpr int kMultiQ = 4;                    // tokens per group (one per wave at set-up), even
 constexpr int kMultiWavesPerSimd = 2;
 constexpr int kMultiRounds = 3;               // work items per column: three rounds of work-groups
 constexpr float kNoMax = -1e30f;              // running max before any score: finite, so a token
                                               // with nothing to attend to in a chunk gets p = 0
 struct MultiLoopSmem {
-  char p[kMultiQ][kBlock * kPRow];            // P'' staging of each token
+  char p[kMultiQ / 2][2][kBlock * kPRow];     // P'' staging of each token pair: hi parts, lo parts
   float sc[64];
 };
 struct MultiSetupSmem {
@@ -1349,33 +1349,37 @@ union MultiSmemU {
   MultiSetupSmem setup;
 };
 struct MultiSmem {
-  uint4v qop[kMultiQ][4][64];                 // QK A operand of each token
+  uint4v qop[kMultiQ / 2][2][4][64];          // QK A operand of each token pair: hi parts, lo parts
   float blk[32][16];                          // the KV head's SO(4) blocks (set-up and the partials)
   MultiSmemU u;
 };
 
-template <int kQ>
+// Lane (n, g4) of a token pair's tile holds rows 4 g4 + r, r = 0..3: token 2 pair + g4 / 2, query
+// head 4 (g4 % 2) + r.
+template <int kP>
 struct MultiState {
-  floatx4 O[kQ][8];
-  float m_run[kQ][2], thr[kQ][2], l_run[kQ][2], ls_run[kQ][2];
+  floatx4 O[kP][8];       // O[pair][j]: rows (token, head), column n = coordinate 8n + j
+  float m_run[kP][4], thr[kP][4], l_run[kP][4], ls_run[kP][4];   // per row r of the lane
   int vexp;
   float vlim, pmul;
 };
 
-// process_block for kQ tokens (3-bit records).  lim[i]: token i attends to the block's tokens below
-// lim[i].  A token the group does not have runs too, with lim = the chunk start: every score is
-// masked, so its p and its products are zero (straight-line code, no per-token branches).
-template <bool kRefill, int kQ>
-__device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, int tok_end, const int (&lim)[kQ],
+// process_block for kP token pairs (3-bit records).  A pair's 16 rows are (token, head), and the hi
+// and lo parts of q' (QK) and of P'' (PV) are the two halves of each product's K dimension: two
+// products into one accumulator.  lim[p]: the lane's token of pair p attends to the block's tokens
+// below lim[p].  A token the group does not have runs too, with lim = the chunk start: every score
+// is masked, so its p and its products are zero (straight-line code, no per-token branches).
+template <bool kRefill, int kP>
+__device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, int tok_end, const int (&lim)[kP],
                                                     int t_refill, const CacheBuffers& cb,
-                                                    const LaneOffsets& lo, bool vscale, MultiState<kQ>& st,
-                                                    const uint4v (&qop)[kMultiQ][4][64], const float (&c1)[kQ],
-                                                    const float (&c2)[kQ][2], MultiLoopSmem& ws, int lane, int n,
-                                                    int g4, unsigned pwr, unsigned prd) {
+                                                    const LaneOffsets& lo, bool vscale, MultiState<kP>& st,
+                                                    const uint4v (&qop)[kMultiQ / 2][2][4][64],
+                                                    const float (&c1)[kP], const float (&c2)[kP][4],
+                                                    MultiLoopSmem& ws, int lane, int n, unsigned pwr, unsigned prd) {
   constexpr int kFmt = IQ_FMT_U3;
   ws.sc[lane] = __uint_as_float(vscale ? cur.vsc : cur.ksc);
-  // ---- QK of every token on the same unpacked codes ----
-  floatx4 S[kQ][2];
+  // ---- QK of every pair on the same unpacked codes ----
+  floatx4 S[kP][2];
 #pragma unroll
   for (int tt = 0; tt < 2; ++tt) {
     unsigned u[16];
@@ -1384,12 +1388,15 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
 #pragma unroll
     for (int k = 0; k < 4; ++k) kb[k] = as_half8(u[4 * k], u[4 * k + 1], u[4 * k + 2], u[4 * k + 3]);
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
+    for (int p = 0; p < kP; ++p) {
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[i][k][lane]), kb[k], acc, 0, 0, 0);
-      S[i][tt] = acc;
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qop[p][part][k][lane]), kb[k], acc,
+                                                      0, 0, 0);
+      S[p][tt] = acc;
     }
   }
   // ---- V byte windows, as in process_block ----
@@ -1414,28 +1421,28 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
     __builtin_amdgcn_sched_barrier(0);
     load_block<kFmt>(cur, cb, t_refill, tok_end, lo);
   }
-  // ---- scores; tokens past the chunk carry no V scale, tokens past lim[i] no score ----
+  // ---- scores; tokens past the chunk carry no V scale, tokens past lim[p] no score ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
   float sv0 = ws.sc[32 + n], sv1 = ws.sc[48 + n];
   const int rem = tok_end - t0;
   if (n >= rem) sv0 = 0.f;
   if (16 + n >= rem) sv1 = 0.f;
-  float z[kQ][2][2];
+  float z[kP][4][2];
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
-    const int ri = lim[i] - t0;
+  for (int p = 0; p < kP; ++p) {
+    const int ri = lim[p] - t0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      z[i][j][0] = n < ri ? sk0 * fmaf(S[i][0][2 * j] + S[i][0][2 * j + 1], c1[i], -c2[i][j]) : -INFINITY;
-      z[i][j][1] = 16 + n < ri ? sk1 * fmaf(S[i][1][2 * j] + S[i][1][2 * j + 1], c1[i], -c2[i][j]) : -INFINITY;
+    for (int r = 0; r < 4; ++r) {
+      z[p][r][0] = n < ri ? sk0 * fmaf(S[p][0][r], c1[p], -c2[p][r]) : -INFINITY;
+      z[p][r][1] = 16 + n < ri ? sk1 * fmaf(S[p][1][r], c1[p], -c2[p][r]) : -INFINITY;
     }
   }
   const float svmax = fmaxf(sv0, sv1);
   bool grow = svmax >= st.vlim;
 #pragma unroll
-  for (int i = 0; i < kQ; ++i)
+  for (int p = 0; p < kP; ++p)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) grow |= fmaxf(z[i][j][0], z[i][j][1]) > st.thr[i][j];
+    for (int r = 0; r < 4; ++r) grow |= fmaxf(z[p][r][0], z[p][r][1]) > st.thr[p][r];
   if (__any(grow)) {
     const float vmax = row_max(svmax);
     float ratio = 1.f;
@@ -1449,59 +1456,73 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
       st.pmul = ldexpf(kPScale, -ex);
     }
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) {
-      float f[2];
+    for (int p = 0; p < kP; ++p) {
+      float f[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float m_new = fmaxf(st.m_run[i][j], row_max(fmaxf(z[i][j][0], z[i][j][1])));
-        const float alpha = __builtin_amdgcn_exp2f(st.m_run[i][j] - m_new);
-        st.l_run[i][j] *= alpha;
-        st.ls_run[i][j] *= alpha * ratio;
-        st.m_run[i][j] = m_new;
-        st.thr[i][j] = m_new + kHeadroom;
-        f[j] = alpha * ratio;
+      for (int r = 0; r < 4; ++r) {
+        const float m_new = fmaxf(st.m_run[p][r], row_max(fmaxf(z[p][r][0], z[p][r][1])));
+        const float alpha = __builtin_amdgcn_exp2f(st.m_run[p][r] - m_new);
+        st.l_run[p][r] *= alpha;
+        st.ls_run[p][r] *= alpha * ratio;
+        st.m_run[p][r] = m_new;
+        st.thr[p][r] = m_new + kHeadroom;
+        f[r] = alpha * ratio;
       }
       // whole accumulator tuples: no copies of them on the path without a rescale
-      const floatx4 fv = {f[0], f[0], f[1], f[1]};
+      const floatx4 fv = {f[0], f[1], f[2], f[3]};
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) st.O[i][nt] *= fv;
+      for (int nt = 0; nt < 8; ++nt) st.O[p][nt] *= fv;
     }
   }
-  // ---- P'' of each token, staged and read back transposed; PV on the shared V windows ----
+  // ---- P'' of each pair, its hi and lo parts staged apart and read back transposed ----
   const float svm[2] = {sv0 * st.pmul, sv1 * st.pmul};
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
+  for (int p = 0; p < kP; ++p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      _Float16 h4[4];
+      _Float16 hh[4], hl[4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const float p = __builtin_amdgcn_exp2f(z[i][j][tt] - st.m_run[i][j]);
-        st.l_run[i][j] += p;
-        const float pp = p * svm[tt];
-        st.ls_run[i][j] += pp;
+      for (int r = 0; r < 4; ++r) {
+        const float pr = __builtin_amdgcn_exp2f(z[p][r][tt] - st.m_run[p][r]);
+        st.l_run[p][r] += pr;
+        const float pp = pr * svm[tt];
+        st.ls_run[p][r] += pp;
         const _Float16 hi = (_Float16)pp;
-        h4[2 * j] = hi;
-        h4[2 * j + 1] = (_Float16)(pp - (float)hi);
+        hh[r] = hi;
+        hl[r] = (_Float16)(pp - (float)hi);
       }
-      *reinterpret_cast<short4v*>(ws.p[i] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, h4);
+      *reinterpret_cast<short4v*>(ws.p[p][0] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, hh);
+      *reinterpret_cast<short4v*>(ws.p[p][1] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, hl);
     }
   }
   __builtin_amdgcn_wave_barrier();
-  half8 pop[kQ];
+  half8 pop[kP][2];
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
-    const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[i] + prd));
-    const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[i] + prd + 16 * kPRow));
-    pop[i] = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
-  }
+  for (int p = 0; p < kP; ++p)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const unsigned m = VField<kFmt>::mask(j);
-    const int wj = VField<kFmt>::win(j);
-    const half8 vb = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
+    for (int part = 0; part < 2; ++part) {
+      const short4v pa = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[p][part] + prd));
+      const short4v pb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4)(ws.p[p][part] + prd + 16 * kPRow));
+      pop[p][part] = __builtin_bit_cast(half8, short8v{pa[0], pa[1], pa[2], pa[3], pb[0], pb[1], pb[2], pb[3]});
+    }
+  // ---- PV on the shared V windows: fields two at a time, so a field's hi and lo products are
+  //      not back to back ----
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) st.O[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop[i], vb, st.O[i][j], 0, 0, 0);
+  for (int j = 0; j < 8; j += 2) {
+    half8 vb[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const unsigned m = VField<kFmt>::mask(j + d);
+      const int wj = VField<kFmt>::win(j + d);
+      vb[d] = as_half8(vwin[0][wj] & m, vwin[1][wj] & m, vwin[2][wj] & m, vwin[3][wj] & m);
+    }
+#pragma unroll
+    for (int part = 0; part < 2; ++part)
+#pragma unroll
+      for (int p = 0; p < kP; ++p)
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+          st.O[p][j + d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pop[p][part], vb[d], st.O[p][j + d], 0, 0, 0);
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -1509,7 +1530,8 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
 template <int kQ>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kMultiWavesPerSimd, kMultiWavesPerSimd)))
 void decode_multi_kernel(DecodeKArgs a) {
-  static_assert(kQ <= kMultiQ && kQ <= kWaves, "one token per set-up wave");
+  static_assert(kQ <= kMultiQ && kQ <= kWaves && kQ % 2 == 0, "one token per set-up wave, pairs of tokens");
+  constexpr int kP = kQ / 2;
   constexpr int kFmt = IQ_FMT_U3;
   constexpr int kRec = 48;
   __shared__ MultiSmem sm;
@@ -1644,46 +1666,58 @@ void decode_multi_kernel(DecodeKArgs a) {
     }
     if (qe == 0) ss.qsum[wave][qi] = qs;
     if (lane == 0) ss.E[wave] = E;
-    __builtin_amdgcn_wave_barrier();
-    const int head = n >> 1, part = n & 1;
+  }
+  __syncthreads();
+  // A operands: wave 2 p + part builds part (hi or lo) of pair p, lane row n = (token 2 p + n / 8,
+  // head n % 8), K slots of quarter g4; tokens the group does not have get zeros
+  if (wave < 2 * kP) {               // uniform
+    const int pr = wave >> 1, part = wave & 1;
+    const int tok = 2 * pr + (n >> 3), head = n & 7;
+    const bool have = tok < nq;
+    const int Et = have ? ss.E[tok] : 0;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       _Float16 hv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int sl = 8 * kb + e;
-        const float v = ldexpf(ss.qrot[wave][head][32 * g4 + slot_coord_f<kFmt>(sl)], E - slot_pow_f<kFmt>(sl));
+        const float v = have ? ldexpf(ss.qrot[tok][head][32 * g4 + slot_coord_f<kFmt>(sl)], Et - slot_pow_f<kFmt>(sl))
+                             : 0.f;
         const _Float16 hi = (_Float16)v;
         hv[e] = part ? (_Float16)(v - (float)hi) : hi;
       }
-      sm.qop[wave][kb][lane] = __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
+      sm.qop[pr][part][kb][lane] =
+          __builtin_bit_cast(uint4v, half8{hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]});
     }
   }
-  __syncthreads();
-  float c1[kQ], c2[kQ][2];
+  // this lane's rows of pair p belong to token 2 p + g4 / 2, query heads 4 (g4 % 2) + r
+  float c1[kP], c2[kP][4];
+  int lim_l[kP];
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
-    const bool in = i < nq;
-    c1[i] = in ? a.sm_log2 * ldexpf(1.f, 24 - ss.E[i]) : 0.f;
+  for (int p = 0; p < kP; ++p) {
+    const int tok = 2 * p + (g4 >> 1);
+    const bool in = tok < nq;
+    c1[p] = in ? a.sm_log2 * ldexpf(1.f, 24 - ss.E[tok]) : 0.f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) c2[i][j] = in ? a.sm_log2 * 3.5f * ss.qsum[i][2 * g4 + j] : 0.f;
+    for (int r = 0; r < 4; ++r) c2[p][r] = in ? a.sm_log2 * 3.5f * ss.qsum[tok][4 * (g4 & 1) + r] : 0.f;
+    lim_l[p] = (g4 & 2) ? lim[2 * p + 1] : lim[2 * p];
   }
-  __syncthreads();                   // the set-up area is staging space from here on
+  __syncthreads();                   // the operands are complete; the set-up area is staging space from here on
   MultiLoopSmem& ws = sm.u.loop[wave];
   const unsigned pwr = (unsigned)(n * kPRow + 8 * g4);
   const unsigned prd = (unsigned)((4 * g4 + (n >> 2)) * kPRow + 8 * (n & 3));
 
-  MultiState<kQ> st;
+  MultiState<kP> st;
 #pragma unroll
-  for (int i = 0; i < kQ; ++i) {
+  for (int p = 0; p < kP; ++p) {
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) st.O[i][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int nt = 0; nt < 8; ++nt) st.O[p][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      st.m_run[i][j] = kNoMax;
-      st.thr[i][j] = kNoMax;
-      st.l_run[i][j] = 0.f;
-      st.ls_run[i][j] = 0.f;
+    for (int r = 0; r < 4; ++r) {
+      st.m_run[p][r] = kNoMax;
+      st.thr[p][r] = kNoMax;
+      st.l_run[p][r] = 0.f;
+      st.ls_run[p][r] = 0.f;
     }
   }
   st.vexp = -200;
@@ -1693,15 +1727,15 @@ void decode_multi_kernel(DecodeKArgs a) {
   while (t0 < tok_end) {            // uniform
     progress_priority(t0 - tok0, tok_end - tok0);
     load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
-    process_block_multi<true, kQ>(buf, t0, tok_end, lim, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane,
-                                  n, g4, pwr, prd);
+    process_block_multi<true, kP>(buf, t0, tok_end, lim_l, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                                  lane, n, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block_multi<true, kQ>(buf2, t0, tok_end, lim, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws,
-                                  lane, n, g4, pwr, prd);
+    process_block_multi<true, kP>(buf2, t0, tok_end, lim_l, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws,
+                                  lane, n, pwr, prd);
     t0 += step;
     if (t0 >= tok_end) break;
-    process_block_multi<false, kQ>(buf3, t0, tok_end, lim, 0, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane, n, g4,
+    process_block_multi<false, kP>(buf3, t0, tok_end, lim_l, 0, cb, lo, vscale, st, sm.qop, c1, c2, ws, lane, n,
                                    pwr, prd);
     t0 += step;
   }
@@ -1712,27 +1746,30 @@ void decode_multi_kernel(DecodeKArgs a) {
 #pragma unroll
   for (int i = 0; i < kQ; ++i) {
     if (i >= nq) continue;             // uniform
-    float l_tot[2], ls_tot[2];
+    const int p = i >> 1;
+    float l_tot[4], ls_tot[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      l_tot[j] = row_sum(st.l_run[i][j]);
-      ls_tot[j] = row_sum(st.ls_run[i][j]);
+    for (int r = 0; r < 4; ++r) {
+      l_tot[r] = row_sum(st.l_run[p][r]);
+      ls_tot[r] = row_sum(st.ls_run[p][r]);
     }
-    if (n == 0) {
+    if ((g4 >> 1) == (i & 1)) {        // the lanes holding token i's rows: query heads 4 (g4 % 2) + r
+      const int h4 = 4 * (g4 & 1);
+      if (n == 0) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        sm.u.merge.m[wave][2 * g4 + j] = st.m_run[i][j];
-        sm.u.merge.l[wave][2 * g4 + j] = l_tot[j];
+        for (int r = 0; r < 4; ++r) {
+          sm.u.merge.m[wave][h4 + r] = st.m_run[p][r];
+          sm.u.merge.l[wave][h4 + r] = l_tot[r];
+        }
       }
-    }
 #pragma unroll
-    for (int j8 = 0; j8 < 8; ++j8) {
-      const int coord = 8 * n + j8;
-      const float up = (float)(1 << (24 - VField<kFmt>::pos(j8)));
+      for (int j8 = 0; j8 < 8; ++j8) {
+        const int coord = 8 * n + j8;
+        const float up = (float)(1 << (24 - VField<kFmt>::pos(j8)));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sm.u.merge.o[wave][2 * g4 + j][coord] =
-            back * fmaf(st.O[i][j8][2 * j] + st.O[i][j8][2 * j + 1], up, -3.5f * ls_tot[j]);
+        for (int r = 0; r < 4; ++r)
+          sm.u.merge.o[wave][h4 + r][coord] = back * fmaf(st.O[p][j8][r], up, -3.5f * ls_tot[r]);
+      }
     }
     __syncthreads();
     {                                  // as in the single-token kernel: merge, rotate back, write
@@ -2050,11 +2087,12 @@ DecodeGeometry decode_geometry(int batch, int n_q_heads, int n_kv_heads, int64_t
   // partial rows per query head: x_max, or, when batch counts the query tokens of
   // iq_decode_attention_multi (B sequences of Q >= 2 tokens), kMultiQ rows for each work item of the
   // multi-token kernel: its target, or one per group of kMultiQ tokens
-  // (B ceil(Q / kMultiQ) kMultiQ <= 2 B Q = 2 batch)
+  // (B ceil(Q / kMultiQ) kMultiQ <= B Q + B (kMultiQ - 1) <= B Q (kMultiQ + 1) / 2, as B <= B Q / 2)
   int64_t rows = geo.x_max;
   const int64_t multi_target = (int64_t)kMultiRounds * kMultiWavesPerSimd * device_cu_count() / columns;
   if (kMultiQ * multi_target > rows) rows = kMultiQ * multi_target;
-  if (2 * (int64_t)batch > rows) rows = 2 * (int64_t)batch;
+  const int64_t multi_groups = ((int64_t)batch * (kMultiQ + 1) + 1) / 2;
+  if (multi_groups > rows) rows = multi_groups;
   const int64_t parts = rows * n_q_heads;
   geo.workspace_bytes = geo.plan_bytes + parts * 128 * 4 + parts * 2 * 4;
   return geo;

@@ -61,8 +61,9 @@ def test_multi_token_f32_queries_shared_rotation_full_cache():
 
 
 def test_multi_token_odd_count_many_chunks_and_empty_tokens():
-    # Q = 5: token groups of 2, 2 and 1 (the last group's second token is absent); lengths long
-    # enough for several chunks per group, and a sequence of 4 whose first token sees nothing
+    # Q = 5: token groups of 4 and 1 (three of the last group's tokens are absent, one of them in a
+    # pair with a present token); lengths long enough for several chunks per group, and a
+    # sequence of 4 whose first token sees nothing
     rng = np.random.default_rng(66)
     out, *_ = _check(rng, 3, 5, 16, 2, 2600, [2600, 700, 4], what="Q=5 ragged")
     assert torch.all(out[2, 0] == 0)                 # position -1
@@ -70,12 +71,13 @@ def test_multi_token_odd_count_many_chunks_and_empty_tokens():
 
 
 def test_multi_token_more_than_64_token_groups():
-    # 40 sequences of 4 tokens: 80 two-token groups, so the chunk plan takes its 64-at-a-time path
+    # 70 sequences of 6 tokens: 140 token groups (of 4 and 2), so the chunk plan takes its
+    # 64-at-a-time path
     rng = np.random.default_rng(67)
-    lens = list(rng.integers(0, 601, size=40))
+    lens = list(rng.integers(0, 601, size=70))
     lens[3], lens[7] = 0, 2                        # an empty sequence and one shorter than Q
-    out, *_ = _check(rng, 40, 4, 8, 2, 600, lens, what="Q=4 B=40")
-    assert torch.all(out[3] == 0) and torch.all(out[7, :2] == 0)
+    out, *_ = _check(rng, 70, 6, 8, 2, 600, lens, what="Q=6 B=70")
+    assert torch.all(out[3] == 0) and torch.all(out[7, :4] == 0)
 
 
 def test_multi_token_chunk_of_sixteen():
