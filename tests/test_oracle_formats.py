@@ -100,6 +100,24 @@ def test_lloyd_max_levels_and_errors_match_max_and_a_fresh_lloyd_iteration():
     assert F.gaussian_distortion(F.LLOYD_MAX_8) == pytest.approx(gold[8][1], abs=6e-5)
 
 
+def test_lloyd_max_table_is_odd_so_four_bit_planes_span_it():
+    # The decode builds each Lloyd-Max level from four exact operand planes of the code c
+    # (c, c & 6, c & 4, parity(c)) plus a constant.  That spans a level table exactly when the
+    # table is odd about the middle code (level 7 - c = -level c), as Max's is: the odd functions
+    # of three bits are spanned by the bits and their parity.  Check the premise on the oracle's
+    # table, and that the span holds it and fails for a table that is not odd.
+    L = np.array(F.LLOYD_MAX_8)
+    np.testing.assert_array_equal(L[::-1], -L)
+    c = np.arange(8)
+    basis = np.stack([c, c & 6, c & 4, (c ^ (c >> 1) ^ (c >> 2)) & 1, np.ones(8)], axis=1).astype(np.float64)
+    coef, *_ = np.linalg.lstsq(basis, L, rcond=None)
+    np.testing.assert_allclose(basis @ coef, L, atol=1e-12)
+    bent = L.copy()
+    bent[7] += 0.01
+    coef_b, *_ = np.linalg.lstsq(basis, bent, rcond=None)
+    assert np.max(np.abs(basis @ coef_b - bent)) > 1e-3
+
+
 def test_lloyd_max_format_nearest_level_and_rms_scale():
     rng = np.random.default_rng(75)
     y = rng.standard_normal((40, 128)) * 3.0
