@@ -550,6 +550,20 @@ __device__ __forceinline__ int range_bytes(int cap, int rec) { return (int)((uns
 // size is validated to stay below it), so its loads return zeros without reaching memory.
 constexpr unsigned kNoBlock = 0xF0000000u;
 
+// Cache policy of every load of the packed cache (codes and scales) in the split kernel:
+// non-temporal.  A decode call reads each record once, and a model's layers together stream far
+// more than the 256 MB last-level cache between two reads of one layer: loads that allocate
+// normally keep evicting lines for data that is not read again in time.  The hint took the
+// 48-layer step (654 MB) from 123 to 112 us on the same box.  The records still come through the
+// caches, so a record appended by the same work-group is read back.  A single call whose records
+// fit the last-level cache, replayed back to back, loses its hits across calls with the hint (the
+// 16-sequence ragged batch, 182 MB: 41.2 against 38.7 us), which a model with more layers than
+// one would not see.  The multi-token kernel keeps the default policy: several token groups read
+// each record within one call, and their re-reads hit the caches (Q = 16 on the 48-layer cache:
+// 0.88 ms, 0.92 ms with the hint).
+constexpr int kRecordLoadPolicy = 2;   // the NT bit of the cache-policy operand
+constexpr int kSharedLoadPolicy = 0;   // default caching
+
 // Keeps v in a register as an opaque value, so per-load constants added to it stay immediate
 // offsets instead of becoming separate loop-invariant registers.
 __device__ __forceinline__ unsigned opaque(unsigned v) {
@@ -561,24 +575,24 @@ __device__ __forceinline__ unsigned opaque(unsigned v) {
 // zeros without a memory access.  The whole offset is in the range-checked part of the buffer
 // address (vector offset plus immediate), so tokens past the end of the slice read as zeros too.
 // Loads one quarter (kQW dwords) at byte offset off of buffer r.
-template <int kQW>
+template <int kQW, int kPolicy>
 __device__ __forceinline__ void load_quarter(unsigned (&w)[kQW], __amdgpu_buffer_rsrc_t r, unsigned off) {
   if constexpr (kQW == 3) {
     typedef unsigned u3v __attribute__((ext_vector_type(3)));
-    const u3v q = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, 0);
+    const u3v q = __builtin_amdgcn_raw_buffer_load_b96(r, off, 0, kPolicy);
     w[0] = q.x; w[1] = q.y; w[2] = q.z;
   } else if constexpr (kQW == 4) {
     typedef unsigned u4v __attribute__((ext_vector_type(4)));
-    const u4v q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    const u4v q = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kPolicy);
     w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
   } else {
     typedef unsigned u2v __attribute__((ext_vector_type(2)));
-    const u2v q = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    const u2v q = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kPolicy);
     w[0] = q.x; w[1] = q.y;
   }
 }
 
-template <int kFmt>
+template <int kFmt, int kPolicy = kRecordLoadPolicy>
 __device__ __forceinline__ void load_block(BlockData<Fmt<kFmt>::kQW>& d, const CacheBuffers& cb, int t0, int tok_end,
                                            const LaneOffsets& lo) {
   constexpr bool kAsym = Fmt<kFmt>::kAsym;
@@ -587,26 +601,26 @@ __device__ __forceinline__ void load_block(BlockData<Fmt<kFmt>::kQW>& d, const C
   const unsigned base = in ? (unsigned)t0 * kRec : kNoBlock;
   const unsigned ko = opaque(lo.kcode + base), vo = opaque(lo.vcode + base);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW>(d.kw[tt], cb.kc, ko + 16 * kRec * tt);
+  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW, kPolicy>(d.kw[tt], cb.kc, ko + 16 * kRec * tt);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW>(d.vw[tt], cb.vc, vo + 16 * kRec * tt);
+  for (int tt = 0; tt < 2; ++tt) load_quarter<Fmt<kFmt>::kQW, kPolicy>(d.vw[tt], cb.vc, vo + 16 * kRec * tt);
   if constexpr (kAsym) {
     // each lane loads the (s, m) pair it stages, under an exec mask: K in lanes 0-31, V in 32-63
     typedef unsigned u2v __attribute__((ext_vector_type(2)));
     const unsigned so = 2 * lo.scale + (in ? (unsigned)t0 * 8u : kNoBlock);
     u2v sm;
     if (lo.vside)
-      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.vs, so, 0, 0);
+      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.vs, so, 0, kPolicy);
     else
-      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.ks, so, 0, 0);
+      sm = __builtin_amdgcn_raw_buffer_load_b64(cb.ks, so, 0, kPolicy);
     d.ksc = sm.x;
     d.vsc = sm.y;
   } else {
     // Both scale loads run in every lane (keeps the resources uniform); the block's consumer picks
     // one, so nothing here waits for the loads.
     const unsigned so = lo.scale + (in ? (unsigned)t0 * 4u : kNoBlock);
-    d.ksc = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, so, 0, 0);
-    d.vsc = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, so, 0, 0);
+    d.ksc = __builtin_amdgcn_raw_buffer_load_b32(cb.ks, so, 0, kPolicy);
+    d.vsc = __builtin_amdgcn_raw_buffer_load_b32(cb.vs, so, 0, kPolicy);
   }
 }
 
@@ -1419,7 +1433,7 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
   }
   if (kRefill) {
     __builtin_amdgcn_sched_barrier(0);
-    load_block<kFmt>(cur, cb, t_refill, tok_end, lo);
+    load_block<kFmt, kSharedLoadPolicy>(cur, cb, t_refill, tok_end, lo);
   }
   // ---- scores; tokens past the chunk carry no V scale, tokens past lim[p] no score ----
   const float sk0 = ws.sc[n], sk1 = ws.sc[16 + n];
@@ -1588,8 +1602,8 @@ void decode_multi_kernel(DecodeKArgs a) {
   const int step = kWaves * kBlock;
   int t0 = tok0 + wave * kBlock;
   BlockData<3> buf, buf2, buf3;
-  load_block<kFmt>(buf, cb, t0, tok_end, lo);
-  load_block<kFmt>(buf2, cb, t0 + step, tok_end, lo);
+  load_block<kFmt, kSharedLoadPolicy>(buf, cb, t0, tok_end, lo);
+  load_block<kFmt, kSharedLoadPolicy>(buf2, cb, t0 + step, tok_end, lo);
 
   // ---------------- set-up: wave w rotates query token t_first + w ----------------
   MultiSetupSmem& ss = sm.u.setup;
@@ -1726,7 +1740,7 @@ void decode_multi_kernel(DecodeKArgs a) {
 
   while (t0 < tok_end) {            // uniform
     progress_priority(t0 - tok0, tok_end - tok0);
-    load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    load_block<kFmt, kSharedLoadPolicy>(buf3, cb, t0 + 2 * step, tok_end, lo);
     process_block_multi<true, kP>(buf, t0, tok_end, lim_l, t0 + 3 * step, cb, lo, vscale, st, sm.qop, c1, c2, ws,
                                   lane, n, pwr, prd);
     t0 += step;
