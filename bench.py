@@ -378,19 +378,24 @@ def main():
     # itself then runs untimed for --settle seconds, whatever --warmup says: a GPU that has just
     # started needs about a second of work before its clocks are steady.
     stream_gbs = t_stream = None
+    t_streams = {}
     if not args.decode_only:
         sbuf = torch.empty(decode_bytes, dtype=torch.uint8, device=dev)
         sink = torch.zeros(4, dtype=torch.uint8, device=dev)
 
-        def stream_pass():
-            iq.stream_read(sbuf, sink, 2048)
+        # both load policies; the faster one is the ceiling
+        for nt in (False, True):
+            def stream_pass(nt=nt):
+                iq.stream_read(sbuf, sink, 2048, nontemporal=nt)
 
-        settle(stream_pass, 0.5)
-        t_stream = median(time_each(stream_pass, 50, stream))
+            settle(stream_pass, 0.5)
+            t_streams[nt] = median(time_each(stream_pass, 50, stream))
+        t_stream = min(t_streams.values())
         stream_gbs = decode_bytes / t_stream / 1e9
         del sbuf
-        log("read-only stream of %d bytes: %.1f us (median of 50), %.0f GB/s" %
-            (decode_bytes, t_stream * 1e6, stream_gbs))
+        log("read-only stream of %d bytes: %.1f us with default loads, %.1f us with non-temporal loads "
+            "(medians of 50), ceiling %.0f GB/s" % (decode_bytes, t_streams[False] * 1e6, t_streams[True] * 1e6,
+                                                    stream_gbs))
     n_settle = settle(step, args.settle)
     log("settle: %d untimed steps in >= %.1f s" % (n_settle, args.settle))
 
@@ -656,7 +661,10 @@ def main():
                      "median_launch_us": t_step * 1e6, "frac_at_median": step_gbs / HBM_PEAK_GBS,
                      "frac_of_measured_stream": step_gbs_mean / stream_gbs},
         "stream_read": {"GBs": stream_gbs, "bytes": decode_bytes, "us": t_stream * 1e6,
-                        "kernel": "iq_probe_stream_read (libiq_probe.so): 16-byte loads, grid-stride, 2048 x 256 threads"},
+                        "us_default_loads": t_streams[False] * 1e6 if t_streams else None,
+                        "us_nontemporal_loads": t_streams[True] * 1e6 if t_streams else None,
+                        "kernel": "iq_probe_stream_read / iq_probe_stream_read_nt (libiq_probe.so): 16-byte "
+                                  "loads, grid-stride, 2048 x 256 threads; the faster of the two"},
         "decode_only": {"ms": t_decode * 1e3, "GBs": decode_bytes / t_decode / 1e9},
         "append_then_decode_ms": t_two * 1e3,
         "append_alone_ms": t_append * 1e3,

@@ -6,23 +6,36 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, int64_t n, unsigned* sink) {
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// kNT: non-temporal loads (the cache-policy hint the decode's record loads carry)
+template <bool kNT>
+__global__ __launch_bounds__(256) void stream_read_kernel(const u4v* __restrict__ p, int64_t n, unsigned* sink) {
   unsigned acc = 0;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-    const uint4 v = p[i];
+    const u4v v = kNT ? __builtin_nontemporal_load(p + i) : p[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) *sink = acc;   // keeps the loads: the compiler cannot rule this out
 }
 
-}  // namespace
-
-extern "C" int iq_probe_stream_read(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream) {
+template <bool kNT>
+int stream_read(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream) {
   if (buf == nullptr || sink == nullptr || bytes <= 0 || bytes % 16 != 0 || n_blocks < 1 || n_blocks > 65535 ||
       reinterpret_cast<uintptr_t>(buf) % 16 != 0)
     return -1;
-  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint4*>(buf), bytes / 16, static_cast<unsigned*>(sink));
+  hipLaunchKernelGGL(stream_read_kernel<kNT>, dim3((unsigned)n_blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u4v*>(buf), bytes / 16, static_cast<unsigned*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // namespace
+
+extern "C" int iq_probe_stream_read(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream) {
+  return stream_read<false>(buf, bytes, n_blocks, sink, stream);
+}
+
+extern "C" int iq_probe_stream_read_nt(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream) {
+  return stream_read<true>(buf, bytes, n_blocks, sink, stream);
 }

@@ -369,17 +369,19 @@ def probe_lib():
         if not os.path.exists(PROBE_LIB_PATH):
             raise ImportError("libiq_probe.so is not built (%s); run __graft_entry__.build()" % PROBE_LIB_PATH)
         handle = ctypes.CDLL(PROBE_LIB_PATH)
-        handle.iq_probe_stream_read.restype = ctypes.c_int
-        handle.iq_probe_stream_read.argtypes = [_P, _I64, _I32, _P, _P]
+        for name in ("iq_probe_stream_read", "iq_probe_stream_read_nt"):
+            getattr(handle, name).restype = ctypes.c_int
+            getattr(handle, name).argtypes = [_P, _I64, _I32, _P, _P]
         _probe = handle
     return _probe
 
 
-def stream_read(buf, sink, n_blocks=2048):
+def stream_read(buf, sink, n_blocks=2048, nontemporal=False):
     """Read every byte of the cuda tensor buf once (asynchronous, on the current stream); sink
-    is a cuda tensor of at least 4 bytes."""
-    rc = probe_lib().iq_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), int(n_blocks),
-                                          sink.data_ptr(), _stream(buf))
+    is a cuda tensor of at least 4 bytes.  nontemporal: loads with the non-temporal hint."""
+    name = "iq_probe_stream_read_nt" if nontemporal else "iq_probe_stream_read"
+    rc = getattr(probe_lib(), name)(buf.data_ptr(), buf.numel() * buf.element_size(), int(n_blocks),
+                                    sink.data_ptr(), _stream(buf))
     if rc != 0:
-        raise IQError(rc, "iq_probe_stream_read: invalid arguments (buf 16-byte aligned, bytes a positive "
+        raise IQError(rc, name + ": invalid arguments (buf 16-byte aligned, bytes a positive "
                           "multiple of 16, 1 <= n_blocks <= 65535) or launch failure")

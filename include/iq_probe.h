@@ -26,6 +26,13 @@ extern "C" {
  */
 int iq_probe_stream_read(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream);
 
+/*
+ * iq_probe_stream_read_nt -- iq_probe_stream_read with non-temporal loads (the
+ * cache-policy hint that the decode's loads of the packed cache carry).
+ * Arguments and returns as iq_probe_stream_read.
+ */
+int iq_probe_stream_read_nt(const void* buf, int64_t bytes, int32_t n_blocks, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -277,12 +277,14 @@ def test_format_entry_points_validate():
 
 
 def test_probe_library_exports_and_validates():
-    # the measurement library beside libiq.so: its one symbol, and argument checks before any launch
+    # the measurement library beside libiq.so: its two symbols (default and non-temporal loads),
+    # and argument checks before any launch
     probe = binding.probe_lib()
-    assert hasattr(probe, "iq_probe_stream_read")
-    assert probe.iq_probe_stream_read(None, 1024, 64, FAKE, None) == -1
-    assert probe.iq_probe_stream_read(FAKE, 1000, 64, FAKE, None) == -1       # not a multiple of 16
-    assert probe.iq_probe_stream_read(FAKE + 4, 1024, 64, FAKE, None) == -1   # misaligned
-    assert probe.iq_probe_stream_read(FAKE, 1024, 0, FAKE, None) == -1
-    assert probe.iq_probe_stream_read(FAKE, 1024, 70000, FAKE, None) == -1
-    assert probe.iq_probe_stream_read(FAKE, 1024, 64, None, None) == -1
+    for name in ("iq_probe_stream_read", "iq_probe_stream_read_nt"):
+        fn = getattr(probe, name)
+        assert fn(None, 1024, 64, FAKE, None) == -1
+        assert fn(FAKE, 1000, 64, FAKE, None) == -1       # not a multiple of 16
+        assert fn(FAKE + 4, 1024, 64, FAKE, None) == -1   # misaligned
+        assert fn(FAKE, 1024, 0, FAKE, None) == -1
+        assert fn(FAKE, 1024, 70000, FAKE, None) == -1
+        assert fn(FAKE, 1024, 64, None, None) == -1
