@@ -154,3 +154,30 @@ def test_decode_format_head_groupings(fmt, Hq, Hkv):
     ref = F.decode_attention_format(q.astype(np.float64), F.unpack_bits(kc.cpu().numpy(), b), ks.cpu().numpy(),
                                     F.unpack_bits(vc.cpu().numpy(), b), vs.cpu().numpy(), params, np.array(lens), fmt)
     P.check_output(out.cpu().numpy(), ref, what="decode %s Hq=%d Hkv=%d" % (fmt, Hq, Hkv))
+
+
+@pytest.mark.parametrize("fmt", ["lm3", "u2", "u4"])
+def test_decode_format_on_uniformly_random_records(fmt):
+    # Random record bytes: every code value at every field position of K and V (3-bit fields that
+    # straddle bytes included), so each operand plane and each unpack mask meets every pattern.
+    # Scales are small so the scores stay moderate; the second sequence ends in a partial block.
+    rng = np.random.default_rng(240 + F.FORMATS.index(fmt))
+    B, Hq, Hkv, cap = 2, 8, 2, 1400
+    lens = [1400, 613]
+    rb = F.record_bytes(fmt)
+    kc = torch.from_numpy(rng.integers(0, 256, (B, Hkv, cap, rb), dtype=np.uint8)).cuda()
+    vc = torch.from_numpy(rng.integers(0, 256, (B, Hkv, cap, rb), dtype=np.uint8)).cuda()
+    ks = torch.from_numpy((rng.random((B, Hkv, cap)) * 0.2 + 0.02).astype(np.float32)).cuda()
+    vs = torch.from_numpy((rng.random((B, Hkv, cap)) * 0.5 + 0.05).astype(np.float32)).cuda()
+    params = _params(rng, B, Hkv)
+    rot = torch.from_numpy(params).cuda()
+    q = (rng.standard_normal((B, Hq, 128)) * 2.0).astype(np.float32)
+    qin = W.f32_to_bf16_bits(q)
+    out = iq.decode_attention(P.torch_input(qin, "bf16"), kc, ks, vc, vs, rot,
+                              seq_lens=torch.tensor(lens, dtype=torch.int32, device="cuda"), fmt=fmt)
+    torch.cuda.synchronize()
+    b = F.bits(fmt)
+    ref = F.decode_attention_format(W.to_f64(qin, "bf16"), F.unpack_bits(kc.cpu().numpy(), b), ks.cpu().numpy(),
+                                    F.unpack_bits(vc.cpu().numpy(), b), vs.cpu().numpy(), params, np.array(lens), fmt)
+    err = P.check_output(out.cpu().numpy(), ref, what="decode %s, random records" % fmt)
+    print("decode %s on random records: max abs error %.3g" % (fmt, err), flush=True)
