@@ -1287,19 +1287,27 @@ void decode_split_kernel(DecodeKArgs a) {
     }
   }
   // o'[coord] = vlim/16 * (kGain O 2^(24 - p) - kCenter ls), O = hi row + lo row; tile j column n is
-  // coordinate 8n + j, taken at bit position field_pos(j).
+  // coordinate 8n + j, taken at bit position field_pos(j).  The wave's 4 KB of the merge area holds
+  // them lane-major as float4 [i][lane]: i = 2 j + h is head row 2 g4 + j, coordinates 8n + 4h ..
+  // 8n + 4h + 3 (128-bit writes that no two lanes share a bank for; written per coordinate into
+  // [row][coord] the lanes of a row group collided eight ways).
   {
     const float back = ldexpf(1.f / kPScale, st.vexp);
+    float4* ow = reinterpret_cast<float4*>(&sm.u.merge.o[wave][0][0]);
 #pragma unroll
-    for (int j8 = 0; j8 < 8; ++j8) {
-      const int coord = 8 * n + j8;
-      const float up = Fmt<kFmt>::kGain * (float)(1 << (Fmt<kFmt>::kSub - VField<kFmt>::pos(j8)));
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sm.u.merge.o[wave][2 * g4 + j][coord] =
-            kAsym ? fmaf(back * up, st.O[j8][2 * j] + st.O[j8][2 * j + 1], ls_tot[j])
-                  : back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -Fmt<kFmt>::kCenter * ls_tot[j]);
-    }
+      for (int h = 0; h < 2; ++h) {
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j8 = 4 * h + t;
+          const float up = Fmt<kFmt>::kGain * (float)(1 << (Fmt<kFmt>::kSub - VField<kFmt>::pos(j8)));
+          v[t] = kAsym ? fmaf(back * up, st.O[j8][2 * j] + st.O[j8][2 * j + 1], ls_tot[j])
+                       : back * fmaf(st.O[j8][2 * j] + st.O[j8][2 * j + 1], up, -Fmt<kFmt>::kCenter * ls_tot[j]);
+        }
+        ow[(2 * j + h) * 64 + lane] = make_float4(v[0], v[1], v[2], v[3]);
+      }
   }
   __syncthreads();
   // ---------------- merge the 4 waves, rotate back, write the chunk partial ----------------
@@ -1316,7 +1324,9 @@ void decode_split_kernel(DecodeKArgs a) {
       const float mw = sm.u.merge.m[w][hr];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
       L += f * sm.u.merge.l[w][hr];
-      const float4 v = *reinterpret_cast<const float4*>(&sm.u.merge.o[w][hr][4 * kq]);
+      // coordinates 4 kq .. 4 kq + 3 of head row hr: lane (kq / 2, hr / 2), float4 2 (hr % 2) + kq % 2
+      const float4 v = reinterpret_cast<const float4*>(&sm.u.merge.o[w][0][0])[(2 * (hr & 1) + (kq & 1)) * 64 +
+                                                                               (kq >> 1) + 16 * (hr >> 1)];
       o[0] += f * v.x;
       o[1] += f * v.y;
       o[2] += f * v.z;
