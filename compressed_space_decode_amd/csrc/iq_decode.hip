@@ -478,16 +478,18 @@ struct SetupSmem {
 };
 template <int kW, int kP>
 union DecodeSmemU {
-  MergeSmemT<kW> merge;
   WaveLoopSmemT<kP> loop[kW];
   SetupSmem setup;
 };
 // The QK A operand in lane order (the same for every wave), built once and read from LDS for
-// every block, which keeps 16 registers per lane free for a second block in flight.
+// every block, which keeps 16 registers per lane free for a second block in flight.  The merge
+// area has its own storage, so a wave writes its results as soon as its loop ends, while other
+// waves still use their loop staging.
 template <int kW, int kP>
 struct DecodeSmem {
   uint4v qop[4][64];
   float blk[32][16];      // the KV head's SO(4) blocks, for the inverse rotation of the partials
+  MergeSmemT<kW> merge;
   DecodeSmemU<kW, kP> u;
 };
 
@@ -1180,7 +1182,7 @@ void decode_split_kernel(DecodeKArgs a) {
   // stores visible to the whole work-group, and every load of the cache is issued after it.
   if (kAppend && pos >= tok0 && pos < tok_end && wave == 1) {
     const int side = (lane >> 3) & 1, c = vec::chunk_of(lane & 7);
-    float* fold = &sm.u.merge.o[2][0][0];   // [32][16] folded blocks; clear of wave 0's set-up data
+    float* fold = &sm.merge.o[2][0][0];     // [32][16] folded blocks (the merge area is free until the end)
     if (lane < 32) vec::build_folded_block(rot + lane * 8, fold + lane * 16, vec::chunk_sign(lane >> 2));
     __builtin_amdgcn_wave_barrier();
     const float (&F)[4][16] = *reinterpret_cast<const float(*)[4][16]>(fold + 64 * c);
@@ -1278,12 +1280,11 @@ void decode_split_kernel(DecodeKArgs a) {
     l_tot[j] = row_sum(st.l_run[j]);
     ls_tot[j] = row_sum(st.ls_run[j]);
   }
-  __syncthreads();                     // every wave is done with the loop smem
   if (n == 0) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      sm.u.merge.m[wave][2 * g4 + j] = st.m_run[j];
-      sm.u.merge.l[wave][2 * g4 + j] = l_tot[j];
+      sm.merge.m[wave][2 * g4 + j] = st.m_run[j];
+      sm.merge.l[wave][2 * g4 + j] = l_tot[j];
     }
   }
   // o'[coord] = vlim/16 * (kGain O 2^(24 - p) - kCenter ls), O = hi row + lo row; tile j column n is
@@ -1293,7 +1294,7 @@ void decode_split_kernel(DecodeKArgs a) {
   // [row][coord] the lanes of a row group collided eight ways).
   {
     const float back = ldexpf(1.f / kPScale, st.vexp);
-    float4* ow = reinterpret_cast<float4*>(&sm.u.merge.o[wave][0][0]);
+    float4* ow = reinterpret_cast<float4*>(&sm.merge.o[wave][0][0]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -1317,15 +1318,15 @@ void decode_split_kernel(DecodeKArgs a) {
     const int hr = tid >> 5, kq = tid & 31;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.u.merge.m[w][hr]);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, sm.merge.m[w][hr]);
     float L = 0.f, o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
-      const float mw = sm.u.merge.m[w][hr];
+      const float mw = sm.merge.m[w][hr];
       const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      L += f * sm.u.merge.l[w][hr];
+      L += f * sm.merge.l[w][hr];
       // coordinates 4 kq .. 4 kq + 3 of head row hr: lane (kq / 2, hr / 2), float4 2 (hr % 2) + kq % 2
-      const float4 v = reinterpret_cast<const float4*>(&sm.u.merge.o[w][0][0])[(2 * (hr & 1) + (kq & 1)) * 64 +
+      const float4 v = reinterpret_cast<const float4*>(&sm.merge.o[w][0][0])[(2 * (hr & 1) + (kq & 1)) * 64 +
                                                                                (kq >> 1) + 16 * (hr >> 1)];
       o[0] += f * v.x;
       o[1] += f * v.y;
