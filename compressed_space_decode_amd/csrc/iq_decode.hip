@@ -1389,6 +1389,25 @@ struct MultiState {
   float vlim, pmul;
 };
 
+// fp16 hi and lo parts of s p_i for four values: hi_i = fp16(s p_i), lo_i = fp16(s p_i - hi_i), each
+// rounded once from the exact product by a mixed-precision FMA; hi = {hi_0 | hi_1 << 16, hi_2 | hi_3 << 16},
+// lo likewise (the compiler splits these with two more instructions per value).  A half written here
+// is read two instructions later at the earliest; the leading s_nop covers a transcendental result
+// read at once.
+__device__ __forceinline__ void split_hi_lo4(float s, const float (&p)[4], unsigned (&hi)[2], unsigned (&lo)[2]) {
+  asm("s_nop 0\n\t"
+      "v_fma_mixlo_f16 %0, %4, %5, 0\n\t"
+      "v_fma_mixlo_f16 %1, %4, %7, 0\n\t"
+      "v_fma_mixlo_f16 %2, %4, %5, -%0 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixlo_f16 %3, %4, %7, -%1 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %4, %6, 0\n\t"
+      "v_fma_mixhi_f16 %1, %4, %8, 0\n\t"
+      "v_fma_mixhi_f16 %2, %4, %6, -%0 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %3, %4, %8, -%1 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(lo[0]), "=&v"(lo[1])
+      : "v"(s), "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+}
+
 // process_block for kP token pairs (3-bit records).  A pair's 16 rows are (token, head), and the hi
 // and lo parts of q' (QK) and of P'' (PV) are the two halves of each product's K dimension: two
 // products into one accumulator.  lim[p]: the lane's token of pair p attends to the block's tokens
@@ -1452,14 +1471,16 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
   const int rem = tok_end - t0;
   if (n >= rem) sv0 = 0.f;
   if (16 + n >= rem) sv1 = 0.f;
+  // The mask is one additive bias per (pair, tile): a lane's four rows of a pair are one token.
   float z[kP][4][2];
 #pragma unroll
   for (int p = 0; p < kP; ++p) {
     const int ri = lim[p] - t0;
+    const float b0 = n < ri ? 0.f : -INFINITY, b1 = 16 + n < ri ? 0.f : -INFINITY;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      z[p][r][0] = n < ri ? sk0 * fmaf(S[p][0][r], c1[p], -c2[p][r]) : -INFINITY;
-      z[p][r][1] = 16 + n < ri ? sk1 * fmaf(S[p][1][r], c1[p], -c2[p][r]) : -INFINITY;
+      z[p][r][0] = fmaf(sk0, fmaf(S[p][0][r], c1[p], -c2[p][r]), b0);
+      z[p][r][1] = fmaf(sk1, fmaf(S[p][1][r], c1[p], -c2[p][r]), b1);
     }
   }
   const float svmax = fmaxf(sv0, sv1);
@@ -1505,19 +1526,17 @@ __device__ __forceinline__ void process_block_multi(BlockData<3>& cur, int t0, i
   for (int p = 0; p < kP; ++p) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      _Float16 hh[4], hl[4];
+      float pr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float pr = __builtin_amdgcn_exp2f(z[p][r][tt] - st.m_run[p][r]);
-        st.l_run[p][r] += pr;
-        const float pp = pr * svm[tt];
-        st.ls_run[p][r] += pp;
-        const _Float16 hi = (_Float16)pp;
-        hh[r] = hi;
-        hl[r] = (_Float16)(pp - (float)hi);
+        pr[r] = __builtin_amdgcn_exp2f(z[p][r][tt] - st.m_run[p][r]);
+        st.l_run[p][r] += pr[r];
+        st.ls_run[p][r] = fmaf(pr[r], svm[tt], st.ls_run[p][r]);
       }
-      *reinterpret_cast<short4v*>(ws.p[p][0] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, hh);
-      *reinterpret_cast<short4v*>(ws.p[p][1] + pwr + 16 * kPRow * tt) = __builtin_bit_cast(short4v, hl);
+      unsigned hh[2], hl[2];
+      split_hi_lo4(svm[tt], pr, hh, hl);
+      *reinterpret_cast<uint2*>(ws.p[p][0] + pwr + 16 * kPRow * tt) = make_uint2(hh[0], hh[1]);
+      *reinterpret_cast<uint2*>(ws.p[p][1] + pwr + 16 * kPRow * tt) = make_uint2(hl[0], hl[1]);
     }
   }
   __builtin_amdgcn_wave_barrier();
