@@ -1357,6 +1357,7 @@ void decode_split_kernel(DecodeKArgs a) {
 constexpr int kMultiQ = 4;                    // tokens per group (one per wave at set-up), even
 constexpr int kMultiWavesPerSimd = 2;
 constexpr int kMultiRounds = 3;               // work items per column: three rounds of work-groups
+constexpr int kMultiRoundsOneGroup = 2;       // two when each sequence has one group of tokens
 constexpr float kNoMax = -1e30f;              // running max before any score: finite, so a token
                                               // with nothing to attend to in a chunk gets p = 0
 struct MultiLoopSmem {
@@ -2190,15 +2191,19 @@ hipError_t launch_decode(const DecodeLaunch& a, const DecodeGeometry& geo, hipSt
   // (x_max, the partial rows' stride, covers every format's work items)
   const dim3 grid1((unsigned)(a.n_kv_heads * geo.head_groups), (unsigned)(target_f > vb ? target_f : vb), 1u);
   // several query tokens (3-bit records): groups of kMultiQ tokens share each block's unpacked
-  // codes; partial rows x kMultiQ + i.  The plan aims at three rounds of work-groups: with one
-  // chunk per (sequence, token group) a single round left compute units idle.
+  // codes; partial rows x kMultiQ + i.  The plan aims at three rounds of work-groups (two when each
+  // sequence has one group): with one chunk per (sequence, token group) a single round left compute
+  // units idle.
   const bool multi = a.q_tokens > 1 && a.format == IQ_FMT_U3 && a.positions == nullptr;
   int xg = 0;
   if (multi) {
     const int ng = (a.q_tokens + kMultiQ - 1) / kMultiQ;
     const int64_t vbg = (int64_t)a.batch * ng;
     const int64_t columns = (int64_t)a.n_kv_heads * geo.head_groups;
-    int64_t tg = (int64_t)kMultiRounds * kMultiWavesPerSimd * device_cu_count() / columns;
+    // (one group per sequence, Q = 4 at 48 layers: 0.273-0.278 ms with two rounds, 0.282-0.284 with
+    // three; Q = 16: 0.85-0.87 ms with three, 0.90 with two)
+    const int rounds = ng == 1 ? kMultiRoundsOneGroup : kMultiRounds;
+    int64_t tg = (int64_t)rounds * kMultiWavesPerSimd * device_cu_count() / columns;
     const int64_t most = vbg * ((a.cache_cap + 255) / 256);
     if (tg > most) tg = most;
     if (tg > kMaxChunks) tg = kMaxChunks;
