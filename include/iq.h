@@ -83,7 +83,7 @@ const char* iq_last_error(void);
 
 /*
  * iq_make_rotation -- draw rotation parameters (host only, no GPU work).
- * Source: Abstract ("256 stored parameters per head").  How the parameters
+ * Source: Abstract (each head stores 256 rotation parameters).  How the parameters
  * are drawn is not stated; this draws each block's left and right
  * quaternions uniformly on the 3-sphere: SplitMix64 (Steele, Lea, Flood
  * 2014) outputs z_i = mix(seed + (i+1)*0x9E3779B97F4A7C15) give uniforms
@@ -182,8 +182,8 @@ int64_t iq_decode_workspace_bytes(int32_t batch, int32_t n_q_heads,
 
 /*
  * iq_decode_attention -- one decode step of attention computed on the
- * packed cache.  Source: Abstract ("performs attention directly on packed
- * 3-bit tensors without materializing full-precision KV state").  The
+ * packed cache.  Source: Abstract (attention runs on the packed 3-bit
+ * tensors; no full-precision K/V is ever formed).  The
  * query is rotated into the compressed space, codes are turned into
  * numbers only in registers, softmax is online and split over the
  * sequence, V is accumulated in rotated space and rotated back once per

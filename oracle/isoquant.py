@@ -27,7 +27,7 @@ def bf16_bits_to_f64(bits):
 
 
 # --------------------------------------------------------------------------
-# Walsh-Hadamard transform (Abstract: "applies a Walsh-Hadamard transform")
+# Walsh-Hadamard transform (Abstract: the first stage of the rotation)
 # --------------------------------------------------------------------------
 def hadamard(n=D):
     """Normalised Sylvester-order Hadamard matrix, H[i, j] = (-1)^popcount(i & j) / sqrt(n).
@@ -47,7 +47,8 @@ def hadamard(n=D):
 
 # --------------------------------------------------------------------------
 # SO(4) blocks from a left/right unit-quaternion pair
-# (Abstract: "block-diagonal SO(4) rotations", "256 stored parameters per head")
+# (Abstract: the second stage, 4x4 rotation blocks on the diagonal, 256 stored parameters
+# per head)
 # --------------------------------------------------------------------------
 def quat_left(a):
     """4x4 matrix of v -> a * v (Hamilton product, components (w, x, y, z))."""
@@ -92,8 +93,8 @@ def rotation_matrix(params):
 
     ``params`` is [32][8]: params[b, 0:4] = q_L, params[b, 4:8] = q_R of
     block b, which acts on coordinates 4b..4b+3.  Order: WHT first, then
-    the block rotation (Abstract: "a Walsh-Hadamard transform followed by
-    block-diagonal SO(4) rotations").
+    the block rotation (Abstract: the Walsh-Hadamard stage, then the diagonal of
+    SO(4) blocks).
     """
     p = np.asarray(params, dtype=np.float64).reshape(NBLK, 8)
     B = np.zeros((D, D))
@@ -110,7 +111,7 @@ def rotate(x, params):
 
 # --------------------------------------------------------------------------
 # 3-bit scalar quantization with a per-vector scale
-# (Abstract: "before 3-bit scalar quantization")
+# (Abstract: each coordinate of the rotated vector gets a 3-bit scalar code)
 # --------------------------------------------------------------------------
 def quantize(x, params):
     """Rotate, then quantize each 128-vector to 3-bit codes and one fp32 scale.
@@ -142,8 +143,8 @@ def dequantize_rotated(codes, scales):
 
 
 # --------------------------------------------------------------------------
-# Bit layout of a 48-byte record (Abstract: "packed 3-bit tensors"; the
-# layout itself is a reading).
+# Bit layout of a 48-byte record (Abstract: the cache holds the codes packed at
+# 3 bits each; the layout itself is a reading).
 #
 # The 128 codes form one little-endian bit stream of 384 bits: bit b of the
 # code of coordinate i is stream bit 3i + b, and byte k of the record holds
@@ -185,8 +186,8 @@ def unpack(records):
 
 
 # --------------------------------------------------------------------------
-# Decode attention on packed codes (Abstract: "performs attention directly on
-# packed 3-bit tensors without materializing full-precision KV state").
+# Decode attention on packed codes (Abstract: attention runs on the packed codes;
+# no full-precision K/V is ever formed).
 # --------------------------------------------------------------------------
 def decode_attention(q, k_codes, k_scales, v_codes, v_scales, params, seq_lens,
                      sm_scale=None):
