@@ -1099,13 +1099,18 @@ void decode_split_kernel(DecodeKArgs a) {
 
   const int step = kW * kBlock;
   int t0 = tok0 + wave * kBlock;
-  // The first two blocks of every wave are loaded now, so that they stream while the queries are
-  // rotated.  In the work-group that appends a token to one of those blocks these loads read
-  // zeros without a memory access (an end of 0), and the blocks are loaded after the append.
-  const bool reload = kAppend && pos >= tok0 && pos < tok0 + 2 * step;   // uniform
+  // The first blocks of every wave are loaded now, so that they stream while the queries are
+  // rotated: three in a grid of at most one work-group per compute unit (eight waves; one 32K
+  // layer 11.88 -> 11.55 us, gqa8k 10.27 -> 9.98 us, same box), two otherwise (the third there
+  // made the 48-layer step 0.6 us slower).  In the work-group that appends a token to one of those
+  // blocks these loads read zeros without a memory access (an end of 0), and the blocks are loaded
+  // after the append.
+  constexpr int kEarly = kW == 2 * kWaves ? 3 : 2;
+  const bool reload = kAppend && pos >= tok0 && pos < tok0 + kEarly * step;   // uniform
   BlockData<Fmt<kFmt>::kQW> buf, buf2, buf3;
   load_block<kFmt>(buf, cb, t0, reload ? 0 : tok_end, lo);
   load_block<kFmt>(buf2, cb, t0 + step, reload ? 0 : tok_end, lo);
+  if constexpr (kEarly == 3) load_block<kFmt>(buf3, cb, t0 + 2 * step, reload ? 0 : tok_end, lo);
 
   // ---------------- set-up (all waves): rotate the queries ----------------
   // Thread (head row hr, block kq) holds coordinates 4 kq .. 4 kq + 3 of its head.  H_128 =
@@ -1253,13 +1258,17 @@ void decode_split_kernel(DecodeKArgs a) {
   if (reload) {                      // uniform; the barriers above ordered it after the append
     load_block<kFmt>(buf, cb, t0, tok_end, lo);
     load_block<kFmt>(buf2, cb, t0 + step, tok_end, lo);
+    if constexpr (kEarly == 3) load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
   }
   // Three buffers: the first two are refilled three blocks ahead once their codes are unpacked;
-  // the third is loaded at the top of each round of three blocks.  So the buffers carried around
-  // the loop were refilled one or two blocks before its back-edge, never just before it.
+  // the third is loaded at the top of each round of three blocks after the first.  So the buffers
+  // carried around the loop were refilled one or two blocks before its back-edge, never just
+  // before it.
+  bool top_load = kEarly == 2;
   while (t0 < tok_end) {            // uniform
     progress_priority(t0 - tok0, tok_end - tok0);
-    load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    if (top_load) load_block<kFmt>(buf3, cb, t0 + 2 * step, tok_end, lo);
+    top_load = true;
     process_block<true, kFmt>(buf, min(tok_end - t0, kBlock), t0 + 3 * step, tok_end, cb, lo, vscale, st, sm.qop, c1, c2,
                         ws, lane, n, g4, pwr, prd);
     t0 += step;
